@@ -1,0 +1,192 @@
+/*
+ * rb.h -- C ABI of librb: residual binarized weights on AMD Instinct MI355X (gfx950).
+ *
+ * The library derives k residual sign bit-planes with dual scales from a full
+ * precision weight matrix, and runs the matmul-free product on the packed planes,
+ * plus the binary-codebook (sub-1-bit) variant. Every entry point only validates its
+ * arguments on the host and enqueues kernels on the caller's stream: no allocation,
+ * no free, no synchronisation, no exceptions across the ABI.
+ *
+ * Sources (web pages on the method, cited by title and section):
+ *   [RaBiT] "RaBiT: Residual-Aware Binarization Training for Accurate and Efficient
+ *           LLMs" (paper summary page): background "Residual binarization", sections
+ *           "Method step details" (Algorithm 2) and "Technical novelty".
+ *   [BTC]   "亚1比特大模型量化技术突破与实践" (BTC-LLM binary codebook page):
+ *           sections 2.1.1, 2.1.2, 3.2.1, 3.2.2, 5.1, 5.2.
+ *
+ * Conventions shared by every call
+ *   - Matrices are row-major. W is N x K (output x input), y = W x.
+ *   - Every pointer except the host-side helpers' is a DEVICE pointer owned by the
+ *     caller (memory from hipMalloc / torch); the library keeps no pointer after a
+ *     call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). The work
+ *     is only enqueued; results are ready when the stream reaches that point.
+ *   - Host-detectable errors (bad sizes, NULL pointers, misalignment, workspace too
+ *     small, unsupported dtype) are returned synchronously before anything is
+ *     enqueued. RB_ERR_HIP means a launch failed (hipGetLastError after launch).
+ *   - Calls are stateless and may be made from several host threads; calls that share
+ *     an output or a workspace buffer must be ordered by the caller (same stream).
+ *
+ * Bit-plane format ("planes"): k planes, each N rows of `ldp` uint32 words
+ *   (ldp >= ceil(K/32)), plane stride N*ldp words. Bit j of word w of row n is column
+ *   32*w + j (LSB first); bit 1 means +1, bit 0 means -1; sign(0) = +1 (also -0.0).
+ *   Bits for columns >= K are 0. Words ceil(K/32) .. ldp-1 are padding: never read,
+ *   never written. [RaBiT "Technical novelty": 32 columns per uint32]
+ * Scales: g is [k][N] (one per output row and plane), h is [k][K] (one per input
+ *   column and plane), both in `scale_dtype`; W_hat = sum_i g_i (.) B_i (.) h_i.
+ *   [RaBiT "Residual binarization"]
+ */
+#ifndef RB_H_
+#define RB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rb_status {
+  RB_OK = 0,
+  RB_ERR_INVALID_ARG = 1,  /* a size, enum or pointer is out of range / NULL          */
+  RB_ERR_UNSUPPORTED = 2,  /* a valid combination this build does not implement      */
+  RB_ERR_MISALIGNED = 3,   /* a pointer violates the alignment the entry point states */
+  RB_ERR_WORKSPACE = 4,    /* ws is NULL or ws_bytes < rb_workspace_bytes(...)        */
+  RB_ERR_HIP = 5           /* a kernel launch failed                                  */
+} rb_status;
+
+typedef enum rb_dtype { RB_F32 = 0, RB_F16 = 1, RB_BF16 = 2 } rb_dtype;
+
+typedef enum rb_op {
+  RB_OP_PACK = 0,
+  RB_OP_GEMV = 1,
+  RB_OP_GEMM_SMALL = 2,
+  RB_OP_CODEBOOK_ENCODE = 3,
+  RB_OP_CODEBOOK_GEMV = 4
+} rb_op;
+
+/* Version of this ABI (major*10000 + minor*100 + patch). */
+int rb_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char* rb_status_string(rb_status s);
+
+/* Device workspace (bytes) an operation needs for the given sizes; 0 when it needs
+ * none. A workspace must be zero-filled once after allocation; every call returns it
+ * to all-zero before its last kernel ends, so it can be reused without clearing. */
+size_t rb_workspace_bytes(rb_op op, int32_t k, int64_t N, int64_t K, int64_t M);
+
+/* Storage cost in bits per weight of k planes plus per-row g_i and (if has_h)
+ * per-column h_i in scale_dtype: k + bits(scale_dtype) * k * (N + has_h*K) / (N*K).
+ * With N = K = 4096, k = 2 and fp16 scales this is 2.015625, the "2.02 effective
+ * bits" of [RaBiT "Limitations"]. Returns -1 on invalid arguments. */
+double rb_storage_bits_per_weight(int64_t N, int64_t K, int32_t k, rb_dtype scale_dtype,
+                                  int32_t has_h);
+
+/*
+ * rb_pack -- derive k residual sign planes and their scales from W.
+ *   [RaBiT "Method step details", Algorithm 2 forward pass; deployment derives the
+ *   planes once and freezes them]
+ *     R_0 = W;  for i = 0..k-1:  B_i = sign(R_i)            (sign(0) = +1)
+ *                                g_i = sum|R_i| h_i / sum h_i^2, rounded to nearest-even
+ *                                      in scale_dtype (row mean |R_i| when h = 1)
+ *                                R_{i+1} = R_i - g_i (.) B_i (.) h_i   (stored g_i)
+ *   The sums are taken in fp64 and the residual is kept in fp64, so the result equals
+ *   the exact derivation except for scales whose quotient falls within ~K*2^-53
+ *   (relative) of a rounding midpoint, which may round to either neighbour.
+ *
+ *   W        [N][ldw] elements of w_dtype (RB_F32, RB_F16 or RB_BF16), 4-byte aligned
+ *   N, K     rows (outputs) and columns (inputs); 1 <= N, K < 2^31
+ *   ldw      row stride of W in elements, >= K
+ *   k        number of planes, 1..4
+ *   group    0: one scale per row (g is [k][N]); otherwise a power of two in 2..64:
+ *            one scale per `group` consecutive columns (g is [k][N][ceil(K/group)]),
+ *            mean |R| over the group's columns; requires h == NULL
+ *   h        [k][K] in scale_dtype, or NULL for all ones
+ *   scale_dtype  RB_F16 or RB_F32 (type of g and h)
+ *   planes   output, [k][N][ldp] uint32, 16-byte aligned; ldp >= ceil(K/32)
+ *   g        output scales, scale_dtype, layout above
+ *   d_status optional device int32; the call ORs 1 into it if W holds a NaN or an
+ *            infinity (outputs are then unspecified). NULL to skip the check report.
+ */
+rb_status rb_pack(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, int32_t k,
+                  int32_t group, const void* h, rb_dtype scale_dtype, uint32_t* planes, int64_t ldp,
+                  void* g, int32_t* d_status, void* stream);
+
+/*
+ * rb_gemv -- the matmul-free product on packed planes for decode-sized batches.
+ *   [RaBiT "Residual binarization": the k paths run in parallel with additions and
+ *   element-wise scaling only]
+ *     y[m][n] = sum_i g_i[n] * sum_c B_i[n][c] * h_i[c] * x[m][c]
+ *   computed as sum_i g_i[n] * (2*T_i[m][n] - S_i[m]) with T_i the sum of h_i (.) x over
+ *   the columns whose bit is 1 and S_i the sum over all columns (fp32 accumulation),
+ *   then rounded to y_dtype.
+ *
+ *   planes, ldp   as produced by rb_pack (16-byte aligned)
+ *   g, h          [k][N] and [k][K] (h may be NULL = ones) in scale_dtype (F16 or F32)
+ *   k             1..4;  N, K >= 1
+ *   x             [M][K] in x_dtype (RB_F16 or RB_F32), 16-byte aligned
+ *   M             1..16 (larger batches: rb_gemm_small)
+ *   y             output [M][N] in y_dtype (RB_F16 or RB_F32), 16-byte aligned
+ *   ws, ws_bytes  device workspace of at least rb_workspace_bytes(RB_OP_GEMV, k, N, K, M)
+ *                 bytes, zero-filled once after allocation (may be NULL if that is 0)
+ */
+rb_status rb_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                  rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,
+                  rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/*
+ * rb_gemm_small -- the same product for larger batches, on the matrix cores: the bits
+ *   of each plane are expanded to +-h_i fp16 tiles and multiplied with the fp16
+ *   activations (fp32 accumulation); y = sum_i g_i (.) acc_i.
+ *   Arguments as rb_gemv, except: x_dtype must be RB_F16; 1 <= M <= 4096; K must be a
+ *   multiple of 64 and ldp a multiple of 2.
+ */
+rb_status rb_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                        rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,
+                        rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * rb_codebook_encode -- nearest binary codeword of every v-column block of a sign plane.
+ *   [BTC 2.1.1: the sign matrix is cut into v-dimensional +-1 sub-vectors, each stored
+ *   as the index of a codeword; distance is Hamming, via XOR + popcount]
+ *     block j of row n = columns v*j .. v*j+v-1 of the plane (bit t = column v*j+t;
+ *     columns >= K count as +1, i.e. bit 1); idx[n][j] = argmin_c popcount(block ^ C[c]),
+ *     ties to the lowest c.
+ *
+ *   sign_plane  [N][ldp] uint32 in the plane format above (one plane), 16-byte aligned
+ *   codebook    [c] uint32, codeword in the low v bits (upper bits must be 0)
+ *   c           1..65536 (index width ceil(log2 c) <= 16 bits, [BTC 5.2])
+ *   v           1..32
+ *   idx         output [N][ceil(K/v)] uint16
+ */
+rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K,
+                             const uint32_t* codebook, int32_t c, int32_t v, uint16_t* idx,
+                             void* stream);
+
+/*
+ * rb_codebook_gemv -- product with codebook-compressed signs and group scales.
+ *   [BTC 2.1.2 (LUT-GEMM: sums of input blocks against codeword patterns are precomputed
+ *   and accumulated by weight index, with no dequantisation) and 3.2.1 (one scale per
+ *   16 weights)]
+ *     y[m][n] = sum_c s[n][c/group] * (+-1 bit (c mod v) of C[idx[n][c/v]]) * x[m][c]
+ *
+ *   idx       [N][ceil(K/v)] uint16 (each < c)
+ *   codebook  [c] uint32 as for rb_codebook_encode
+ *   s         [N][ceil(K/group)] fp16 group scales
+ *   group     a power of two in 2..64
+ *   x         [M][K] fp16, 16-byte aligned;  M = 1..4
+ *   y         output [M][N] fp16
+ *   ws        rb_workspace_bytes(RB_OP_CODEBOOK_GEMV, 1, N, K, M) bytes (may be 0)
+ */
+rb_status rb_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, int32_t c, int32_t v,
+                           const void* s, int32_t group, int64_t N, int64_t K, const void* x,
+                           int64_t M, void* y, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RB_H_ */

@@ -1,0 +1,132 @@
+"""Residual binarized weights on AMD Instinct MI355X: Python face of librb.
+
+Thin wrappers over the C ABI in include/rb.h. PyTorch provides device buffers and the
+current HIP stream; every computation runs in librb's HIP kernels. Functions take and
+return CUDA (HIP) tensors on the current device and enqueue on the current stream.
+
+  planes, g = pack(W, k)                         residual sign planes + row scales
+  y = gemv(planes, g, h, x, K)                   y = sum_i g_i (.) (B_i (h_i (.) x)), M <= 16
+  y = gemm_small(planes, g, h, x, K)             same on the matrix cores, larger M
+  idx = codebook_encode(sign_plane, K, C, v)     nearest binary codeword per v-block
+  y = codebook_gemv(idx, C, v, s, group, x, K)   product on codebook indices
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (RB_F16, RB_F32, RB_BF16, RB_OP_CODEBOOK_GEMV, RB_OP_GEMM_SMALL, RB_OP_GEMV,
+                   RbError, check, lib)
+
+__all__ = ["pack", "gemv", "gemm_small", "codebook_encode", "codebook_gemv", "workspace",
+           "workspace_bytes", "storage_bits_per_weight", "version", "RbError", "lib"]
+
+_DT = {torch.float32: RB_F32, torch.float16: RB_F16, torch.bfloat16: RB_BF16}
+
+
+def _dt(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t}")
+    return _DT[t]
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("librb takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("librb takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def version() -> int:
+    return lib.rb_version()
+
+
+def workspace_bytes(op: int, k: int, N: int, K: int, M: int) -> int:
+    return int(lib.rb_workspace_bytes(op, k, N, K, M))
+
+
+def storage_bits_per_weight(N: int, K: int, k: int, scale_dtype=torch.float16, has_h: bool = True) -> float:
+    return float(lib.rb_storage_bits_per_weight(N, K, k, _dt(scale_dtype), int(has_h)))
+
+
+def workspace(op: int, k: int, N: int, K: int, M: int, device=None) -> torch.Tensor | None:
+    """A zero-filled workspace for the given operation (None when it needs none)."""
+    n = workspace_bytes(op, k, N, K, M)
+    if n == 0:
+        return None
+    return torch.zeros((n + 15) // 16 * 16, dtype=torch.uint8, device=device or "cuda")
+
+
+def pack(W: torch.Tensor, k: int, h: torch.Tensor | None = None, group: int = 0,
+         scale_dtype=torch.float16, ldp: int | None = None, planes: torch.Tensor | None = None,
+         d_status: torch.Tensor | None = None):
+    """Residual sign planes (int32 storage of the uint32 words, [k][N][ldp]) and scales
+    ([k][N] or [k][N][ceil(K/group)]) of W [N][K] (fp32/fp16/bf16)."""
+    N, K = W.shape
+    Kw = (K + 31) // 32
+    ldp = Kw if ldp is None else ldp
+    if planes is None:
+        planes = torch.zeros((k, N, ldp), dtype=torch.int32, device=W.device)
+    shape = (k, N) if group == 0 else (k, N, (K + group - 1) // group)
+    g = torch.empty(shape, dtype=scale_dtype, device=W.device)
+    check("rb_pack", lib.rb_pack(_ptr(W), _dt(W.dtype), N, K, W.stride(0), k, group, _ptr(h),
+                                 _dt(scale_dtype), _ptr(planes), ldp, _ptr(g), _ptr(d_status),
+                                 _stream()))
+    return planes, g
+
+
+def _product(fn_name: str, planes, g, h, x, K, y_dtype, ws, y, op):
+    k, N, ldp = planes.shape
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=x.device)
+    if ws is None:
+        ws = workspace(op, k, N, K, M, device=x.device)
+    fn = getattr(lib, fn_name)
+    check(fn_name, fn(_ptr(planes), ldp, _ptr(g), _ptr(h), _dt(g.dtype), k, N, K, _ptr(x),
+                      _dt(x.dtype), M, _ptr(y), _dt(y.dtype), _ptr(ws),
+                      0 if ws is None else ws.numel(), _stream()))
+    return y
+
+
+def gemv(planes, g, h, x, K: int, y_dtype=torch.float16, ws=None, y=None):
+    """y [M][N] = sum_i g_i (.) (B_i (h_i (.) x)) for x [M][K], M <= 16."""
+    return _product("rb_gemv", planes, g, h, x, K, y_dtype, ws, y, RB_OP_GEMV)
+
+
+def gemm_small(planes, g, h, x, K: int, y_dtype=torch.float16, ws=None, y=None):
+    """Same product on the matrix cores, for larger batches (x fp16)."""
+    return _product("rb_gemm_small", planes, g, h, x, K, y_dtype, ws, y, RB_OP_GEMM_SMALL)
+
+
+def codebook_encode(sign_plane: torch.Tensor, K: int, codebook: torch.Tensor, v: int):
+    """uint16 indices (int16 storage) [N][ceil(K/v)] of the nearest codewords."""
+    N, ldp = sign_plane.shape
+    nb = (K + v - 1) // v
+    idx = torch.empty((N, nb), dtype=torch.int16, device=sign_plane.device)
+    check("rb_codebook_encode", lib.rb_codebook_encode(_ptr(sign_plane), ldp, N, K, _ptr(codebook),
+                                                       codebook.numel(), v, _ptr(idx), _stream()))
+    return idx
+
+
+def codebook_gemv(idx, codebook, v: int, s, group: int, x, K: int, ws=None, y=None):
+    N = idx.shape[0]
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    if ws is None:
+        ws = workspace(RB_OP_CODEBOOK_GEMV, 1, N, K, M, device=x.device)
+    check("rb_codebook_gemv", lib.rb_codebook_gemv(_ptr(idx), _ptr(codebook), codebook.numel(), v,
+                                                   _ptr(s), group, N, K, _ptr(x), M, _ptr(y),
+                                                   _ptr(ws), 0 if ws is None else ws.numel(),
+                                                   _stream()))
+    return y

@@ -1,0 +1,170 @@
+// rb_api.cpp -- C ABI of librb: host-side validation, then one enqueue per call.
+//
+// Every check below runs before any HIP call, so an invalid call returns its status
+// without touching the device (and can be tested on a machine with no GPU).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/rb.h"
+#include "rb_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_dtype(rb_dtype d) { return d == RB_F32 || d == RB_F16 || d == RB_BF16; }
+
+bool is_pow2_in(int32_t v, int32_t lo, int32_t hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+rb_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return RB_OK;
+  if (std::getenv("RB_LOG")) std::fprintf(stderr, "librb: launch failed: %s\n", hipGetErrorString(e));
+  return RB_ERR_HIP;
+}
+
+void log_call(const char* what, int64_t N, int64_t K, int64_t M, int k) {
+  if (std::getenv("RB_LOG")) std::fprintf(stderr, "librb: %s N=%lld K=%lld M=%lld k=%d\n", what,
+                                          (long long)N, (long long)K, (long long)M, k);
+}
+
+rb_status check_product_args(const uint32_t* planes, int64_t ldp, const void* g, rb_dtype scale_dtype,
+                             int32_t k, int64_t N, int64_t K, const void* x, rb_dtype x_dtype,
+                             int64_t M, void* y, rb_dtype y_dtype, int64_t max_m) {
+  if (!planes || !g || !x || !y) return RB_ERR_INVALID_ARG;
+  if (k < 1 || k > 4) return RB_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (M < 1) return RB_ERR_INVALID_ARG;
+  if (ldp < (K + 31) / 32) return RB_ERR_INVALID_ARG;
+  if (!valid_dtype(scale_dtype) || !valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return RB_ERR_INVALID_ARG;
+  if (scale_dtype == RB_BF16 || x_dtype == RB_BF16 || y_dtype == RB_BF16) return RB_ERR_UNSUPPORTED;
+  if (M > max_m) return RB_ERR_UNSUPPORTED;
+  if (!aligned(planes, 16) || !aligned(x, 16) || !aligned(y, 16)) return RB_ERR_MISALIGNED;
+  if (!aligned(g, scale_dtype == RB_F32 ? 4 : 2)) return RB_ERR_MISALIGNED;
+  return RB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rb_version(void) { return 100; }
+
+const char* rb_status_string(rb_status s) {
+  switch (s) {
+    case RB_OK: return "RB_OK";
+    case RB_ERR_INVALID_ARG: return "RB_ERR_INVALID_ARG: an argument is out of range or NULL";
+    case RB_ERR_UNSUPPORTED: return "RB_ERR_UNSUPPORTED: valid arguments this build does not implement";
+    case RB_ERR_MISALIGNED: return "RB_ERR_MISALIGNED: a pointer is not aligned as required";
+    case RB_ERR_WORKSPACE: return "RB_ERR_WORKSPACE: workspace missing or too small";
+    case RB_ERR_HIP: return "RB_ERR_HIP: a kernel launch failed";
+  }
+  return "RB_ERR_UNKNOWN";
+}
+
+size_t rb_workspace_bytes(rb_op op, int32_t k, int64_t N, int64_t K, int64_t M) {
+  if (k < 1 || k > 4 || N < 1 || K < 1 || M < 1) return 0;
+  switch (op) {
+    case RB_OP_GEMV: return rb::gemv_workspace_bytes(k, N, K, M);
+    case RB_OP_GEMM_SMALL: return rb::gemm_small_workspace_bytes(k, N, K, M);
+    case RB_OP_CODEBOOK_GEMV: return rb::codebook_gemv_workspace_bytes(N, K, M);
+    default: return 0;
+  }
+}
+
+double rb_storage_bits_per_weight(int64_t N, int64_t K, int32_t k, rb_dtype scale_dtype, int32_t has_h) {
+  if (N < 1 || K < 1 || k < 1 || k > 4 || !valid_dtype(scale_dtype)) return -1.0;
+  const double sbits = scale_dtype == RB_F32 ? 32.0 : 16.0;
+  const double per_plane = (double)N + (has_h ? (double)K : 0.0);
+  return (double)k + sbits * (double)k * per_plane / ((double)N * (double)K);
+}
+
+rb_status rb_pack(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, int32_t k,
+                  int32_t group, const void* h, rb_dtype scale_dtype, uint32_t* planes, int64_t ldp,
+                  void* g, int32_t* d_status, void* stream) {
+  if (!W || !planes || !g) return RB_ERR_INVALID_ARG;
+  if (!valid_dtype(w_dtype) || !valid_dtype(scale_dtype)) return RB_ERR_INVALID_ARG;
+  if (scale_dtype == RB_BF16) return RB_ERR_UNSUPPORTED;
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (ldw < K || ldp < (K + 31) / 32) return RB_ERR_INVALID_ARG;
+  if (k < 1 || k > 4) return RB_ERR_INVALID_ARG;
+  if (group != 0 && !is_pow2_in(group, 2, 64)) return RB_ERR_INVALID_ARG;
+  if (group != 0 && h != nullptr) return RB_ERR_UNSUPPORTED;
+  if (!aligned(planes, 16)) return RB_ERR_MISALIGNED;
+  if (!aligned(W, w_dtype == RB_F32 ? 4 : 2) || !aligned(g, scale_dtype == RB_F32 ? 4 : 2) ||
+      (h && !aligned(h, scale_dtype == RB_F32 ? 4 : 2)) || (d_status && !aligned(d_status, 4)))
+    return RB_ERR_MISALIGNED;
+  log_call("rb_pack", N, K, 0, k);
+  return from_hip(rb::launch_pack(W, w_dtype, N, K, ldw, k, group, h, scale_dtype, planes, ldp, g,
+                                  d_status, static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                  rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,
+                  rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws, size_t ws_bytes,
+                  void* stream) {
+  rb_status st = check_product_args(planes, ldp, g, scale_dtype, k, N, K, x, x_dtype, M, y, y_dtype, 16);
+  if (st != RB_OK) return st;
+  if (h && !aligned(h, scale_dtype == RB_F32 ? 4 : 2)) return RB_ERR_MISALIGNED;
+  const size_t need = rb::gemv_workspace_bytes(k, N, K, M);
+  if (need > 0 && (!ws || ws_bytes < need)) return RB_ERR_WORKSPACE;
+  if (ws && !aligned(ws, 16)) return RB_ERR_MISALIGNED;
+  log_call("rb_gemv", N, K, M, k);
+  return from_hip(rb::launch_gemv(planes, ldp, g, h, scale_dtype, k, N, K, x, x_dtype, M, y, y_dtype,
+                                  ws, static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                        rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,
+                        rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,
+                        size_t ws_bytes, void* stream) {
+  rb_status st = check_product_args(planes, ldp, g, scale_dtype, k, N, K, x, x_dtype, M, y, y_dtype, 4096);
+  if (st != RB_OK) return st;
+  if (x_dtype != RB_F16) return RB_ERR_UNSUPPORTED;
+  if (K % 64 != 0 || ldp % 2 != 0) return RB_ERR_UNSUPPORTED;
+  if (h && !aligned(h, scale_dtype == RB_F32 ? 4 : 2)) return RB_ERR_MISALIGNED;
+  const size_t need = rb::gemm_small_workspace_bytes(k, N, K, M);
+  if (need > 0 && (!ws || ws_bytes < need)) return RB_ERR_WORKSPACE;
+  log_call("rb_gemm_small", N, K, M, k);
+  return from_hip(rb::launch_gemm_small(planes, ldp, g, h, scale_dtype, k, N, K, x, M, y, y_dtype, ws,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K,
+                             const uint32_t* codebook, int32_t c, int32_t v, uint16_t* idx,
+                             void* stream) {
+  if (!sign_plane || !codebook || !idx) return RB_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (ldp < (K + 31) / 32) return RB_ERR_INVALID_ARG;
+  if (c < 1 || c > 65536 || v < 1 || v > 32) return RB_ERR_INVALID_ARG;
+  if (!aligned(sign_plane, 16) || !aligned(codebook, 4) || !aligned(idx, 2)) return RB_ERR_MISALIGNED;
+  log_call("rb_codebook_encode", N, K, 0, 1);
+  return from_hip(rb::launch_codebook_encode(sign_plane, ldp, N, K, codebook, c, v, idx,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, int32_t c, int32_t v,
+                           const void* s, int32_t group, int64_t N, int64_t K, const void* x,
+                           int64_t M, void* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!idx || !codebook || !s || !x || !y) return RB_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (c < 1 || c > 65536 || v < 1 || v > 32) return RB_ERR_INVALID_ARG;
+  if (!is_pow2_in(group, 2, 64)) return RB_ERR_INVALID_ARG;
+  if (M < 1) return RB_ERR_INVALID_ARG;
+  if (M > 4) return RB_ERR_UNSUPPORTED;
+  if (!aligned(idx, 2) || !aligned(codebook, 4) || !aligned(s, 2) || !aligned(x, 16) || !aligned(y, 16))
+    return RB_ERR_MISALIGNED;
+  const size_t need = rb::codebook_gemv_workspace_bytes(N, K, M);
+  if (need > 0 && (!ws || ws_bytes < need)) return RB_ERR_WORKSPACE;
+  log_call("rb_codebook_gemv", N, K, M, 1);
+  return from_hip(rb::launch_codebook_gemv(idx, codebook, c, v, s, group, N, K, x, M, y, ws,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

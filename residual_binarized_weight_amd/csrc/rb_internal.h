@@ -1,0 +1,38 @@
+// rb_internal.h -- launchers behind the C ABI (arguments already validated by rb_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rb.h"
+
+namespace rb {
+
+hipError_t launch_pack(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, int k,
+                       int group, const void* h, rb_dtype scale_dtype, uint32_t* planes, int64_t ldp,
+                       void* g, int32_t* d_status, hipStream_t s);
+
+// GEMV (M <= 16)
+size_t gemv_workspace_bytes(int k, int64_t N, int64_t K, int64_t M);
+hipError_t launch_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                       rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x,
+                       rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,
+                       hipStream_t s);
+
+// small GEMM on the matrix cores
+size_t gemm_small_workspace_bytes(int k, int64_t N, int64_t K, int64_t M);
+hipError_t launch_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                             rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x,
+                             int64_t M, void* y, rb_dtype y_dtype, void* ws, hipStream_t s);
+
+// binary codebook
+hipError_t launch_codebook_encode(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K,
+                                  const uint32_t* codebook, int c, int v, uint16_t* idx,
+                                  hipStream_t s);
+size_t codebook_gemv_workspace_bytes(int64_t N, int64_t K, int64_t M);
+hipError_t launch_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, int c, int v,
+                                const void* s, int group, int64_t N, int64_t K, const void* x,
+                                int64_t M, void* y, void* ws, hipStream_t st);
+
+}  // namespace rb

@@ -1,0 +1,162 @@
+"""The C-ABI library loads and exports every symbol include/rb.h declares, and rejects
+invalid calls with the documented status before touching the device (no GPU needed:
+validation runs before any HIP call, so these calls never reach a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from residual_binarized_weight_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = _lib.lib
+
+# fake, suitably aligned device addresses: validation must reject before using them
+P = ctypes.c_void_p(0x100000)
+P_MIS = ctypes.c_void_p(0x100004)   # 4-byte aligned only
+P_ODD = ctypes.c_void_p(0x100001)
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "rb.h")).read()
+    return sorted(set(re.findall(r"\b(rb_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert {"rb_pack", "rb_gemv", "rb_gemm_small", "rb_codebook_encode", "rb_codebook_gemv"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), s
+        assert s in _lib.SIGNATURES, f"binding lacks {s}"
+
+
+def test_version_and_status_strings():
+    assert L.rb_version() >= 100
+    for st in range(6):
+        assert L.rb_status_string(st)
+    assert L.rb_status_string(0) == b"RB_OK"
+    assert L.rb_status_string(99) == b"RB_ERR_UNKNOWN"
+
+
+def test_storage_bits_per_weight():
+    assert L.rb_storage_bits_per_weight(4096, 4096, 2, _lib.RB_F16, 1) == 2.015625
+    assert L.rb_storage_bits_per_weight(4096, 4096, 2, _lib.RB_F16, 0) == 2.0 + 16 * 2 * 4096 / 4096 ** 2
+    assert L.rb_storage_bits_per_weight(0, 4096, 2, _lib.RB_F16, 1) == -1.0
+    assert L.rb_storage_bits_per_weight(16, 16, 5, _lib.RB_F16, 1) == -1.0
+
+
+def _pack(**kw):
+    a = dict(W=P, wdt=_lib.RB_F32, N=16, K=64, ldw=64, k=2, group=0, h=None, sdt=_lib.RB_F16,
+             planes=P, ldp=2, g=P, st=None, stream=None)
+    a.update(kw)
+    return L.rb_pack(a["W"], a["wdt"], a["N"], a["K"], a["ldw"], a["k"], a["group"], a["h"], a["sdt"],
+                     a["planes"], a["ldp"], a["g"], a["st"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(planes=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(N=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(K=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(k=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(k=5), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldw=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldp=1), _lib.RB_ERR_INVALID_ARG),
+    (dict(group=3), _lib.RB_ERR_INVALID_ARG),
+    (dict(group=128), _lib.RB_ERR_INVALID_ARG),
+    (dict(group=16, h=P), _lib.RB_ERR_UNSUPPORTED),
+    (dict(wdt=7), _lib.RB_ERR_INVALID_ARG),
+    (dict(sdt=_lib.RB_BF16), _lib.RB_ERR_UNSUPPORTED),
+    (dict(planes=P_MIS), _lib.RB_ERR_MISALIGNED),
+    (dict(W=P_ODD), _lib.RB_ERR_MISALIGNED),
+    (dict(st=P_ODD), _lib.RB_ERR_MISALIGNED),
+])
+def test_pack_rejects(kw, status):
+    assert _pack(**kw) == status
+
+
+def _prod(fn, **kw):
+    a = dict(planes=P, ldp=2, g=P, h=None, sdt=_lib.RB_F16, k=2, N=16, K=64, x=P, xdt=_lib.RB_F16, M=1,
+             y=P, ydt=_lib.RB_F16, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return getattr(L, fn)(a["planes"], a["ldp"], a["g"], a["h"], a["sdt"], a["k"], a["N"], a["K"], a["x"],
+                          a["xdt"], a["M"], a["y"], a["ydt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["rb_gemv", "rb_gemm_small"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(planes=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(x=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(y=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(g=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(k=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(k=5), _lib.RB_ERR_INVALID_ARG),
+    (dict(N=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(M=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldp=1), _lib.RB_ERR_INVALID_ARG),
+    (dict(xdt=9), _lib.RB_ERR_INVALID_ARG),
+    (dict(ydt=_lib.RB_BF16), _lib.RB_ERR_UNSUPPORTED),
+    (dict(planes=P_MIS), _lib.RB_ERR_MISALIGNED),
+    (dict(x=P_MIS), _lib.RB_ERR_MISALIGNED),
+    (dict(y=P_MIS), _lib.RB_ERR_MISALIGNED),
+    (dict(h=P_ODD), _lib.RB_ERR_MISALIGNED),
+])
+def test_product_rejects(fn, kw, status):
+    assert _prod(fn, **kw) == status
+
+
+def test_gemv_batch_limit_and_gemm_constraints():
+    assert _prod("rb_gemv", M=17) == _lib.RB_ERR_UNSUPPORTED
+    assert _prod("rb_gemm_small", M=4097) == _lib.RB_ERR_UNSUPPORTED
+    assert _prod("rb_gemm_small", xdt=_lib.RB_F32) == _lib.RB_ERR_UNSUPPORTED
+    assert _prod("rb_gemm_small", K=96, ldp=3) == _lib.RB_ERR_UNSUPPORTED
+
+
+def test_workspace_too_small_is_reported():
+    for fn, op in (("rb_gemv", _lib.RB_OP_GEMV), ("rb_gemm_small", _lib.RB_OP_GEMM_SMALL)):
+        for (k, N, K, M) in ((2, 4096, 11008, 1), (2, 4096, 4096, 4), (1, 28672, 8192, 64)):
+            need = L.rb_workspace_bytes(op, k, N, K, M)
+            if need == 0:
+                continue
+            ldp = (K + 31) // 32 + ((K + 31) // 32) % 2
+            assert _prod(fn, k=k, N=N, K=K, M=M, ldp=ldp, ws=None, wsb=0) == _lib.RB_ERR_WORKSPACE
+            assert _prod(fn, k=k, N=N, K=K, M=M, ldp=ldp, ws=P, wsb=need - 1) == _lib.RB_ERR_WORKSPACE
+
+
+def test_workspace_bytes_invalid_sizes():
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMV, 0, 16, 16, 1) == 0
+    assert L.rb_workspace_bytes(_lib.RB_OP_PACK, 2, 16, 16, 1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(plane=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(c=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(c=65537), _lib.RB_ERR_INVALID_ARG),
+    (dict(v=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(v=33), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldp=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(plane=P_MIS), _lib.RB_ERR_MISALIGNED),
+    (dict(idx=P_ODD), _lib.RB_ERR_MISALIGNED),
+])
+def test_codebook_encode_rejects(kw, status):
+    a = dict(plane=P, ldp=2, N=4, K=64, C=P, c=16, v=20, idx=P, stream=None)
+    a.update(kw)
+    assert L.rb_codebook_encode(a["plane"], a["ldp"], a["N"], a["K"], a["C"], a["c"], a["v"], a["idx"],
+                                a["stream"]) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(idx=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(group=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(group=12), _lib.RB_ERR_INVALID_ARG),
+    (dict(M=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(M=5), _lib.RB_ERR_UNSUPPORTED),
+    (dict(c=70000), _lib.RB_ERR_INVALID_ARG),
+    (dict(x=P_MIS), _lib.RB_ERR_MISALIGNED),
+])
+def test_codebook_gemv_rejects(kw, status):
+    a = dict(idx=P, C=P, c=16, v=20, s=P, group=16, N=4, K=64, x=P, M=1, y=P, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    assert L.rb_codebook_gemv(a["idx"], a["C"], a["c"], a["v"], a["s"], a["group"], a["N"], a["K"], a["x"],
+                              a["M"], a["y"], a["ws"], a["wsb"], a["stream"]) == status

@@ -1,0 +1,125 @@
+"""GPU parity of rb_gemv (and cross-feeding with rb_pack) against the CPU oracle:
+|y - y_ref| <= 1e-3 * sum|terms| for every output."""
+import numpy as np
+import pytest
+import torch
+
+import residual_binarized_weight_amd as rb
+import workloads as wl
+from oracle import rb_oracle as O
+from tests.gpu_util import assert_product_close, dev, planes_np, scales_np, to_dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs the GPU")]
+
+
+def oracle_case(W, k, h=None, fmt="f16"):
+    res = O.binarize(W, k, h=h, scale_fmt=fmt)
+    return res["planes"], res["g"]
+
+
+def gpu_gemv(planes, g, h, x, K, y_dtype=torch.float16, fmt="f16", ldp=None):
+    k, N, Kw = planes.shape
+    if ldp is not None and ldp != Kw:
+        pad = np.zeros((k, N, ldp), dtype=np.uint32)
+        pad[:, :, :Kw] = planes
+        planes = pad
+    sdt = np.float16 if fmt == "f16" else np.float32
+    pd = to_dev(planes)
+    gd = to_dev(g.reshape(k, N).astype(sdt))
+    hd = None if h is None else to_dev(h.astype(sdt))
+    xd = to_dev(x)
+    y = rb.gemv(pd, gd, hd, xd, K, y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy()
+
+
+def test_gemv_tiny_fp32():
+    W = wl.weights_for("tiny")
+    x = wl.activations_for("tiny", 1)
+    planes, g = oracle_case(W, 1, fmt="f32")
+    y = gpu_gemv(planes, g, None, x, 512, y_dtype=torch.float32, fmt="f32")
+    y_ref, sabs = O.gemv(planes, g, None, x, 512)
+    assert_product_close(y, y_ref, sabs, fp16_out=False)
+    # config special case: y = alpha (.) (B x)
+    B = O.unpack_bits(planes[0], 512)
+    assert np.allclose(y_ref[0], g[0, :, 0] * (B @ x[0].astype(np.float64)), rtol=1e-12, atol=1e-12)
+
+
+def test_gemv_square_m1():
+    W = wl.weights_for("square")
+    x = wl.activations_for("square", 1)
+    planes, g = oracle_case(W, 2)
+    y = gpu_gemv(planes, g, None, x, 4096)
+    y_ref, sabs = O.gemv(planes, g, None, x, 4096)
+    assert_product_close(y, y_ref, sabs)
+
+
+@pytest.mark.parametrize("name", ["down", "gateup"])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_gemv_mlp(name, M):
+    W = wl.weights_for(name)
+    N, K = W.shape
+    rows = np.arange(N) if M == 1 else np.random.default_rng(M).choice(N, 1024, replace=False)
+    # pack on the GPU (all rows), compare the product against the oracle on the GPU's planes
+    Wd = torch.from_numpy(W).to(dev())
+    planes_d, g_d = rb.pack(Wd, 2)
+    x = wl.activations_for(name, M)
+    y = rb.gemv(planes_d, g_d, None, to_dev(x), K).float().cpu().numpy()
+    planes = planes_np(planes_d, K)
+    g = scales_np(g_d, 2, N)
+    y_ref, sabs = O.gemv(planes[:, rows], g[:, rows], None, x, K)
+    assert_product_close(y[:, rows], y_ref, sabs)
+
+
+@pytest.mark.parametrize("K", [1, 31, 33, 1000, 2049, 4099])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 3])
+def test_gemv_ragged(K, k, M):
+    N = 37
+    W = wl.heavy_tailed_weights(70 + k, N, K)
+    x = wl.activations(71, M, K)
+    planes, g = oracle_case(W, k)
+    y = gpu_gemv(planes, g, None, x, K)
+    y_ref, sabs = O.gemv(planes, g, None, x, K)
+    assert_product_close(y, y_ref, sabs)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "f32"])
+def test_gemv_general_h_fp32_x(fmt):
+    K, N, k = 1500, 70, 3
+    W = wl.heavy_tailed_weights(72, N, K)
+    sdt = np.float16 if fmt == "f16" else np.float32
+    h = wl.random_scales(11, k, K, negative_frac=0.3, dtype=sdt)
+    x = wl.activations(73, 2, K, dtype=np.float32)
+    planes, g = oracle_case(W, k, h=h, fmt=fmt)
+    y = gpu_gemv(planes, g, h, x, K, y_dtype=torch.float32, fmt=fmt)
+    y_ref, sabs = O.gemv(planes, g, h, x, K)
+    assert_product_close(y, y_ref, sabs, fp16_out=False)
+
+
+def test_gemv_single_row_and_padded_ldp():
+    K = 700
+    W = wl.heavy_tailed_weights(74, 1, K)
+    x = wl.activations(75, 1, K)
+    planes, g = oracle_case(W, 2)
+    y = gpu_gemv(planes, g, None, x, K, ldp=40)
+    y_ref, sabs = O.gemv(planes, g, None, x, K)
+    assert_product_close(y, y_ref, sabs)
+
+
+def test_gemv_writes_nothing_past_y_and_is_deterministic():
+    W = wl.weights_for("square", N=600, K=1000)
+    x = wl.activations(76, 2, 1000)
+    planes, g = oracle_case(W, 2)
+    pd, gd, xd = to_dev(planes), to_dev(g.reshape(2, 600).astype(np.float16)), to_dev(x)
+    buf = torch.full((2 * 600 + 64,), 12345.0, dtype=torch.float16, device=dev())
+    y = buf[:1200].view(2, 600)
+    rb.gemv(pd, gd, None, xd, 1000, y=y)
+    y1 = y.clone()
+    rb.gemv(pd, gd, None, xd, 1000, y=y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[1200:] == 12345.0)
+    assert torch.equal(y1, y)
+    y_ref, sabs = O.gemv(planes, g, None, x, 1000)
+    assert_product_close(y.float().cpu().numpy(), y_ref, sabs)

@@ -35,6 +35,7 @@ SIGNATURES = {
                                         _vp, _sz, _vp]),
     # streaming-read probe used by the bench (not part of the method)
     "rb_bench_stream_read": (ctypes.c_int, [_vp, _i64, _vp, _i32, _vp]),
+    "rb_bench_spin": (ctypes.c_int, [ctypes.c_double, _vp]),
 }
 
 

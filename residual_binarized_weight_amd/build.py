@@ -1,6 +1,7 @@
 """Build librb.so (all HIP sources for gfx950) in place, next to this file.
 
-Usage: python -m residual_binarized_weight_amd.build  (or build() from Python).
+Usage: python residual_binarized_weight_amd/build.py  (run by path: importing the package
+would first load the previously built library).
 Every HIP source is compiled with hipcc for gfx950 only; packed fp32 instructions are
 disabled at the code-generation level (-packed-fp32-ops), then the objects are linked
 into one shared library that exports the C ABI declared in include/rb.h.

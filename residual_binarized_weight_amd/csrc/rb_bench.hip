@@ -35,3 +35,21 @@ extern "C" int rb_bench_stream_read(const void* src, int64_t bytes, uint32_t* si
       static_cast<const u32x4*>(src), bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
+
+namespace {
+
+// One wave that returns once the device's 100 MHz real-time counter has advanced by
+// `ticks` (a bounded wait: it always ends). Queued ahead of a batch of timed launches, it
+// keeps the GPU busy while the host enqueues them, so they then run back to back.
+__global__ void spin_kernel(uint64_t ticks) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(10);
+}
+
+}  // namespace
+
+extern "C" int rb_bench_spin(double microseconds, void* stream) {
+  if (!(microseconds >= 0.0) || microseconds > 1.0e6) return 1;
+  spin_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>((uint64_t)(microseconds * 100.0));
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}

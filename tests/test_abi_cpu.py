@@ -114,8 +114,10 @@ def test_gemv_batch_limit_and_gemm_constraints():
 
 
 def test_workspace_too_small_is_reported():
+    cases = {"rb_gemv": ((2, 4096, 11008, 1), (2, 4096, 4096, 4), (1, 11008, 4096, 16)),
+             "rb_gemm_small": ((2, 4096, 4096, 64), (1, 28672, 8192, 64), (2, 28672, 8192, 256))}
     for fn, op in (("rb_gemv", _lib.RB_OP_GEMV), ("rb_gemm_small", _lib.RB_OP_GEMM_SMALL)):
-        for (k, N, K, M) in ((2, 4096, 11008, 1), (2, 4096, 4096, 4), (1, 28672, 8192, 64)):
+        for (k, N, K, M) in cases[fn]:
             need = L.rb_workspace_bytes(op, k, N, K, M)
             if need == 0:
                 continue

@@ -141,7 +141,11 @@ rb_status rb_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void
  *   of each plane are expanded to +-h_i fp16 tiles and multiplied with the fp16
  *   activations (fp32 accumulation); y = sum_i g_i (.) acc_i.
  *   Arguments as rb_gemv, except: x_dtype must be RB_F16; 1 <= M <= 4096; K must be a
- *   multiple of 64 and ldp a multiple of 2.
+ *   multiple of 64 and at most 2^22, ldp even and at most 2^20; a non-NULL h must be RB_F16 (scale_dtype
+ *   RB_F16, else RB_ERR_UNSUPPORTED) and 16-byte aligned. Rows of y past M and columns
+ *   past N are not written. No workspace (rb_workspace_bytes returns 0).
+ *   With fp16 g and h = NULL, +-g_i itself is the expanded operand and all planes share
+ *   one accumulator; otherwise each plane's sum is scaled by g_i in fp32.
  */
 rb_status rb_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                         rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,

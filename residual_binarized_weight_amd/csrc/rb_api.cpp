@@ -128,7 +128,9 @@ rb_status rb_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, cons
   if (st != RB_OK) return st;
   if (x_dtype != RB_F16) return RB_ERR_UNSUPPORTED;
   if (K % 64 != 0 || ldp % 2 != 0) return RB_ERR_UNSUPPORTED;
-  if (h && !aligned(h, scale_dtype == RB_F32 ? 4 : 2)) return RB_ERR_MISALIGNED;
+  if (K > (int64_t(1) << 22) || ldp > (int64_t(1) << 20)) return RB_ERR_UNSUPPORTED;  // 32-bit offsets
+  if (h && scale_dtype != RB_F16) return RB_ERR_UNSUPPORTED;  // h enters the fp16 operand
+  if (h && !aligned(h, 16)) return RB_ERR_MISALIGNED;
   const size_t need = rb::gemm_small_workspace_bytes(k, N, K, M);
   if (need > 0 && (!ws || ws_bytes < need)) return RB_ERR_WORKSPACE;
   log_call("rb_gemm_small", N, K, M, k);

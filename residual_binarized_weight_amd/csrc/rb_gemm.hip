@@ -1,14 +1,358 @@
-// rb_gemm.hip -- batched product on the matrix cores (gfx950 MFMA). Work in progress.
+// rb_gemm.hip -- batched product on the matrix cores (gfx950 MFMA).
+//
+// [RaBiT summary page, background "Residual binarization"] y = sum_i g_i (.) (B_i (h_i (.) x))
+// for a batch of activation rows X [M][K]. For batches that can feed the matrix cores, the
+// bits of each plane are expanded in registers into the fp16 B operand of
+// v_mfma_f32_32x32x16_f16 (A = activations staged in LDS), with fp32 accumulation.
+//
+// Operand order. The MFMA contracts its 16 K slots in any order, as long as A and B agree,
+// so the slots are permuted to make the bit expansion cheap: within a 32-column word,
+// operand dword e of lane half hh at k-step t holds columns j and j+16 with
+// j = 8t + 4hh + e, i.e. bits j and j+16, which one left shift by 15-j moves onto the two
+// fp16 sign positions (15, 31). One AND-OR (or AND-XOR) then puts the sign on a fixed
+// magnitude pair:
+//   fold mode  (fp16 g, h = 1): +-|g_i[n]|, the sign of g folded into the bits; every
+//              plane then adds into the same fp32 accumulator (products are exact)
+//   ones mode  (fp32 g, h = 1): +-1, and y += g_i * acc_i in fp32 after each plane
+//   h mode     (fp16 g and h):  +-h_i[c], and y += g_i * acc_i in fp32 after each plane
+// The activations are staged in LDS in the same permuted order, 128 columns per stage,
+// rows padded to 272 B so the 16-byte A reads of consecutive rows hit distinct banks.
+//
+// Tiles: a block is 4 waves; wave w owns 32 weight rows (one MFMA column tile) and the MT
+// 32-row batch tiles of its block, so each expanded B operand feeds MT MFMAs and each A
+// read feeds one MFMA per plane. Plane words are prefetched kDepth stages ahead in
+// registers; the next activation stage is loaded into registers while the current one is
+// multiplied, then written to the other LDS buffer (one barrier per stage).
 #include "rb_device.hpp"
 #include "rb_internal.h"
 
 namespace rb {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2g __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4g __attribute__((ext_vector_type(4)));
+
+constexpr int kGemmWaves = 4;
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kGemmTileN = 32 * kGemmWaves;     // weight rows per block
+constexpr int kStageCols = 128;                 // columns per stage: 4 words per plane row
+constexpr int kStageWords = kStageCols / 32;
+constexpr int kRowBytes = kStageCols * 2 + 16;  // 16 groups of 16 B + pad
+constexpr int kDepth = 4;                       // plane-word prefetch distance in stages
+
+enum { kModeFold = 0, kModeOnes = 1, kModeH = 2 };
+
+template <typename T> __device__ __forceinline__ void gemm_store(T* p, float v);
+template <> __device__ __forceinline__ void gemm_store<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void gemm_store<__half>(__half* p, float v) { *p = __float2half_rn(v); }
+
+template <typename TS> __device__ __forceinline__ float scale_f32(const TS* p);
+template <> __device__ __forceinline__ float scale_f32<__half>(const __half* p) { return __half2float(*p); }
+template <> __device__ __forceinline__ float scale_f32<float>(const float* p) { return *p; }
+
+// two groups (hh = 0, 1) of word w, k-step t from 8 consecutive values at column 32w + 8t
+// (lo) and 8 at column 32w + 8t + 16 (hi): dword e of group hh = (lo[4hh + e], hi[4hh + e])
+__device__ __forceinline__ void interleave(const u32x4g lo, const u32x4g hi, u32x4g& g0, u32x4g& g1) {
+  g0[0] = __builtin_amdgcn_perm(hi[0], lo[0], 0x05040100u);
+  g0[1] = __builtin_amdgcn_perm(hi[0], lo[0], 0x07060302u);
+  g0[2] = __builtin_amdgcn_perm(hi[1], lo[1], 0x05040100u);
+  g0[3] = __builtin_amdgcn_perm(hi[1], lo[1], 0x07060302u);
+  g1[0] = __builtin_amdgcn_perm(hi[2], lo[2], 0x05040100u);
+  g1[1] = __builtin_amdgcn_perm(hi[2], lo[2], 0x07060302u);
+  g1[2] = __builtin_amdgcn_perm(hi[3], lo[3], 0x05040100u);
+  g1[3] = __builtin_amdgcn_perm(hi[3], lo[3], 0x07060302u);
+}
+
+// buffer resource over [base, base + bytes): loads at or past `bytes` return 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0x7fffffffll ? 0x7fffffffu : (uint32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every resource above
+
+__device__ __forceinline__ u32x4g buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4g, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// activation stage in registers: MT units per thread, unit q = (row, word w, k-step t)
+template <int MT>
+struct XStage {
+  u32x4g lo[MT], hi[MT];
+};
+
+// rows past M and columns past K read as 0 (the resource ends at the block's last row;
+// a column past K gets an out-of-range offset)
+template <int MT>
+__device__ __forceinline__ void load_x_stage(XStage<MT>& r, __amdgpu_buffer_rsrc_t rx, int64_t K, int64_t k0,
+                                             int tid) {
+#pragma unroll
+  for (int u = 0; u < MT; ++u) {
+    const int q = tid + u * kGemmThreads;  // 0 .. 256 MT - 1
+    const int row = q >> 3, wt = q & 7;    // wt = 2 w + t
+    const int64_t c = k0 + 32 * (wt >> 1) + 8 * (wt & 1);
+    const uint32_t off = c < K ? (uint32_t)((row * K + c) * 2) : kOob;
+    r.lo[u] = buf_load16(rx, off);
+    r.hi[u] = buf_load16(rx, off + 32u);
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void store_x_stage(const XStage<MT>& r, uint8_t* buf, int tid) {
+#pragma unroll
+  for (int u = 0; u < MT; ++u) {
+    const int q = tid + u * kGemmThreads;
+    const int row = q >> 3, wt = q & 7;
+    u32x4g g0, g1;
+    interleave(r.lo[u], r.hi[u], g0, g1);
+    // group index 4 w + 2 t + hh = 2 wt + hh
+    *reinterpret_cast<u32x4g*>(buf + row * kRowBytes + (2 * wt) * 16) = g0;
+    *reinterpret_cast<u32x4g*>(buf + row * kRowBytes + (2 * wt + 1) * 16) = g1;
+  }
+}
+
+// h stage (h mode): one plane's h over the stage, in the same 16 groups; every thread
+// loads the unit of tid % 8 (so no load sits in a branch) and threads 0..7 store it.
+// Columns past K read as 0.
+struct HStage {
+  u32x4g lo, hi;
+};
+
+__device__ __forceinline__ void load_h_stage(HStage& r, __amdgpu_buffer_rsrc_t rh, int64_t K, int64_t k0, int tid) {
+  const int u = tid & 7;
+  const int64_t c = k0 + 32 * (u >> 1) + 8 * (u & 1);
+  const uint32_t off = c < K ? (uint32_t)(c * 2) : kOob;
+  r.lo = buf_load16(rh, off);
+  r.hi = buf_load16(rh, off + 32u);
+}
+
+__device__ __forceinline__ void store_h_stage(const HStage& r, uint8_t* hbuf, int tid) {
+  if (tid < 8) {
+    u32x4g g0, g1;
+    interleave(r.lo, r.hi, g0, g1);
+    *reinterpret_cast<u32x4g*>(hbuf + (2 * tid) * 16) = g0;
+    *reinterpret_cast<u32x4g*>(hbuf + (2 * tid + 1) * 16) = g1;
+  }
+}
+
+// B operand from complemented bits `nw` at k-step t, lane half hh: dword e carries the
+// signs of bits j, j+16 (j = 8t + 4hh + e) on the magnitude pair base[e]
+template <int MODE>
+__device__ __forceinline__ h8 expand_b(uint32_t nw, int t, int hh, u32x4g base) {
+  u32x4g d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 8 * t + 4 * hh + e;
+    const uint32_t sgn = (nw << (15 - j)) & 0x80008000u;
+    d[e] = MODE == kModeH ? (base[e] ^ sgn) : (base[e] | sgn);
+  }
+  return __builtin_bit_cast(h8, d);
+}
+
+// KP = planes multiplied per pass (fold mode: all k; otherwise 1).
+// Stages run in groups of kDepth with no branch inside a group: the plane words of a
+// stage past the end (or past K in a 64-column tail) are whatever the row holds there,
+// and they meet activations that read as 0, so they add +-0 (a non-finite g, which no
+// finite W packs to, would turn that row's +-0 into NaN).
+template <typename TS, typename TY, int MT, int MODE, int KP>
+__global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
+    const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, const __half* __restrict__ h,
+    int k, int64_t N, int64_t K, const __half* __restrict__ x, int64_t M, TY* __restrict__ y) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* const xbuf0 = smem;
+  uint8_t* const xbuf1 = smem + MT * 32 * kRowBytes;
+  uint8_t* const hbuf0 = smem + 2 * MT * 32 * kRowBytes;
+  uint8_t* const hbuf1 = hbuf0 + 256;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps resources scalar
+  const int nl = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t n0 = (int64_t)blockIdx.x * kGemmTileN + wave * 32;  // wave's first row
+  const int64_t n = n0 + nl;
+  const int64_t nc = n < N ? n : N - 1;  // rows past N repeat the last row and are not stored
+  const int64_t rb = n0 < N ? n0 : N - 1;
+  const int64_t m_base = (int64_t)blockIdx.y * MT * 32;
+  const int64_t m_rows = M - m_base < MT * 32 ? M - m_base : MT * 32;
+  const int nch = (int)((K + kStageCols - 1) / kStageCols);
+  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(x + m_base * K, m_rows * K * 2);
+  const uint32_t lane_off = (uint32_t)((nc - rb) * ldp * 4);
+
+  f32x16 yacc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) yacc[mt] = (f32x16){};
+
+  const int passes = MODE == kModeFold ? 1 : k;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int i0 = MODE == kModeFold ? 0 : pass;
+    __amdgpu_buffer_rsrc_t rw[KP];
+    u32x4g base[KP];
+    uint32_t gsgn[KP];
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+      const int i = i0 + p;
+      const int64_t first = (int64_t)i * N + rb;
+      rw[p] = gemm_rsrc(planes + first * ldp, ((int64_t)k * N - first) * ldp * 4);
+      if (MODE == kModeFold) {
+        const uint32_t gb = (uint32_t)__half_as_ushort(*reinterpret_cast<const __half*>(g + (int64_t)i * N + nc));
+        const uint32_t mag = gb & 0x7fffu;
+        const uint32_t pair = mag | (mag << 16);
+        base[p] = (u32x4g){pair, pair, pair, pair};
+        gsgn[p] = (gb & 0x8000u) ? 0xffffffffu : 0u;
+      } else {
+        base[p] = (u32x4g){0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // +-1
+        gsgn[p] = 0u;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rh = gemm_rsrc(MODE == kModeH ? h + (int64_t)i0 * K : x, K * 2);
+
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x16){};
+
+    // prologue: plane words of stages 0 .. kDepth-1, activation stage 0
+    u32x4g wr[kDepth][KP];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+#pragma unroll
+      for (int p = 0; p < KP; ++p) wr[d][p] = buf_load16(rw[p], lane_off + 16u * d);
+    {
+      XStage<MT> xs0;
+      HStage hs0;
+      load_x_stage<MT>(xs0, rx, K, 0, tid);
+      if (MODE == kModeH) load_h_stage(hs0, rh, K, 0, tid);
+      __syncthreads();  // the previous pass may still read buffer 0
+      store_x_stage<MT>(xs0, xbuf0, tid);
+      if (MODE == kModeH) store_h_stage(hs0, hbuf0, tid);
+      __syncthreads();
+    }
+
+    for (int cb = 0; cb < nch; cb += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int c = cb + d;
+        u32x4g cur[KP];
+#pragma unroll
+        for (int p = 0; p < KP; ++p) cur[p] = wr[d][p];
+        XStage<MT> xn;
+        HStage hn;
+        load_x_stage<MT>(xn, rx, K, (int64_t)(c + 1) * kStageCols, tid);
+        if (MODE == kModeH) load_h_stage(hn, rh, K, (int64_t)(c + 1) * kStageCols, tid);
+#pragma unroll
+        for (int p = 0; p < KP; ++p) wr[d][p] = buf_load16(rw[p], lane_off + 16u * (uint32_t)(c + kDepth));
+        // keep the loads at the top of the stage: they must be in flight during its MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+
+        const uint8_t* xb = (d & 1) ? xbuf1 : xbuf0;  // kDepth is even: stage parity = d parity
+        const uint8_t* hb = (d & 1) ? hbuf1 : hbuf0;
+#pragma unroll
+        for (int w = 0; w < kStageWords; ++w) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int r = 4 * w + 2 * t + hh;
+            h8 a[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              a[mt] = *reinterpret_cast<const h8*>(xb + (mt * 32 + nl) * kRowBytes + r * 16);
+            u32x4g hbase = base[0];
+            if (MODE == kModeH) hbase = *reinterpret_cast<const u32x4g*>(hb + r * 16);
+#pragma unroll
+            for (int p = 0; p < KP; ++p) {
+              const uint32_t nwd = ~cur[p][w] ^ gsgn[p];
+              const h8 b = expand_b<MODE>(nwd, t, hh, MODE == kModeH ? hbase : base[p]);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt], b, acc[mt], 0, 0, 0);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        store_x_stage<MT>(xn, (d & 1) ? xbuf0 : xbuf1, tid);
+        if (MODE == kModeH) store_h_stage(hn, (d & 1) ? hbuf0 : hbuf1, tid);
+        __syncthreads();
+      }
+    }
+
+    if (MODE == kModeFold) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) yacc[mt] = acc[mt];
+    } else {
+      const float gi = scale_f32<TS>(g + (int64_t)i0 * N + nc);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) yacc[mt] += gi * acc[mt];
+    }
+  }
+
+  // D of the 32x32 MFMA: lane l holds column n = l % 32 of the tile, element j holds
+  // batch row 8 (j / 4) + 4 (l / 32) + j % 4
+  if (n < N) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t m = m_base + mt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+        if (m < M) gemm_store<TY>(&y[m * N + n], yacc[mt][j]);
+      }
+    }
+  }
+}
+
+template <int MT>
+constexpr size_t gemm_lds_bytes() {
+  return (size_t)2 * MT * 32 * kRowBytes + 512;
+}
+
+template <typename TS, typename TY, int MT, int MODE, int KP>
+hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
+                      int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
+  constexpr size_t lds = gemm_lds_bytes<MT>();
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)gemm_small_kernel<TS, TY, MT, MODE, KP>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned gx = (unsigned)((N + kGemmTileN - 1) / kGemmTileN);
+  const unsigned gy = (unsigned)((M + 32 * MT - 1) / (32 * MT));
+  gemm_small_kernel<TS, TY, MT, MODE, KP><<<dim3(gx, gy), kGemmThreads, lds, s>>>(
+      planes, ldp, static_cast<const TS*>(g), static_cast<const __half*>(h), k, N, K,
+      static_cast<const __half*>(x), M, static_cast<TY*>(y));
+  return hipGetLastError();
+}
+
+template <typename TS, typename TY, int MODE, int KP>
+hipError_t launch_mt(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
+                     int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
+  if (M <= 32) return launch_one<TS, TY, 1, MODE, KP>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if (M <= 64) return launch_one<TS, TY, 2, MODE, KP>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  return launch_one<TS, TY, 4, MODE, KP>(planes, ldp, g, h, k, N, K, x, M, y, s);
+}
+
+template <typename TY>
+hipError_t launch_y(rb_dtype scale_dtype, const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                    int k, int64_t N, int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
+  if (h != nullptr) return launch_mt<__half, TY, kModeH, 1>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if (scale_dtype == RB_F32) return launch_mt<float, TY, kModeOnes, 1>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  switch (k) {
+    case 1: return launch_mt<__half, TY, kModeFold, 1>(planes, ldp, g, h, k, N, K, x, M, y, s);
+    case 2: return launch_mt<__half, TY, kModeFold, 2>(planes, ldp, g, h, k, N, K, x, M, y, s);
+    case 3: return launch_mt<__half, TY, kModeFold, 3>(planes, ldp, g, h, k, N, K, x, M, y, s);
+    default: return launch_mt<__half, TY, kModeFold, 4>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  }
+}
+
+}  // namespace
 
 size_t gemm_small_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
 
-hipError_t launch_gemm_small(const uint32_t*, int64_t, const void*, const void*, rb_dtype, int, int64_t,
-                             int64_t, const void*, int64_t, void*, rb_dtype, void*, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                             rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x, int64_t M,
+                             void* y, rb_dtype y_dtype, void*, hipStream_t s) {
+  if (y_dtype == RB_F16) return launch_y<__half>(scale_dtype, planes, ldp, g, h, k, N, K, x, M, y, s);
+  return launch_y<float>(scale_dtype, planes, ldp, g, h, k, N, K, x, M, y, s);
 }
 
 }  // namespace rb

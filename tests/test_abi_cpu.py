@@ -111,6 +111,11 @@ def test_gemv_batch_limit_and_gemm_constraints():
     assert _prod("rb_gemm_small", M=4097) == _lib.RB_ERR_UNSUPPORTED
     assert _prod("rb_gemm_small", xdt=_lib.RB_F32) == _lib.RB_ERR_UNSUPPORTED
     assert _prod("rb_gemm_small", K=96, ldp=3) == _lib.RB_ERR_UNSUPPORTED
+    assert _prod("rb_gemm_small", K=(1 << 22) + 64, ldp=(1 << 17) + 2) == _lib.RB_ERR_UNSUPPORTED
+    assert _prod("rb_gemm_small", ldp=(1 << 20) + 2) == _lib.RB_ERR_UNSUPPORTED
+    # h enters the fp16 MFMA operand: fp32 h is refused, and h must be 16-byte aligned
+    assert _prod("rb_gemm_small", h=P, sdt=_lib.RB_F32) == _lib.RB_ERR_UNSUPPORTED
+    assert _prod("rb_gemm_small", h=ctypes.c_void_p(0x100002)) == _lib.RB_ERR_MISALIGNED
 
 
 def test_workspace_too_small_is_reported():

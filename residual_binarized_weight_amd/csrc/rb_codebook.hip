@@ -102,6 +102,191 @@ __global__ __launch_bounds__(256) void codebook_gemv_kernel(
   if (lane == 0) y[m * N + n] = __float2half_rn(acc);
 }
 
+// ---------------------------------------------------------------------------
+// LUT product (M = 1, v = 20, group = 16).
+//
+// [BTC 2.1.2] LUT-GEMM replaces the dequantised dot product by sums of input blocks that
+// are precomputed once and then accumulated by weight pattern. Here the precomputed sums
+// are nibble tables over x: for every 4 consecutive columns, T[e] = sum_j (bit j of e ? +x
+// : -x) over the 4 columns, for all 16 sign patterns e (the +-1 form, so no separate sum of
+// x is needed). The codeword patterns of a row, concatenated, are exactly its sign bits; a
+// 16-column scale group is 4 nibbles, so
+//   y[n] = sum_q s[n][q] * (T[e_4q] + T[e_4q+1] + T[e_4q+2] + T[e_4q+3]).
+// An 80-column unit (lcm of v = 20 and group = 16) is 4 codewords, 5 scale groups and 20
+// nibbles; lane l of a row's wave takes units l and l + 64 of a phase.
+//
+// Layout: entry e of every table of a phase lies in one 8 KB row of LDS (entry-major),
+// table slot 21 u + i for nibble i of unit u (20 nibbles + 1 pad slot per unit). The slot
+// stride 21 is odd, so the 64 lanes of a wave, which read the same nibble i of 64
+// consecutive units, hit 64 different banks whatever the pattern values; a lookup address is
+// (e << 13) + 84 u + 4 i (4 i is the instruction's immediate offset).
+//
+// A block is 16 waves, one output row each, and runs the whole row: at most two phases of
+// up to 97 units (15520 columns) whose tables are rebuilt in place, so the result needs no
+// cross-block reduction, is deterministic and uses no workspace.
+// ---------------------------------------------------------------------------
+constexpr int kCbThreads = 1024;
+constexpr int kCbRowsPerBlock = kCbThreads / 64;
+constexpr int kCbUnitCols = 80;
+constexpr int kCbSlots = 21;
+constexpr int kCbEntryShift = 13;                                   // 8 KB per entry row
+constexpr int kCbMaxUnits = (1 << kCbEntryShift) / (4 * kCbSlots);  // 97 units per phase
+constexpr size_t kCbLdsBytes = (size_t)16 << kCbEntryShift;          // 128 KB
+
+typedef uint32_t cb_u32x2 __attribute__((ext_vector_type(2)));
+
+// the 16 +-x sums of one nibble table, written to its slot (x4: the 4 columns' activations)
+__device__ __forceinline__ void cb_build_table(const float x4[4], uint32_t slot) {
+  float lo[4], hi[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo[e] = ((e & 1) ? x4[0] : -x4[0]) + ((e & 2) ? x4[1] : -x4[1]);
+    hi[e] = ((e & 1) ? x4[2] : -x4[2]) + ((e & 2) ? x4[3] : -x4[3]);
+  }
+  typedef __attribute__((address_space(3))) float lds_f32p;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    *(lds_f32p*)(size_t)(((uint32_t)e << kCbEntryShift) + slot * 4u) = lo[e & 3] + hi[e >> 2];
+}
+
+// 4 fp16 activations of one table from a b64 load; columns >= K are 0
+__device__ __forceinline__ void cb_x4(cb_u32x2 raw, int64_t col0, int64_t K, float x4[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t h = (raw[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+    x4[j] = col0 + j < K ? __half2float(__ushort_as_half((uint16_t)h)) : 0.0f;
+  }
+}
+
+// address of the nibble at bit 4i of d (i < 8) within entry-major tables: (nibble << 13) | base
+template <int I>
+__device__ __forceinline__ uint32_t cb_addr(uint32_t d, uint32_t base) {
+  constexpr int sh = 4 * I;
+  const uint32_t t = sh <= kCbEntryShift ? (d << (kCbEntryShift - sh)) : (d >> (sh - kCbEntryShift));
+  return (t & (15u << kCbEntryShift)) | base;
+}
+
+// table value of nibble I of a unit (I < 20; nibble I lives in dword I / 8 at bit 4 (I % 8))
+template <int I>
+__device__ __forceinline__ float cb_nib(const uint32_t d[3], uint32_t base) {
+  return lds_f32(cb_addr<I % 8>(d[I / 8], base) + 4u * I);
+}
+
+// +-x sum of the 16 columns of scale group R of a unit (nibbles 4R .. 4R+3)
+template <int R>
+__device__ __forceinline__ float cb_group(const uint32_t d[3], uint32_t base) {
+  return (cb_nib<4 * R>(d, base) + cb_nib<4 * R + 1>(d, base)) +
+         (cb_nib<4 * R + 2>(d, base) + cb_nib<4 * R + 3>(d, base));
+}
+
+template <int NPH>
+__global__ __launch_bounds__(kCbThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void codebook_lut_kernel(
+    const uint16_t* __restrict__ idx, const uint32_t* __restrict__ codebook, int c,
+    const __half* __restrict__ s, int64_t N, int64_t K, const __half* __restrict__ x, __half* __restrict__ y,
+    int units_per_phase) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n = (int64_t)blockIdx.x * kCbRowsPerBlock + wave;
+  const int64_t nb = (K + 19) / 20;   // codeword blocks per row
+  const int64_t G = (K + 15) / 16;    // scale groups per row
+  const int UP = units_per_phase;
+  const uint32_t OOB = 0x80000000u;
+
+  // resources: x (whole dwords, the tail column masked below), this wave's idx and scale rows
+  // (a row past N has no bytes, so it reads 0), the codebook
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)(((K * 2) + 3) & ~3ll));
+  const __amdgpu_buffer_rsrc_t ri = buffer_rsrc(idx + (n < N ? n : 0) * nb, n < N ? (uint32_t)(nb * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(s + (n < N ? n : 0) * G, n < N ? (uint32_t)(G * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codebook, (uint32_t)c * 4u);
+
+  // 1. activations of this thread's tables (tables t and t + 1024 of each phase)
+  cb_u32x2 xr[NPH][2];
+#pragma unroll
+  for (int ph = 0; ph < NPH; ++ph)
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int p = tid + it * kCbThreads;
+      const int64_t nib = (int64_t)20 * ph * UP + p;  // global nibble index
+      const uint32_t off = p < 20 * UP ? (uint32_t)(nib * 8) : OOB;
+      xr[ph][it] = __builtin_bit_cast(cb_u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (int)off, 0, 0));
+    }
+  // activations first, in every wave, then the row data: requests return in order and the
+  // table build must not wait behind the index stream
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. indices and scales of this lane's units
+  uint32_t id[NPH][2][4], sc[NPH][2][5];
+#pragma unroll
+  for (int ph = 0; ph < NPH; ++ph)
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int ul = lane + 64 * it;
+      const int64_t ug = (int64_t)ph * UP + ul;
+      const bool ok = ul < UP;  // units past the row end read 0 through the row resources
+#pragma unroll
+      for (int r = 0; r < 4; ++r) id[ph][it][r] = buf_u16(ri, ok ? (uint32_t)((4 * ug + r) * 2) : OOB, 0);
+#pragma unroll
+      for (int r = 0; r < 5; ++r) sc[ph][it][r] = buf_u16(rs, ok ? (uint32_t)((5 * ug + r) * 2) : OOB, 0);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. codewords (indices are < c by contract; clamped so a bad index cannot read past the codebook)
+  uint32_t cw[NPH][2][4];
+#pragma unroll
+  for (int ph = 0; ph < NPH; ++ph)
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t i = id[ph][it][r] < (uint32_t)c ? id[ph][it][r] : (uint32_t)(c - 1);
+        cw[ph][it][r] = buf_u32(rc, i * 4u, 0);
+      }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float acc = 0.0f;
+#pragma unroll
+  for (int ph = 0; ph < NPH; ++ph) {
+    // 4. tables of this phase (after every wave is done with the previous phase's)
+    if (ph > 0) __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      // threads past the phase's tables write the pad slot of unit 0, which no lookup reads
+      // (no branch: the activation loads above must not sink into one)
+      const int p = tid + it * kCbThreads;
+      const int u = p / 20, i = p - 20 * (p / 20);
+      float x4[4];
+      cb_x4(xr[ph][it], (int64_t)4 * (20 * (int64_t)ph * UP + p), K, x4);
+      cb_build_table(x4, p < 20 * UP ? (uint32_t)(kCbSlots * u + i) : (uint32_t)(kCbSlots - 1));
+    }
+    __syncthreads();
+    // 5. lookups: per unit 20 nibbles in 5 scale groups
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int ul = lane + 64 * it;
+      if (ul < UP) {
+        uint32_t w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = cw[ph][it][r] & 0xfffffu;
+        const uint32_t d[3] = {w[0] | (w[1] << 20), (w[1] >> 12) | (w[2] << 8) | (w[3] << 28), w[3] >> 4};
+        const uint32_t base = (uint32_t)(kCbSlots * 4 * ul);
+        float sf[5];
+#pragma unroll
+        for (int r = 0; r < 5; ++r) sf[r] = __half2float(__ushort_as_half((uint16_t)sc[ph][it][r]));
+        acc += sf[0] * cb_group<0>(d, base);
+        acc += sf[1] * cb_group<1>(d, base);
+        acc += sf[2] * cb_group<2>(d, base);
+        acc += sf[3] * cb_group<3>(d, base);
+        acc += sf[4] * cb_group<4>(d, base);
+      }
+    }
+  }
+  acc = wave_sum_dpp(acc);
+  if (lane == 63 && n < N) y[n] = __float2half_rn(acc);
+}
+
 }  // namespace
 
 hipError_t launch_codebook_encode(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K,
@@ -117,9 +302,36 @@ hipError_t launch_codebook_encode(const uint32_t* plane, int64_t ldp, int64_t N,
 
 size_t codebook_gemv_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
+template <int NPH>
+hipError_t launch_codebook_lut(const uint16_t* idx, const uint32_t* codebook, int c, const void* s, int64_t N,
+                               int64_t K, const void* x, void* y, int units_per_phase, hipStream_t st) {
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)codebook_lut_kernel<NPH>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kCbLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned grid = (unsigned)((N + kCbRowsPerBlock - 1) / kCbRowsPerBlock);
+  codebook_lut_kernel<NPH><<<grid, kCbThreads, kCbLdsBytes, st>>>(
+      idx, codebook, c, static_cast<const __half*>(s), N, K, static_cast<const __half*>(x),
+      static_cast<__half*>(y), units_per_phase);
+  return hipGetLastError();
+}
+
 hipError_t launch_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, int c, int v,
                                 const void* s, int group, int64_t N, int64_t K, const void* x,
                                 int64_t M, void* y, void*, hipStream_t st) {
+  // the LUT path: one activation row, the pages' block and group sizes, rows of at most two
+  // phases, and 32-bit byte offsets into the index and scale arrays
+  const int64_t units = (K + kCbUnitCols - 1) / kCbUnitCols;
+  const int64_t phases = (units + kCbMaxUnits - 1) / kCbMaxUnits;
+  if (M == 1 && v == 20 && group == 16 && phases <= 2 && N * ((K + 19) / 20) * 2 < 0x7fffffffll &&
+      N * ((K + 15) / 16) * 2 < 0x7fffffffll) {
+    const int up = (int)((units + phases - 1) / phases);
+    if (phases == 1) return launch_codebook_lut<1>(idx, codebook, c, s, N, K, x, y, up, st);
+    return launch_codebook_lut<2>(idx, codebook, c, s, N, K, x, y, up, st);
+  }
   const dim3 grid((unsigned)((N + 3) / 4), (unsigned)M);
   codebook_gemv_kernel<<<grid, 256, 0, st>>>(idx, codebook, c, v, static_cast<const __half*>(s), group,
                                              N, K, static_cast<const __half*>(x), M,

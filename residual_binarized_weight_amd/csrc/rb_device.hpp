@@ -88,4 +88,43 @@ __device__ __forceinline__ double group_sum(double v, int width) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// buffer loads, absolute LDS reads and DPP reductions
+// ---------------------------------------------------------------------------
+// Raw buffer resource over [base, base + bytes): loads through it take a 32-bit byte offset
+// (per-lane VGPR + uniform SGPR/immediate part, no 64-bit address math) and return 0 past
+// the end instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+// LDS read at an absolute LDS byte address. A kernel that declares no static LDS has its
+// dynamic LDS at address 0, so a computed table offset is usable as the address itself.
+typedef __attribute__((address_space(3))) const float lds_cf32;
+__device__ __forceinline__ float lds_f32(uint32_t byte_addr) {
+  return *(lds_cf32*)(size_t)byte_addr;
+}
+
+// sum over each 32-lane half of the wave; the total lands in lanes 16..31 and 48..63
+__device__ __forceinline__ float half_wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  return v;
+}
+
+// sum over the whole wave; the total lands in lane 63
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = half_wave_sum(v);  // lanes 16..31 and 48..63 hold the two half sums
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0x8, 0xF, false));  // row_bcast:31
+  return v;
+}
+
 }  // namespace rb

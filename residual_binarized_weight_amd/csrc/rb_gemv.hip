@@ -154,18 +154,6 @@ constexpr int kLutThreads = 1024;
 constexpr int kLutWaves = 16;
 constexpr int kLutTableBytes = 128 * 1024;
 
-// Raw buffer resource over [base, base + bytes): loads through it take a 32-bit byte offset
-// (per-lane VGPR + uniform SGPR/immediate part, no 64-bit address math) and return 0 past
-// the end instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
-}
-__device__ __forceinline__ uint32_t buf_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
-}
 template <typename T> struct BufElem;
 template <> struct BufElem<__half> {
   using raw = uint32_t;
@@ -217,23 +205,6 @@ template <> struct RawScale<float> {
   __device__ static __forceinline__ float f32(float v) { return v; }
 };
 
-// LDS read at an absolute LDS byte address. The LUT kernel declares no static LDS, so its
-// dynamic LDS (the tables) starts at address 0 and a v_perm result is usable as is.
-typedef __attribute__((address_space(3))) const float lds_cf32;
-__device__ __forceinline__ float lds_f32(uint32_t byte_addr) {
-  return *(lds_cf32*)(size_t)byte_addr;
-}
-
-// sum over each 32-lane half of the wave; the total lands in lanes 16..31 and 48..63
-__device__ __forceinline__ float half_wave_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
-  return v;
-}
-
 // Split-K handoff through one 64-bit atomic per row. Each block adds its row partial p as
 // a fixed-point integer q = rint(p * 2^(30 - e)), where 2^e is the smallest power of two above
 // U = sum_i |g_i[row]| * sum_c |x_c|, a bound on |p| for every slice (so |q| < 2^31, and the
@@ -246,13 +217,6 @@ __device__ __forceinline__ float half_wave_sum(float v) {
 // bit-identically.
 constexpr uint64_t kAccCount = 1ull << 56;
 constexpr uint64_t kAccBias = 1ull << 48;
-
-// sum over the whole wave; the total lands in lane 63
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v = half_wave_sum(v);  // lanes 16..31 and 48..63 hold the two half sums
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0x8, 0xF, false));  // row_bcast:31
-  return v;
-}
 
 // One block per compute unit (its tables take 128 KB of LDS), i.e. 4 waves per SIMD: the
 // register budget is 128 per lane, and the scheduler need not trade loads in flight for

@@ -64,3 +64,38 @@ def test_codebook_gemv_shapes(K, v, group, M):
     y = rb.codebook_gemv(to_dev(idx), to_dev(C), v, to_dev(s), group, to_dev(x), K).float().cpu().numpy()
     y_ref, sabs = O.codebook_gemv(idx, C, v, s.astype(np.float64), group, x, K)
     assert_product_close(y, y_ref, sabs)
+
+
+@pytest.mark.parametrize("K", [16, 80, 81, 1000, 5519, 7760, 7761, 11008, 15520, 15521])
+@pytest.mark.parametrize("N", [1, 37])
+def test_codebook_lut_path_shapes(K, N):
+    # M = 1, v = 20, group = 16 takes the nibble-table kernel for K <= 15520 (one phase up to
+    # 7760 columns, two above); 15521 goes to the per-column kernel. Odd K exercises the
+    # activation tail inside a dword; N = 37 leaves rows past N in the last block.
+    v, group = 20, 16
+    rng = np.random.default_rng(K * 7 + N)
+    C = wl.codebook()
+    idx = rng.integers(0, C.size, size=(N, (K + v - 1) // v)).astype(np.uint16)
+    s = rng.uniform(0.001, 0.05, (N, (K + group - 1) // group)).astype(np.float16)
+    x = wl.activations(82, 1, K)
+    y = rb.codebook_gemv(to_dev(idx), to_dev(C), v, to_dev(s), group, to_dev(x), K).float().cpu().numpy()
+    y_ref, sabs = O.codebook_gemv(idx, C, v, s.astype(np.float64), group, x, K)
+    assert_product_close(y, y_ref, sabs)
+
+
+def test_codebook_pipeline_pack_encode_product():
+    # sign plane and group scales from rb_pack, indices from rb_codebook_encode, then the
+    # LUT product, all on the GPU; the oracle recomputes every stage from W
+    W = wl.weights_for("codebook", N=40)
+    N, K = W.shape
+    C = wl.codebook()
+    planes, s = rb.pack(torch.from_numpy(W).to(dev()), 1, group=16)
+    idx = rb.codebook_encode(planes[0], K, to_dev(C), 20)
+    x = wl.activations_for("codebook", 1)
+    y = rb.codebook_gemv(idx, to_dev(C), 20, s.reshape(N, -1), 16, to_dev(x), K).float().cpu().numpy()
+    res = O.binarize(W, 1, group=16)
+    assert not res["ambiguous"].any()
+    idx_ref = O.hamming_encode(O.sign_blocks(res["planes"][0], K, 20), C)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint16), idx_ref)
+    y_ref, sabs = O.codebook_gemv(idx_ref, C, 20, res["g"][0], 16, x, K)
+    assert_product_close(y, y_ref, sabs)

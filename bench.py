@@ -17,6 +17,12 @@ of this script (FETCH_SIZE, WRITE_SIZE) into the HBM-traffic record that the roo
 block reads; the streaming-read kernel (bytes known) and the weight-copy kernel (bytes known)
 of the same runs calibrate the counters.
 
+Besides the metric, `rows` reports every other step of the path on its own seeded workload
+with the roofline that bounds it: the deploy-time derivation (HBM), the batched product on
+the matrix cores for the 28672 x 8192 layer at M = 64 / 256 (MFMA fp16 peak) with the M = 1
+product on the same weights, the codebook encode (VALU) and the codebook LUT product (HBM).
+`--no-rows` skips them.
+
 Prints one JSON line (see the keys below). `python bench.py --gpus N` with N > 1 exits:
 this build runs on one GPU.
 """
@@ -38,9 +44,10 @@ METRIC = "k=2 4096×11008 M=1 binary GEMV µs; achieved HBM GB/s as % of MI355X 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 N_ROWS, K_COLS, K_PLANES = 4096, 11008, 2
 COPIES = 40
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_lut_down_4096x11008_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_nib_down_4096x11008_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "residual_binarized_weight_amd", "csrc", f)
-                  for f in ("rb_gemv.hip", "rb_device.hpp")]
+                  for f in ("rb_gemv_nib.hip", "rb_device.hpp")]
+PRODUCT_KERNEL = "gemv_nib_kernel"    # the dominant kernel of a step
 
 
 def algorithmic_bytes(N: int, K: int, k: int, M: int = 1) -> int:
@@ -107,6 +114,117 @@ def cpu_baseline(planes_np, g_np, x_np, budget_s: float = 12.0):
     }
 
 
+PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, vendor figure
+# VALU lane-operations per second: 256 CUs x 128 fp32 lanes x 2.4 GHz (157.3 TFLOP/s counts an
+# FMA as two flops); the codebook search spends 4 such operations per (pattern, codeword) pair
+PEAK_VALU_OPS = 157.3e12 / 2
+ENCODE_OPS_PER_PAIR = 4
+
+
+def graph_us(torch, calls, rounds: int = 5) -> float:
+    """Capture the calls once in a HIP graph on a side stream, replay it `rounds` times and
+    return the average duration of one call (events on the replay stream)."""
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        for c in calls[:2]:
+            c()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(gr, stream=st):
+            for c in calls:
+                c()
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (rounds * len(calls))
+
+
+def roof(bound: str, achieved: float, peak: float, unit: str, us: float, **extra) -> dict:
+    d = {"us": round(us, 3), "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4)}
+    d.update(extra)
+    return d
+
+
+def measure_rows(torch, np, rb, wl, dev, pack_ms: float) -> dict:
+    """Every step of the path besides the metric product, each on its own workload, timed
+    on the GPU against the roofline that bounds it (inputs are seeded synthetic data)."""
+    rows = {}
+    N, K, k = N_ROWS, K_COLS, K_PLANES
+    pack_bytes = N * K * 4 + k * N * K // 8 + 2 * k * N      # W fp32 read once, planes + g written
+    rows["a1_a2_pack_down_4096x11008_k2"] = roof("hbm", pack_bytes / (pack_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+                                                 pack_ms * 1e3, algorithmic_bytes=pack_bytes)
+
+    # a6: the 28672x8192 layer on the matrix cores at M = 64 and 256, k = 1 and 2, and the
+    # M = 1 product on the same weights; 8 weight copies rotate (470 MB > the 256 MB cache)
+    Wd = torch.from_numpy(wl.weights_for("wide")).to(dev)
+    NW, KW = Wd.shape
+    planes2, g2 = rb.pack(Wd, 2)
+    del Wd
+    torch.cuda.synchronize()
+    copies = [planes2.clone() for _ in range(8)]
+    for kk in (1, 2):
+        cps = [c[:kk] for c in copies]
+        gk = g2[:kk].contiguous()
+        for M in (64, 256):
+            x = torch.from_numpy(wl.activations_for("wide", M)).to(dev)
+            y = torch.empty((M, NW), dtype=torch.float16, device=dev)
+            us = graph_us(torch, [lambda c=c: rb.gemm_small(c, gk, None, x, KW, y=y) for c in cps], 3)
+            flops = 2.0 * M * NW * KW * kk
+            rows[f"a6_gemm_small_28672x8192_k{kk}_m{M}"] = roof("mfma", flops / (us * 1e-6) / 1e12, PEAK_FP16_MFMA_TFLOPS,
+                                                                "TFLOP/s", us, flops=flops)
+        x1 = torch.from_numpy(wl.activations_for("wide", 1)).to(dev)
+        ws = rb.workspace(rb.RB_OP_GEMV, kk, NW, KW, 1, device=dev)
+        y1 = torch.empty((1, NW), dtype=torch.float16, device=dev)
+        us = graph_us(torch, [lambda c=c: rb.gemv(c, gk, None, x1, KW, ws=ws, y=y1) for c in cps], 5)
+        byt = algorithmic_bytes(NW, KW, kk)
+        rows[f"gemv_m1_28672x8192_k{kk}"] = roof("hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us,
+                                                 algorithmic_bytes=byt)
+    del copies, planes2
+    torch.cuda.synchronize()
+
+    # a7, a8: the 4096x11008 sign matrix, v = 20, c = 65536, fp16 scales per 16 weights
+    Wc = torch.from_numpy(wl.weights_for("codebook")).to(dev)
+    Nc, Kc = Wc.shape
+    pl, sc = rb.pack(Wc, 1, group=16)
+    del Wc
+    C = torch.from_numpy(wl.codebook().view(np.int32)).to(dev)
+    idx = rb.codebook_encode(pl[0], Kc, C, 20)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        rb.codebook_encode(pl[0], Kc, C, 20)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 3
+    nb = (Kc + 19) // 20
+    pairs = Nc * nb * C.numel()
+    rows["a7_codebook_encode_4096x11008_v20_c65536"] = roof(
+        "alu", pairs * ENCODE_OPS_PER_PAIR / (us * 1e-6) / 1e12, PEAK_VALU_OPS / 1e12, "Tops/s", us,
+        pairs=pairs, ops_per_pair=ENCODE_OPS_PER_PAIR)
+    s2 = sc[0].reshape(Nc, -1).contiguous()
+    xc = torch.from_numpy(wl.activations_for("codebook", 1)).to(dev)
+    yc = torch.empty((1, Nc), dtype=torch.float16, device=dev)
+    icp = [idx.clone() for _ in range(40)]
+    scp = [s2.clone() for _ in range(40)]
+    us = graph_us(torch, [lambda i=i, q=q: rb.codebook_gemv(i, C, 20, q, 16, xc, Kc, y=yc) for i, q in zip(icp, scp)], 5)
+    byt = idx.numel() * 2 + s2.numel() * 2 + C.numel() * 4 + 2 * Kc + 2 * Nc
+    rows["a8_codebook_gemv_4096x11008_m1"] = roof("hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us,
+                                                  algorithmic_bytes=byt,
+                                                  note="bound in practice by 2.26 M random codeword reads from L2")
+    del icp, scp
+    torch.cuda.synchronize()
+    return rows
+
+
 def summarize_counters(root: str) -> int:
     """Read rocprofv3 --pmc CSVs (FETCH_SIZE and WRITE_SIZE runs of this script) under
     `root`, calibrate each counter against a kernel whose traffic is known, and write the
@@ -130,8 +248,8 @@ def summarize_counters(root: str) -> int:
     stream_bytes = nbytes // 256 * 256                     # the stream-read kernel's footprint
     Kw = (K_COLS + 31) // 32
     copy_bytes = K_PLANES * N_ROWS * ((Kw + 31) // 32 * 32) * 4   # one weight-copy dispatch
-    f_gemv, f_stream = med("FETCH_SIZE", "gemv_lut"), med("FETCH_SIZE", "stream_read")
-    w_gemv, w_copy = med("WRITE_SIZE", "gemv_lut"), med("WRITE_SIZE", "copyBuffer")
+    f_gemv, f_stream = med("FETCH_SIZE", PRODUCT_KERNEL), med("FETCH_SIZE", "stream_read")
+    w_gemv, w_copy = med("WRITE_SIZE", PRODUCT_KERNEL), med("WRITE_SIZE", "copyBuffer")
     rec = {"kernel_source_hash": kernel_source_hash(),
            "fetch_kib_per_dispatch": f_gemv, "write_kib_per_dispatch": w_gemv,
            "stream_read_fetch_kib": f_stream, "stream_read_bytes": stream_bytes,
@@ -154,6 +272,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements of the other steps")
     ap.add_argument("--summarize-counters", metavar="DIR", help="write the traffic record from rocprofv3 CSVs")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -291,6 +410,8 @@ def main() -> int:
             "traffic": measured_traffic(),
         },
     }
+    if not args.no_rows:
+        out["rows"] = measure_rows(torch, np, rb, wl, dev, pack_ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np.ascontiguousarray(planes.cpu().numpy().view(np.uint32)[:, :, :Kw]),
                                            g.float().cpu().numpy().astype(np.float64).reshape(k, N, 1),

@@ -431,17 +431,6 @@ struct LutPlan {
   int n_slices, pairs, n_blocks;
 };
 
-int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = cus;
-  }
-  return cached[dev];
-}
 
 // Row pairs per wave are a compile-time class (so every load is branch-free); the plan picks
 // the smallest class that spreads the (slice, row block) grid over the compute units.
@@ -547,6 +536,19 @@ hipError_t launch_s(rb_dtype scale_dtype, rb_dtype y_dtype, const uint32_t* plan
 
 }  // namespace
 
+// compute units of the current device (cached per device)
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 // The LUT path (M = 1) needs one 64-bit accumulator per row; the workspace is sized
 // for it whatever M is, so one workspace serves every batch size of a layer.
 size_t gemv_workspace_bytes(int, int64_t N, int64_t K, int64_t) { return lut_workspace_bytes(N, K); }
@@ -554,6 +556,12 @@ size_t gemv_workspace_bytes(int, int64_t N, int64_t K, int64_t) { return lut_wor
 hipError_t launch_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                        rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x,
                        rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws, hipStream_t s) {
+  // one activation row, h = 1: the whole-row nibble-table kernel where it applies (fp16
+  // data, k <= 2), else the byte-table kernel below
+  if (M == 1 && h == nullptr && gemv_nib_fits(k, N, K, ldp, x_dtype, scale_dtype, y_dtype)) {
+    const hipError_t e = launch_gemv_nib(planes, ldp, g, scale_dtype, k, N, K, x, x_dtype, y, y_dtype, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (x_dtype == RB_F16)
     return launch_s<__half>(scale_dtype, y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   return launch_s<float>(scale_dtype, y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, s);

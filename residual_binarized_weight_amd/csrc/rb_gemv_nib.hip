@@ -1,0 +1,301 @@
+// rb_gemv_nib.hip -- whole-row nibble-table product for one activation row (gfx950).
+//
+// [RaBiT summary page, background "Residual binarization"] y = sum_i g_i (.) (B_i x): the k
+// paths need only additions and one scale per row and plane. With h = 1 every plane is
+// multiplied by the same x, so one set of precomputed partial sums of x serves all of them
+// (the idea the BTC-LLM page's LUT-GEMM describes in 2.1.2).
+//
+// Tables: for each run of 4 columns ("nibble" q), T_q[e] = sum of the x_c whose bit is set
+// in the 4-bit pattern e (T_q[0] = 0). Per row and plane, Sum_c B x = 2 T - S with
+// T = sum over nibbles of T_q[bits] and S = sum of x (the masked-add identity), so
+//   y[n] = sum_i g_i[n] * (2 T_i[n] - S).
+// 16 entries per 4 columns is 4 table bytes per column, so the tables of a whole row fit in
+// LDS in at most two phases and a block can own complete rows: no cross-block reduction,
+// deterministic, no workspace.
+//
+// Layout: entry e of all tables of a phase is one 4 KB row of LDS (entry-major);
+// nibble i of word w sits in slot 8 w + (i ^ a(w)), a(w) = ((w >> 2) ^ ((w >> 5) & 1)) & 7.
+// Lane l of a wave reads word 64 j + l, so for a fixed i the lanes of each 32-lane half
+// land in 32 different banks of a 32-bank LDS (lanes that share w mod 4 differ in a), and
+// the 64 lanes in 64 different banks of a 64-bank one, whatever the bit values. A lookup
+// address is (e << 12) | (32 l + 4 (i ^ a_l)), plus the immediate 2048 j (a does not
+// depend on j).
+//
+// A block is 16 waves with RW rows each. Instantiated for fp16 activations, scales and
+// outputs and k <= 2 (the byte-table kernel in rb_gemv.hip covers the other cases).
+#include "rb_device.hpp"
+#include "rb_internal.h"
+
+namespace rb {
+namespace {
+
+constexpr int kNibThreads = 1024;
+constexpr int kNibRows = kNibThreads / 64;
+constexpr uint32_t kNibOob = 0x80000000u;  // an offset past every resource below
+
+typedef uint32_t nib_u32x2 __attribute__((ext_vector_type(2)));
+
+// 4 activations of nibble q (columns 4q .. 4q+3), in raw form; columns >= K become 0 later
+template <typename TX> struct NibX;
+template <> struct NibX<__half> {
+  using raw = nib_u32x2;
+  __device__ static __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+  }
+  static constexpr uint32_t bytes = 8;
+  __device__ static __forceinline__ float get(raw v, int j) {
+    return __half2float(__ushort_as_half((uint16_t)((v[j >> 1] >> (16 * (j & 1))) & 0xffffu)));
+  }
+};
+
+template <typename TS> struct NibScale;
+template <> struct NibScale<__half> {
+  __device__ static __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return buf_u16(r, voff, soff);
+  }
+  __device__ static __forceinline__ float f32(uint32_t v) { return __half2float(__ushort_as_half((uint16_t)v)); }
+};
+
+template <typename T> __device__ __forceinline__ void nib_store(T* p, float v);
+template <> __device__ __forceinline__ void nib_store<__half>(__half* p, float v) { *p = __float2half_rn(v); }
+
+// the entry field (e << SH) of nibble I of word w
+template <int I, int SH>
+__device__ __forceinline__ uint32_t nib_entry(uint32_t w) {
+  constexpr int at = 4 * I;
+  const uint32_t t = at <= SH ? (w << (SH - at)) : (w >> (at - SH));
+  return t & (15u << SH);
+}
+
+// Phases of 128 words (4096 columns): 16 entry rows of 4 KB = 64 KB of tables, two buffers
+// (buffer b at byte 65536 b). Phase p + 1 is built while phase p is looked up.
+constexpr int kNibPhaseWords = 128;
+constexpr int kNibTables = 8 * kNibPhaseWords;  // 1024 nibble tables per phase: one per thread
+constexpr int kNibSH = 12;                      // entry row = 4 KB
+constexpr uint32_t kNibBuf = 65536u;
+
+// RW rows per wave (row r of wave w of block b: (b * 16 + w) * RW + r)
+template <typename TX, typename TS, typename TY, int KP, int NPH, int RW>
+__global__ __launch_bounds__(kNibThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib_kernel(
+    const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, int64_t N, int64_t K,
+    const TX* __restrict__ x, TY* __restrict__ y) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  float* red = reinterpret_cast<float*>(lds + (NPH == 1 ? 1 : 2) * kNibBuf);  // after the table buffers
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = ((int64_t)blockIdx.x * kNibRows + wave) * RW;
+  const uint32_t Kw = (uint32_t)((K + 31) >> 5);
+  const uint32_t Kc = (uint32_t)K;
+  const uint32_t ldp_b = (uint32_t)ldp * 4u;
+
+  // plane words and scales through 32-bit offsets (the host checks k N ldp * 4 < 2^31), x
+  // through whole dwords (a column past K inside the last one is masked); past the end: 0
+  const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(planes, (uint32_t)((uint64_t)KP * N * ldp * 4));
+  const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g, (uint32_t)((uint64_t)KP * N * sizeof(TS)));
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)((uint64_t)((K * sizeof(TX) + 3) & ~3ull)));
+
+  // 1. the activations of this thread's table (nibble tid) of every phase
+  typename NibX<TX>::raw xr[NPH];
+#pragma unroll
+  for (int p = 0; p < NPH; ++p)
+    xr[p] = NibX<TX>::load(rx, (uint32_t)(p * kNibTables + tid) * NibX<TX>::bytes);
+  // activations first, in every wave: requests return in order, and the table build must not
+  // queue behind the weight stream
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. this wave's rows' plane words (lane l: words 128 p + l and 128 p + 64 + l) and scales
+  uint32_t wd[RW][NPH][2][KP];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const uint32_t row_off = (uint32_t)(n0 + r) * ldp_b;
+#pragma unroll
+    for (int p = 0; p < NPH; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w = (uint32_t)(kNibPhaseWords * p + 64 * j + lane);
+        const uint32_t voff = w < Kw ? row_off + 4u * w : kNibOob;
+#pragma unroll
+        for (int i = 0; i < KP; ++i) wd[r][p][j][i] = buf_u32(rp, voff, (uint32_t)i * (uint32_t)N * ldp_b);
+      }
+  }
+  uint32_t gr[RW][KP];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int i = 0; i < KP; ++i)
+      gr[r][i] = NibScale<TS>::load(rg, (uint32_t)(n0 + r) * (uint32_t)sizeof(TS),
+                                    (uint32_t)i * (uint32_t)N * (uint32_t)sizeof(TS));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // per-lane slot bases 32 l + 4 (i ^ a(l)) in each buffer
+  uint32_t cb[2][8];
+  const int al = ((lane >> 2) ^ ((lane >> 5) & 1)) & 7;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    cb[0][i] = 32u * (uint32_t)lane + 4u * (uint32_t)(i ^ al);
+    cb[1][i] = cb[0][i] | kNibBuf;
+  }
+
+  float xs = 0.0f;  // this thread's share of sum x
+  // table of nibble `tid` of phase p into buffer p % 2
+  auto build = [&](int p) {
+    const uint32_t Q = (uint32_t)(p * kNibTables + tid);
+    float xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v = NibX<TX>::get(xr[p], j);
+      xv[j] = 4u * Q + (uint32_t)j < Kc ? v : 0.0f;
+    }
+    xs += (xv[0] + xv[1]) + (xv[2] + xv[3]);
+    const uint32_t w = (uint32_t)tid >> 3, i = (uint32_t)tid & 7;
+    const uint32_t slot = 8u * w + (i ^ (((w >> 2) ^ ((w >> 5) & 1u)) & 7u));
+    const uint32_t base = (uint32_t)(p & 1) * kNibBuf + slot * 4u;
+    const float lo[4] = {0.0f, xv[0], xv[1], xv[0] + xv[1]};
+    const float hi[4] = {0.0f, xv[2], xv[3], xv[2] + xv[3]};
+    typedef __attribute__((address_space(3))) float lds_f32p;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float v = (e & 3) == 0 ? hi[e >> 2] : ((e >> 2) == 0 ? lo[e & 3] : lo[e & 3] + hi[e >> 2]);
+      *(lds_f32p*)(size_t)(((uint32_t)e << kNibSH) + base) = v;
+    }
+    if (p == NPH - 1) {
+      // every column has been seen: publish this wave's share of sum x (a barrier follows)
+      const float xw = wave_sum_dpp(xs);
+      if (lane == 63) red[wave] = xw;
+    }
+  };
+
+  float acc[RW][KP];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int i = 0; i < KP; ++i) acc[r][i] = 0.0f;
+
+  build(0);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < NPH; ++p) {
+    // 3. the next phase's tables (activations only: no wait on the weight stream)
+    if (p + 1 < NPH) build(p + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // 4. lookups in this phase's buffer: one LDS read per 4 weight bits
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+          const uint32_t w = wd[r][p][j][i];
+          const uint32_t o = 2048u * (uint32_t)j;
+          const uint32_t* c = cb[p & 1];
+          float t = (lds_f32((nib_entry<0, kNibSH>(w) | c[0]) + o) + lds_f32((nib_entry<1, kNibSH>(w) | c[1]) + o)) +
+                    (lds_f32((nib_entry<2, kNibSH>(w) | c[2]) + o) + lds_f32((nib_entry<3, kNibSH>(w) | c[3]) + o));
+          t += (lds_f32((nib_entry<4, kNibSH>(w) | c[4]) + o) + lds_f32((nib_entry<5, kNibSH>(w) | c[5]) + o)) +
+               (lds_f32((nib_entry<6, kNibSH>(w) | c[6]) + o) + lds_f32((nib_entry<7, kNibSH>(w) | c[7]) + o));
+          acc[r][i] += t;
+        }
+      }
+    // the next phase's tables are complete, and this phase's buffer is free for phase p + 2
+    if (p + 1 < NPH) {
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // 5. row sums; sum x over the block, read in the same order by every wave
+  float S = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kNibRows; ++w) S += red[w];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) v += NibScale<TS>::f32(gr[r][i]) * (2.0f * wave_sum_dpp(acc[r][i]) - S);
+    if (lane == 63 && n0 + r < N) nib_store<TY>(&y[n0 + r], v);
+  }
+}
+
+template <typename TX, typename TS, typename TY, int KP, int NPH, int RW>
+hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
+                            const void* x, void* y, hipStream_t s) {
+  // one phase needs one table buffer (two blocks fit on a compute unit), more need two
+  constexpr size_t lds = (NPH == 1 ? 1 : 2) * (size_t)kNibBuf + 64;
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib_kernel<TX, TS, TY, KP, NPH, RW>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned grid = (unsigned)((N + kNibRows * RW - 1) / (kNibRows * RW));
+  gemv_nib_kernel<TX, TS, TY, KP, NPH, RW><<<grid, kNibThreads, lds, s>>>(
+      planes, ldp, static_cast<const TS*>(g), N, K, static_cast<const TX*>(x), static_cast<TY*>(y));
+  return hipGetLastError();
+}
+
+// rows per wave: the smallest count that puts at most one block on each compute unit, up
+// to the most whose plane words still fit in registers next to the lookups' temporaries
+// (larger counts spill)
+constexpr int nib_max_rows(int kp, int nph) { return kp == 1 ? (nph <= 3 ? 3 : 2) : (nph == 1 ? 3 : nph <= 3 ? 2 : 1); }
+
+template <typename TX, typename TS, typename TY, int KP, int NPH>
+hipError_t launch_nib_rows(int rw, const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
+                           const void* x, void* y, hipStream_t s) {
+  constexpr int kMax = nib_max_rows(KP, NPH);
+  if (rw > kMax) rw = kMax;
+  if constexpr (kMax >= 3) {
+    if (rw == 3) return launch_nib_shape<TX, TS, TY, KP, NPH, 3>(planes, ldp, g, N, K, x, y, s);
+  }
+  if constexpr (kMax >= 2) {
+    if (rw == 2) return launch_nib_shape<TX, TS, TY, KP, NPH, 2>(planes, ldp, g, N, K, x, y, s);
+  }
+  return launch_nib_shape<TX, TS, TY, KP, NPH, 1>(planes, ldp, g, N, K, x, y, s);
+}
+
+template <typename TX, typename TS, typename TY, int KP>
+hipError_t launch_nib_kp(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
+                         const void* x, void* y, hipStream_t s) {
+  const int64_t phases = ((K + 31) / 32 + kNibPhaseWords - 1) / kNibPhaseWords;
+  const int64_t cus = device_cu_count();
+  int rw = 3;
+  for (int c = 1; c <= 3; ++c)
+    if ((N + kNibRows * c - 1) / (kNibRows * c) <= cus) {
+      rw = c;
+      break;
+    }
+  switch (phases) {
+    case 1: return launch_nib_rows<TX, TS, TY, KP, 1>(rw, planes, ldp, g, N, K, x, y, s);
+    case 2: return launch_nib_rows<TX, TS, TY, KP, 2>(rw, planes, ldp, g, N, K, x, y, s);
+    case 3: return launch_nib_rows<TX, TS, TY, KP, 3>(rw, planes, ldp, g, N, K, x, y, s);
+    default: return launch_nib_rows<TX, TS, TY, KP, 4>(rw, planes, ldp, g, N, K, x, y, s);
+  }
+}
+
+}  // namespace
+
+bool gemv_nib_fits(int k, int64_t N, int64_t K, int64_t ldp, rb_dtype x_dtype, rb_dtype scale_dtype,
+                   rb_dtype y_dtype) {
+  const uint64_t lim = 0x7fffffffull;
+  return x_dtype == RB_F16 && scale_dtype == RB_F16 && y_dtype == RB_F16 && (k == 1 || k == 2) &&
+         (K + 31) / 32 <= 4 * kNibPhaseWords && (uint64_t)k * N * ldp * 4 < lim && (uint64_t)k * N * 4 < lim &&
+         (uint64_t)K * 4 + 16 < lim && (uint64_t)(N + kNibRows * 3) * ldp * 4 < lim;
+}
+
+hipError_t launch_gemv_nib(const uint32_t* planes, int64_t ldp, const void* g, rb_dtype scale_dtype, int k,
+                           int64_t N, int64_t K, const void* x, rb_dtype x_dtype, void* y, rb_dtype y_dtype,
+                           hipStream_t s) {
+  if (x_dtype != RB_F16 || scale_dtype != RB_F16 || y_dtype != RB_F16) return hipErrorNotSupported;
+  switch (k) {
+    case 1: return launch_nib_kp<__half, __half, __half, 1>(planes, ldp, g, N, K, x, y, s);
+    case 2: return launch_nib_kp<__half, __half, __half, 2>(planes, ldp, g, N, K, x, y, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace rb

@@ -9,6 +9,8 @@
 
 namespace rb {
 
+int device_cu_count();  // compute units of the current device (cached)
+
 hipError_t launch_pack(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, int k,
                        int group, const void* h, rb_dtype scale_dtype, uint32_t* planes, int64_t ldp,
                        void* g, int32_t* d_status, hipStream_t s);
@@ -19,6 +21,13 @@ hipError_t launch_gemv(const uint32_t* planes, int64_t ldp, const void* g, const
                        rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x,
                        rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,
                        hipStream_t s);
+
+// whole-row nibble-table GEMV (M = 1, h = 1); hipErrorNotSupported for types it does not cover
+bool gemv_nib_fits(int k, int64_t N, int64_t K, int64_t ldp, rb_dtype x_dtype, rb_dtype scale_dtype,
+                   rb_dtype y_dtype);
+hipError_t launch_gemv_nib(const uint32_t* planes, int64_t ldp, const void* g, rb_dtype scale_dtype, int k,
+                           int64_t N, int64_t K, const void* x, rb_dtype x_dtype, void* y, rb_dtype y_dtype,
+                           hipStream_t s);
 
 // small GEMM on the matrix cores
 size_t gemm_small_workspace_bytes(int k, int64_t N, int64_t K, int64_t M);

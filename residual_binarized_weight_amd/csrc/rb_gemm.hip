@@ -34,8 +34,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2g __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4g __attribute__((ext_vector_type(4)));
 
-constexpr int kGemmWaves = 4;
-constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kGemmWaves = 4;                   // waves per K group
+constexpr int kGemmGroupThreads = 64 * kGemmWaves;
+constexpr int kGemmGroups = 2;                  // K halves per block, one group of waves each
+constexpr int kGemmThreads = kGemmGroupThreads * kGemmGroups;
 constexpr int kGemmTileN = 32 * kGemmWaves;     // weight rows per block
 constexpr int kStageCols = 128;                 // columns per stage: 4 words per plane row
 constexpr int kStageWords = kStageCols / 32;
@@ -85,14 +87,14 @@ struct XStage {
 // rows past M and columns past K read as 0 (the resource ends at the block's last row;
 // a column past K gets an out-of-range offset)
 template <int MT>
-__device__ __forceinline__ void load_x_stage(XStage<MT>& r, __amdgpu_buffer_rsrc_t rx, int64_t K, int64_t k0,
-                                             int tid) {
+__device__ __forceinline__ void load_x_stage(XStage<MT>& r, __amdgpu_buffer_rsrc_t rx, int64_t K, int64_t kend,
+                                             int64_t k0, int tid) {
 #pragma unroll
   for (int u = 0; u < MT; ++u) {
-    const int q = tid + u * kGemmThreads;  // 0 .. 256 MT - 1
-    const int row = q >> 3, wt = q & 7;    // wt = 2 w + t
+    const int q = tid + u * kGemmGroupThreads;  // 0 .. 256 MT - 1
+    const int row = q >> 3, wt = q & 7;         // wt = 2 w + t
     const int64_t c = k0 + 32 * (wt >> 1) + 8 * (wt & 1);
-    const uint32_t off = c < K ? (uint32_t)((row * K + c) * 2) : kOob;
+    const uint32_t off = c < kend ? (uint32_t)((row * K + c) * 2) : kOob;
     r.lo[u] = buf_load16(rx, off);
     r.hi[u] = buf_load16(rx, off + 32u);
   }
@@ -102,7 +104,7 @@ template <int MT>
 __device__ __forceinline__ void store_x_stage(const XStage<MT>& r, uint8_t* buf, int tid) {
 #pragma unroll
   for (int u = 0; u < MT; ++u) {
-    const int q = tid + u * kGemmThreads;
+    const int q = tid + u * kGemmGroupThreads;
     const int row = q >> 3, wt = q & 7;
     u32x4g g0, g1;
     interleave(r.lo[u], r.hi[u], g0, g1);
@@ -119,10 +121,10 @@ struct HStage {
   u32x4g lo, hi;
 };
 
-__device__ __forceinline__ void load_h_stage(HStage& r, __amdgpu_buffer_rsrc_t rh, int64_t K, int64_t k0, int tid) {
+__device__ __forceinline__ void load_h_stage(HStage& r, __amdgpu_buffer_rsrc_t rh, int64_t kend, int64_t k0, int tid) {
   const int u = tid & 7;
   const int64_t c = k0 + 32 * (u >> 1) + 8 * (u & 1);
-  const uint32_t off = c < K ? (uint32_t)(c * 2) : kOob;
+  const uint32_t off = c < kend ? (uint32_t)(c * 2) : kOob;
   r.lo = buf_load16(rh, off);
   r.hi = buf_load16(rh, off + 32u);
 }
@@ -155,30 +157,43 @@ __device__ __forceinline__ h8 expand_b(uint32_t nw, int t, int hh, u32x4g base) 
 // stage past the end (or past K in a 64-column tail) are whatever the row holds there,
 // and they meet activations that read as 0, so they add +-0 (a non-finite g, which no
 // finite W packs to, would turn that row's +-0 into NaN).
-template <typename TS, typename TY, int MT, int MODE, int KP>
+// MSPLIT: the two wave groups take two halves of the batch (else two halves of K)
+template <typename TS, typename TY, int MT, int MODE, int KP, bool MSPLIT>
 __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, const __half* __restrict__ h,
     int k, int64_t N, int64_t K, const __half* __restrict__ x, int64_t M, TY* __restrict__ y) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* const xbuf0 = smem;
-  uint8_t* const xbuf1 = smem + MT * 32 * kRowBytes;
-  uint8_t* const hbuf0 = smem + 2 * MT * 32 * kRowBytes;
+  const int tid_all = threadIdx.x;
+  const int lane = tid_all & 63;
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid_all >> 6);  // uniform: keeps resources scalar
+  const int grp = wave_all / kGemmWaves;    // K group of this wave
+  const int wave = wave_all % kGemmWaves;   // wave within its group
+  const int tid = tid_all % kGemmGroupThreads;
+  uint8_t* const gbase = smem + grp * (2 * MT * 32 * kRowBytes + 512);
+  uint8_t* const xbuf0 = gbase;
+  uint8_t* const xbuf1 = gbase + MT * 32 * kRowBytes;
+  uint8_t* const hbuf0 = gbase + 2 * MT * 32 * kRowBytes;
   uint8_t* const hbuf1 = hbuf0 + 256;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps resources scalar
   const int nl = lane & 31;
   const int hh = lane >> 5;
   const int64_t n0 = (int64_t)blockIdx.x * kGemmTileN + wave * 32;  // wave's first row
   const int64_t n = n0 + nl;
   const int64_t nc = n < N ? n : N - 1;  // rows past N repeat the last row and are not stored
   const int64_t rb = n0 < N ? n0 : N - 1;
-  const int64_t m_base = (int64_t)blockIdx.y * MT * 32;
-  const int64_t m_rows = M - m_base < MT * 32 ? M - m_base : MT * 32;
-  const int nch = (int)((K + kStageCols - 1) / kStageCols);
-  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(x + m_base * K, m_rows * K * 2);
-  const uint32_t lane_off = (uint32_t)((nc - rb) * ldp * 4);
+  // batch split: group g takes batch rows [m_base, m_base + 32 MT) of the block's 64 MT;
+  // K split: group 0 takes columns [0, kh), group 1 [kh, K), kh a whole number of stages,
+  // and both groups run group 0's stage count (group 1's extra stages read activations as 0)
+  const int64_t m_base = MSPLIT ? ((int64_t)blockIdx.y * kGemmGroups + grp) * MT * 32 : (int64_t)blockIdx.y * MT * 32;
+  const int64_t m_left = M - m_base;
+  const int64_t m_rows = m_left < 0 ? 0 : (m_left < MT * 32 ? m_left : MT * 32);
+  const int64_t kh_raw = (((K + 1) / 2 + kStageCols - 1) / kStageCols) * kStageCols;
+  const int64_t kh = MSPLIT ? K : (kh_raw < K ? kh_raw : K);
+  const int64_t kbeg = MSPLIT || grp == 0 ? 0 : kh;
+  const int64_t kend = MSPLIT || grp == 0 ? kh : K;
+  const int nch = (int)((kh + kStageCols - 1) / kStageCols);
+  const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(x + (m_rows > 0 ? m_base : 0) * K, m_rows * K * 2);
+  const uint32_t lane_off = (uint32_t)((nc - rb) * ldp * 4 + kbeg / 8);  // 4 bytes per 32 columns
 
   f32x16 yacc[MT];
 #pragma unroll
@@ -221,8 +236,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
     {
       XStage<MT> xs0;
       HStage hs0;
-      load_x_stage<MT>(xs0, rx, K, 0, tid);
-      if (MODE == kModeH) load_h_stage(hs0, rh, K, 0, tid);
+      load_x_stage<MT>(xs0, rx, K, kend, kbeg, tid);
+      if (MODE == kModeH) load_h_stage(hs0, rh, kend, kbeg, tid);
       __syncthreads();  // the previous pass may still read buffer 0
       store_x_stage<MT>(xs0, xbuf0, tid);
       if (MODE == kModeH) store_h_stage(hs0, hbuf0, tid);
@@ -238,8 +253,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
         for (int p = 0; p < KP; ++p) cur[p] = wr[d][p];
         XStage<MT> xn;
         HStage hn;
-        load_x_stage<MT>(xn, rx, K, (int64_t)(c + 1) * kStageCols, tid);
-        if (MODE == kModeH) load_h_stage(hn, rh, K, (int64_t)(c + 1) * kStageCols, tid);
+        load_x_stage<MT>(xn, rx, K, kend, kbeg + (int64_t)(c + 1) * kStageCols, tid);
+        if (MODE == kModeH) load_h_stage(hn, rh, kend, kbeg + (int64_t)(c + 1) * kStageCols, tid);
 #pragma unroll
         for (int p = 0; p < KP; ++p) wr[d][p] = buf_load16(rw[p], lane_off + 16u * (uint32_t)(c + kDepth));
         // keep the loads at the top of the stage: they must be in flight during its MFMAs
@@ -285,6 +300,24 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
     }
   }
 
+  // group 1 hands its sums to group 0 through LDS (the stage loop ended on a barrier, so the
+  // activation buffers are free); group 0 adds them in a fixed order and stores
+  float* const ex = reinterpret_cast<float*>(smem);
+  if (!MSPLIT && grp == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ex[((wave * MT + mt) * 16 + j) * 64 + lane] = yacc[mt][j];
+  }
+  if (!MSPLIT) {
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) yacc[mt][j] += ex[((wave * MT + mt) * 16 + j) * 64 + lane];
+  }
+
   // D of the 32x32 MFMA: lane l holds column n = l % 32 of the tile, element j holds
   // batch row 8 (j / 4) + 4 (l / 32) + j % 4
   if (n < N) {
@@ -301,34 +334,42 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
 
 template <int MT>
 constexpr size_t gemm_lds_bytes() {
-  return (size_t)2 * MT * 32 * kRowBytes + 512;
+  return (size_t)kGemmGroups * (2 * MT * 32 * kRowBytes + 512);
 }
 
-template <typename TS, typename TY, int MT, int MODE, int KP>
+template <typename TS, typename TY, int MT, int MODE, int KP, bool MSPLIT>
 hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
                       int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
   constexpr size_t lds = gemm_lds_bytes<MT>();
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemm_small_kernel<TS, TY, MT, MODE, KP>,
+    const hipError_t e = hipFuncSetAttribute((const void*)gemm_small_kernel<TS, TY, MT, MODE, KP, MSPLIT>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  const int64_t m_per_block = (int64_t)32 * MT * (MSPLIT ? kGemmGroups : 1);
   const unsigned gx = (unsigned)((N + kGemmTileN - 1) / kGemmTileN);
-  const unsigned gy = (unsigned)((M + 32 * MT - 1) / (32 * MT));
-  gemm_small_kernel<TS, TY, MT, MODE, KP><<<dim3(gx, gy), kGemmThreads, lds, s>>>(
+  const unsigned gy = (unsigned)((M + m_per_block - 1) / m_per_block);
+  gemm_small_kernel<TS, TY, MT, MODE, KP, MSPLIT><<<dim3(gx, gy), kGemmThreads, lds, s>>>(
       planes, ldp, static_cast<const TS*>(g), static_cast<const __half*>(h), k, N, K,
       static_cast<const __half*>(x), M, static_cast<TY*>(y));
   return hipGetLastError();
 }
 
+// Batch tiles per wave and the role of the two wave groups: up to 64 batch rows the groups
+// split K (more waves per SIMD on a grid of N / 128 blocks); beyond, they split the batch
+// (64 or 128 rows per group), which keeps the grid at one block per 128 weight rows and
+// 256 batch rows.
 template <typename TS, typename TY, int MODE, int KP>
 hipError_t launch_mt(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
                      int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
-  if (M <= 32) return launch_one<TS, TY, 1, MODE, KP>(planes, ldp, g, h, k, N, K, x, M, y, s);
-  if (M <= 64) return launch_one<TS, TY, 2, MODE, KP>(planes, ldp, g, h, k, N, K, x, M, y, s);
-  return launch_one<TS, TY, 4, MODE, KP>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if (M <= 32) return launch_one<TS, TY, 1, MODE, KP, false>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if (M <= 64) return launch_one<TS, TY, 2, MODE, KP, false>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  // h mode stages h as well and keeps at most two batch tiles (four would spill registers)
+  if (M <= 128 || MODE == kModeH) return launch_one<TS, TY, 2, MODE, KP, true>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if constexpr (MODE != kModeH) return launch_one<TS, TY, 4, MODE, KP, true>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  return hipErrorNotSupported;
 }
 
 template <typename TY>

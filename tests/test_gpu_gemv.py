@@ -123,3 +123,24 @@ def test_gemv_writes_nothing_past_y_and_is_deterministic():
     assert torch.equal(y1, y)
     y_ref, sabs = O.gemv(planes, g, None, x, 1000)
     assert_product_close(y.float().cpu().numpy(), y_ref, sabs)
+
+
+@pytest.mark.parametrize("N,K,k", [(600, 1000, 2), (4113, 4096, 2), (9000, 4096, 1), (5000, 11001, 2)])
+def test_gemv_m1_writes_nothing_past_y_and_is_deterministic(N, K, k):
+    # the M = 1 table kernels with 1, 2 and 3 rows per wave and 1 or 3 table phases; N not a
+    # multiple of the block's rows; repeated calls bit-identical; nothing written past y
+    W = wl.heavy_tailed_weights(77 + k, N, K)
+    x = wl.activations(78, 1, K)
+    pd, gd = rb.pack(torch.from_numpy(W).to(dev()), k)
+    xd = to_dev(x)
+    ws = rb.workspace(rb.RB_OP_GEMV, k, N, K, 1)
+    buf = torch.full((N + 64,), 12345.0, dtype=torch.float16, device=dev())
+    y = buf[:N].view(1, N)
+    rb.gemv(pd, gd, None, xd, K, ws=ws, y=y)
+    y1 = y.clone()
+    rb.gemv(pd, gd, None, xd, K, ws=ws, y=y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[N:] == 12345.0)
+    assert torch.equal(y1, y)
+    y_ref, sabs = O.gemv(planes_np(pd, K), scales_np(gd, k, N), None, x, K)
+    assert_product_close(y.float().cpu().numpy(), y_ref, sabs)

@@ -29,8 +29,7 @@
 namespace rb {
 namespace {
 
-constexpr int kNibThreads = 1024;
-constexpr int kNibRows = kNibThreads / 64;
+constexpr int kNibWaves = 16;  // waves per block, RW rows each (8 measured slower: fewer waves keep LDS less busy)
 constexpr uint32_t kNibOob = 0x80000000u;  // an offset past every resource below
 
 typedef uint32_t nib_u32x2 __attribute__((ext_vector_type(2)));
@@ -74,9 +73,10 @@ constexpr int kNibTables = 8 * kNibPhaseWords;  // 1024 nibble tables per phase:
 constexpr int kNibSH = 12;                      // entry row = 4 KB
 constexpr uint32_t kNibBuf = 65536u;
 
-// RW rows per wave (row r of wave w of block b: (b * 16 + w) * RW + r)
-template <typename TX, typename TS, typename TY, int KP, int NPH, int RW>
-__global__ __launch_bounds__(kNibThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib_kernel(
+// WV waves per block, RW rows per wave (row r of wave w of block b: (b * WV + w) * RW + r);
+// each thread builds 1024 / (64 WV) tables per phase
+template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, int64_t N, int64_t K,
     const TX* __restrict__ x, TY* __restrict__ y) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -84,7 +84,9 @@ __global__ __launch_bounds__(kNibThreads) __attribute__((amdgpu_waves_per_eu(1, 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t n0 = ((int64_t)blockIdx.x * kNibRows + wave) * RW;
+  constexpr int kThreads = 64 * WV;
+  constexpr int kTB = kNibTables / kThreads;  // tables per thread and phase
+  const int64_t n0 = ((int64_t)blockIdx.x * WV + wave) * RW;
   const uint32_t Kw = (uint32_t)((K + 31) >> 5);
   const uint32_t Kc = (uint32_t)K;
   const uint32_t ldp_b = (uint32_t)ldp * 4u;
@@ -96,10 +98,12 @@ __global__ __launch_bounds__(kNibThreads) __attribute__((amdgpu_waves_per_eu(1, 
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)((uint64_t)((K * sizeof(TX) + 3) & ~3ull)));
 
   // 1. the activations of this thread's table (nibble tid) of every phase
-  typename NibX<TX>::raw xr[NPH];
+  typename NibX<TX>::raw xr[NPH][kTB];
 #pragma unroll
   for (int p = 0; p < NPH; ++p)
-    xr[p] = NibX<TX>::load(rx, (uint32_t)(p * kNibTables + tid) * NibX<TX>::bytes);
+#pragma unroll
+    for (int b = 0; b < kTB; ++b)
+      xr[p][b] = NibX<TX>::load(rx, (uint32_t)(p * kNibTables + b * kThreads + tid) * NibX<TX>::bytes);
   // activations first, in every wave: requests return in order, and the table build must not
   // queue behind the weight stream
   __builtin_amdgcn_sched_barrier(0);
@@ -142,24 +146,33 @@ __global__ __launch_bounds__(kNibThreads) __attribute__((amdgpu_waves_per_eu(1, 
   float xs = 0.0f;  // this thread's share of sum x
   // table of nibble `tid` of phase p into buffer p % 2
   auto build = [&](int p) {
-    const uint32_t Q = (uint32_t)(p * kNibTables + tid);
-    float xv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float v = NibX<TX>::get(xr[p], j);
-      xv[j] = 4u * Q + (uint32_t)j < Kc ? v : 0.0f;
-    }
-    xs += (xv[0] + xv[1]) + (xv[2] + xv[3]);
-    const uint32_t w = (uint32_t)tid >> 3, i = (uint32_t)tid & 7;
-    const uint32_t slot = 8u * w + (i ^ (((w >> 2) ^ ((w >> 5) & 1u)) & 7u));
-    const uint32_t base = (uint32_t)(p & 1) * kNibBuf + slot * 4u;
-    const float lo[4] = {0.0f, xv[0], xv[1], xv[0] + xv[1]};
-    const float hi[4] = {0.0f, xv[2], xv[3], xv[2] + xv[3]};
     typedef __attribute__((address_space(3))) float lds_f32p;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float v = (e & 3) == 0 ? hi[e >> 2] : ((e >> 2) == 0 ? lo[e & 3] : lo[e & 3] + hi[e >> 2]);
-      *(lds_f32p*)(size_t)(((uint32_t)e << kNibSH) + base) = v;
+    for (int b = 0; b < kTB; ++b) {
+      const uint32_t q = (uint32_t)(b * kThreads + tid);  // table within the phase
+      const uint32_t Q = (uint32_t)(p * kNibTables) + q;
+      float xv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = NibX<TX>::get(xr[p][b], j);
+        xv[j] = 4u * Q + (uint32_t)j < Kc ? v : 0.0f;
+      }
+      xs += (xv[0] + xv[1]) + (xv[2] + xv[3]);
+      const uint32_t w = q >> 3, i = q & 7;
+      const uint32_t slot = 8u * w + (i ^ (((w >> 2) ^ ((w >> 5) & 1u)) & 7u));
+      const uint32_t base = (uint32_t)(p & 1) * kNibBuf + slot * 4u;
+      const float lo[4] = {0.0f, xv[0], xv[1], xv[0] + xv[1]};
+      const float hi[4] = {0.0f, xv[2], xv[3], xv[2] + xv[3]};
+      // entry 0 is 0 for every table: written by each buffer's first build only. Tables wholly
+      // past K are read only at entry 0 (their words are 0), so they need no other entry.
+      if (p < 2) *(lds_f32p*)(size_t)base = 0.0f;
+      if (4u * Q < Kc) {
+#pragma unroll
+        for (int e = 1; e < 16; ++e) {
+          const float v = (e & 3) == 0 ? hi[e >> 2] : ((e >> 2) == 0 ? lo[e & 3] : lo[e & 3] + hi[e >> 2]);
+          *(lds_f32p*)(size_t)(((uint32_t)e << kNibSH) + base) = v;
+        }
+      }
     }
     if (p == NPH - 1) {
       // every column has been seen: publish this wave's share of sum x (a barrier follows)
@@ -183,11 +196,13 @@ __global__ __launch_bounds__(kNibThreads) __attribute__((amdgpu_waves_per_eu(1, 
     // 3. the next phase's tables (activations only: no wait on the weight stream)
     if (p + 1 < NPH) build(p + 1);
     __builtin_amdgcn_sched_barrier(0);
-    // 4. lookups in this phase's buffer: one LDS read per 4 weight bits
+    // 4. lookups in this phase's buffer: one LDS read per 4 weight bits. Lanes past the row's
+    // last word add nothing and stay idle (only the last phase has such lanes)
 #pragma unroll
     for (int r = 0; r < RW; ++r)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        if (p == NPH - 1 && (uint32_t)(kNibPhaseWords * p + 64 * j + lane) >= Kw) continue;
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
           const uint32_t w = wd[r][p][j][i];
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(kNibThreads) __attribute__((amdgpu_waves_per_eu(1, 
   // 5. row sums; sum x over the block, read in the same order by every wave
   float S = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kNibRows; ++w) S += red[w];
+  for (int w = 0; w < WV; ++w) S += red[w];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     float v = 0.0f;
@@ -221,27 +236,27 @@ __global__ __launch_bounds__(kNibThreads) __attribute__((amdgpu_waves_per_eu(1, 
   }
 }
 
-template <typename TX, typename TS, typename TY, int KP, int NPH, int RW>
+template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV = kNibWaves>
 hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
                             const void* x, void* y, hipStream_t s) {
   // one phase needs one table buffer (two blocks fit on a compute unit), more need two
   constexpr size_t lds = (NPH == 1 ? 1 : 2) * (size_t)kNibBuf + 64;
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib_kernel<TX, TS, TY, KP, NPH, RW>,
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib_kernel<TX, TS, TY, KP, NPH, RW, WV>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const unsigned grid = (unsigned)((N + kNibRows * RW - 1) / (kNibRows * RW));
-  gemv_nib_kernel<TX, TS, TY, KP, NPH, RW><<<grid, kNibThreads, lds, s>>>(
+  const unsigned grid = (unsigned)((N + WV * RW - 1) / (WV * RW));
+  gemv_nib_kernel<TX, TS, TY, KP, NPH, RW, WV><<<grid, 64 * WV, lds, s>>>(
       planes, ldp, static_cast<const TS*>(g), N, K, static_cast<const TX*>(x), static_cast<TY*>(y));
   return hipGetLastError();
 }
 
 // rows per wave: the smallest count that puts at most one block on each compute unit, up
-// to the most whose plane words still fit in registers next to the lookups' temporaries
-// (larger counts spill)
+// to the most whose plane words still fit in registers next to the lookups' temporaries at
+// 16 waves per block (larger counts spill)
 constexpr int nib_max_rows(int kp, int nph) { return kp == 1 ? (nph <= 3 ? 3 : 2) : (nph == 1 ? 3 : nph <= 3 ? 2 : 1); }
 
 template <typename TX, typename TS, typename TY, int KP, int NPH>
@@ -265,7 +280,7 @@ hipError_t launch_nib_kp(const uint32_t* planes, int64_t ldp, const void* g, int
   const int64_t cus = device_cu_count();
   int rw = 3;
   for (int c = 1; c <= 3; ++c)
-    if ((N + kNibRows * c - 1) / (kNibRows * c) <= cus) {
+    if ((N + kNibWaves * c - 1) / (kNibWaves * c) <= cus) {
       rw = c;
       break;
     }
@@ -284,7 +299,7 @@ bool gemv_nib_fits(int k, int64_t N, int64_t K, int64_t ldp, rb_dtype x_dtype, r
   const uint64_t lim = 0x7fffffffull;
   return x_dtype == RB_F16 && scale_dtype == RB_F16 && y_dtype == RB_F16 && (k == 1 || k == 2) &&
          (K + 31) / 32 <= 4 * kNibPhaseWords && (uint64_t)k * N * ldp * 4 < lim && (uint64_t)k * N * 4 < lim &&
-         (uint64_t)K * 4 + 16 < lim && (uint64_t)(N + kNibRows * 3) * ldp * 4 < lim;
+         (uint64_t)K * 4 + 16 < lim && (uint64_t)(N + kNibWaves * 3) * ldp * 4 < lim;
 }
 
 hipError_t launch_gemv_nib(const uint32_t* planes, int64_t ldp, const void* g, rb_dtype scale_dtype, int k,

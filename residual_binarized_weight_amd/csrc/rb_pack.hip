@@ -7,8 +7,8 @@
 //
 // One wave64 per weight row. Lane l reads column c0 + l of each 64-column step, so
 // every load of W is a fully coalesced 64-element run. __ballot of (R >= 0) turns one
-// step into two uint32 words; after 32 steps each lane holds one word of a 2048-column
-// chunk and the wave writes the 64 words with one coalesced store.
+// step into two uint32 words; after 16 steps lanes 0..31 hold the words of a 1024-column
+// chunk and the wave writes them with one coalesced store.
 //
 // Row-scale mode (group == 0): the scale of plane i needs the whole row of R_i, so the
 // row is traversed once per plane. The residual is never stored: each pass recomputes
@@ -26,6 +26,7 @@ namespace rb {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // 4 waves of 64
+constexpr int kPackSteps = 16;    // 64-column steps per chunk of the row kernel
 
 template <typename TW, typename TS>
 __global__ __launch_bounds__(256) void pack_rows_kernel(const TW* __restrict__ W, int64_t N,
@@ -45,13 +46,21 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const TW* __restrict__ W
   for (int i = 0; i < k; ++i) {
     double num = 0.0, den = 0.0;
     uint32_t* __restrict__ prow = planes + ((int64_t)i * N + n) * ldp;
-    for (int64_t c0 = 0; c0 < K; c0 += 64 * 32) {
+    // 1024-column chunks: the 16 loads of a chunk are issued before any is used (enough
+    // requests in flight to stream W); lanes 0..31 collect the chunk's 32 words
+    for (int64_t c0 = 0; c0 < K; c0 += 64 * kPackSteps) {
+      float wv[kPackSteps];
+#pragma unroll
+      for (int j = 0; j < kPackSteps; ++j) {
+        const int64_t col = c0 + 64 * j + lane;
+        wv[j] = col < K ? to_f32(Wr[col]) : 0.0f;
+      }
       uint32_t word = 0u;
-#pragma unroll 4
-      for (int j = 0; j < 32; ++j) {
+#pragma unroll
+      for (int j = 0; j < kPackSteps; ++j) {
         const int64_t col = c0 + 64 * j + lane;
         const bool valid = col < K;
-        const float w = valid ? to_f32(Wr[col]) : 0.0f;
+        const float w = wv[j];
         if (i == 0) bad |= valid && !isfinite(w);
         // R_i at this column, re-derived through the earlier planes
         double R = (double)w;
@@ -72,7 +81,7 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const TW* __restrict__ W
         if (lane == ((2 * j + 1) & 63)) word = (uint32_t)(m >> 32);
       }
       const int64_t w0 = c0 >> 5;
-      if (w0 + lane < Kw) prow[w0 + lane] = word;
+      if (lane < 2 * kPackSteps && w0 + lane < Kw) prow[w0 + lane] = word;
     }
     num = wave_sum(num);
     den = h ? wave_sum(den) : (double)K;

@@ -225,10 +225,10 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float) -> dict:
     return rows
 
 
-def summarize_counters(root: str) -> int:
+def summarize_counters(root: str, out_path: str = COUNTERS_FILE) -> int:
     """Read rocprofv3 --pmc CSVs (FETCH_SIZE and WRITE_SIZE runs of this script) under
     `root`, calibrate each counter against a kernel whose traffic is known, and write the
-    per-launch HBM traffic of the product kernel to the counters record."""
+    per-launch HBM traffic of the product kernel to the counters record `out_path`."""
     import csv
     import glob
     per = {}  # (counter, kernel) -> list of per-dispatch totals
@@ -259,8 +259,8 @@ def summarize_counters(root: str) -> int:
         write_scale = copy_bytes / (w_copy * 1024.0)
         rec.update({"fetch_scale": fetch_scale, "write_scale": write_scale,
                     "hbm_bytes_per_launch": round(f_gemv * 1024.0 * fetch_scale + w_gemv * 1024.0 * write_scale)})
-    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
-    with open(COUNTERS_FILE, "w") as f:
+    os.makedirs(os.path.dirname(os.path.abspath(out_path)), exist_ok=True)
+    with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
     return 0

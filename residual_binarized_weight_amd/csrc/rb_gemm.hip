@@ -108,9 +108,12 @@ __device__ __forceinline__ void store_x_stage(const XStage<MT>& r, uint8_t* buf,
     const int row = q >> 3, wt = q & 7;
     u32x4g g0, g1;
     interleave(r.lo[u], r.hi[u], g0, g1);
-    // group index 4 w + 2 t + hh = 2 wt + hh
-    *reinterpret_cast<u32x4g*>(buf + row * kRowBytes + (2 * wt) * 16) = g0;
-    *reinterpret_cast<u32x4g*>(buf + row * kRowBytes + (2 * wt + 1) * 16) = g1;
+    // group index 4 w + 2 t + hh = 2 wt + hh. Lanes with wt >= 4 write their odd group
+    // first: then the 8 lanes of a row cover 8 different 16-byte bank groups in each of
+    // the two stores (in order, groups 2wt, 2wt+1 would put wt and wt+4 on the same banks)
+    const bool swap = wt >= 4;
+    *reinterpret_cast<u32x4g*>(buf + row * kRowBytes + (2 * wt + (swap ? 1 : 0)) * 16) = swap ? g1 : g0;
+    *reinterpret_cast<u32x4g*>(buf + row * kRowBytes + (2 * wt + (swap ? 0 : 1)) * 16) = swap ? g0 : g1;
   }
 }
 
@@ -262,6 +265,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
 
         const uint8_t* xb = (d & 1) ? xbuf1 : xbuf0;  // kDepth is even: stage parity = d parity
         const uint8_t* hb = (d & 1) ? hbuf1 : hbuf0;
+        // A fragments of step s = 2 w + t are read one step ahead of their MFMAs
+        h8 anext[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          anext[mt] = *reinterpret_cast<const h8*>(xb + (mt * 32 + nl) * kRowBytes + hh * 16);
 #pragma unroll
         for (int w = 0; w < kStageWords; ++w) {
 #pragma unroll
@@ -269,8 +277,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
             const int r = 4 * w + 2 * t + hh;
             h8 a[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              a[mt] = *reinterpret_cast<const h8*>(xb + (mt * 32 + nl) * kRowBytes + r * 16);
+            for (int mt = 0; mt < MT; ++mt) a[mt] = anext[mt];
+            if (2 * w + t + 1 < 2 * kStageWords) {
+              const int rn = 2 * (2 * w + t + 1) + hh;
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                anext[mt] = *reinterpret_cast<const h8*>(xb + (mt * 32 + nl) * kRowBytes + rn * 16);
+            }
             u32x4g hbase = base[0];
             if (MODE == kModeH) hbase = *reinterpret_cast<const u32x4g*>(hb + r * 16);
 #pragma unroll

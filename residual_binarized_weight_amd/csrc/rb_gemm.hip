@@ -36,8 +36,6 @@ typedef uint32_t u32x4g __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmWaves = 4;                   // waves per K group
 constexpr int kGemmGroupThreads = 64 * kGemmWaves;
-constexpr int kGemmGroups = 2;                  // K halves per block, one group of waves each
-constexpr int kGemmThreads = kGemmGroupThreads * kGemmGroups;
 constexpr int kGemmTileN = 32 * kGemmWaves;     // weight rows per block
 constexpr int kStageCols = 128;                 // columns per stage: 4 words per plane row
 constexpr int kStageWords = kStageCols / 32;
@@ -160,16 +158,17 @@ __device__ __forceinline__ h8 expand_b(uint32_t nw, int t, int hh, u32x4g base) 
 // stage past the end (or past K in a 64-column tail) are whatever the row holds there,
 // and they meet activations that read as 0, so they add +-0 (a non-finite g, which no
 // finite W packs to, would turn that row's +-0 into NaN).
-// MSPLIT: the two wave groups take two halves of the batch (else two halves of K)
-template <typename TS, typename TY, int MT, int MODE, int KP, bool MSPLIT>
-__global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
+// NG wave groups per block (1 or 2). With two, MSPLIT: they take two halves of the batch,
+// else two halves of K.
+template <typename TS, typename TY, int MT, int MODE, int KP, int NG, bool MSPLIT>
+__global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, const __half* __restrict__ h,
     int k, int64_t N, int64_t K, const __half* __restrict__ x, int64_t M, TY* __restrict__ y) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid_all = threadIdx.x;
   const int lane = tid_all & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(tid_all >> 6);  // uniform: keeps resources scalar
-  const int grp = wave_all / kGemmWaves;    // K group of this wave
+  const int grp = NG == 1 ? 0 : wave_all / kGemmWaves;  // group of this wave
   const int wave = wave_all % kGemmWaves;   // wave within its group
   const int tid = tid_all % kGemmGroupThreads;
   uint8_t* const gbase = smem + grp * (2 * MT * 32 * kRowBytes + 512);
@@ -187,11 +186,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
   // batch split: group g takes batch rows [m_base, m_base + 32 MT) of the block's 64 MT;
   // K split: group 0 takes columns [0, kh), group 1 [kh, K), kh a whole number of stages,
   // and both groups run group 0's stage count (group 1's extra stages read activations as 0)
-  const int64_t m_base = MSPLIT ? ((int64_t)blockIdx.y * kGemmGroups + grp) * MT * 32 : (int64_t)blockIdx.y * MT * 32;
+  const int64_t m_base = MSPLIT ? ((int64_t)blockIdx.y * NG + grp) * MT * 32 : (int64_t)blockIdx.y * MT * 32;
   const int64_t m_left = M - m_base;
   const int64_t m_rows = m_left < 0 ? 0 : (m_left < MT * 32 ? m_left : MT * 32);
   const int64_t kh_raw = (((K + 1) / 2 + kStageCols - 1) / kStageCols) * kStageCols;
-  const int64_t kh = MSPLIT ? K : (kh_raw < K ? kh_raw : K);
+  const int64_t kh = (MSPLIT || NG == 1) ? K : (kh_raw < K ? kh_raw : K);
   const int64_t kbeg = MSPLIT || grp == 0 ? 0 : kh;
   const int64_t kend = MSPLIT || grp == 0 ? kh : K;
   const int nch = (int)((kh + kStageCols - 1) / kStageCols);
@@ -316,13 +315,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
   // group 1 hands its sums to group 0 through LDS (the stage loop ended on a barrier, so the
   // activation buffers are free); group 0 adds them in a fixed order and stores
   float* const ex = reinterpret_cast<float*>(smem);
-  if (!MSPLIT && grp == 1) {
+  if (NG == 2 && !MSPLIT && grp == 1) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) ex[((wave * MT + mt) * 16 + j) * 64 + lane] = yacc[mt][j];
   }
-  if (!MSPLIT) {
+  if (NG == 2 && !MSPLIT) {
     __syncthreads();
     if (grp == 1) return;
 #pragma unroll
@@ -345,43 +344,44 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
   }
 }
 
-template <int MT>
+template <int MT, int NG>
 constexpr size_t gemm_lds_bytes() {
-  return (size_t)kGemmGroups * (2 * MT * 32 * kRowBytes + 512);
+  return (size_t)NG * (2 * MT * 32 * kRowBytes + 512);
 }
 
-template <typename TS, typename TY, int MT, int MODE, int KP, bool MSPLIT>
+template <typename TS, typename TY, int MT, int MODE, int KP, int NG, bool MSPLIT>
 hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
                       int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
-  constexpr size_t lds = gemm_lds_bytes<MT>();
+  constexpr size_t lds = gemm_lds_bytes<MT, NG>();
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemm_small_kernel<TS, TY, MT, MODE, KP, MSPLIT>,
+    const hipError_t e = hipFuncSetAttribute((const void*)gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t m_per_block = (int64_t)32 * MT * (MSPLIT ? kGemmGroups : 1);
+  const int64_t m_per_block = (int64_t)32 * MT * (MSPLIT ? NG : 1);
   const unsigned gx = (unsigned)((N + kGemmTileN - 1) / kGemmTileN);
   const unsigned gy = (unsigned)((M + m_per_block - 1) / m_per_block);
-  gemm_small_kernel<TS, TY, MT, MODE, KP, MSPLIT><<<dim3(gx, gy), kGemmThreads, lds, s>>>(
+  gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT><<<dim3(gx, gy), kGemmGroupThreads * NG, lds, s>>>(
       planes, ldp, static_cast<const TS*>(g), static_cast<const __half*>(h), k, N, K,
       static_cast<const __half*>(x), M, static_cast<TY*>(y));
   return hipGetLastError();
 }
 
-// Batch tiles per wave and the role of the two wave groups: up to 64 batch rows the groups
-// split K (more waves per SIMD on a grid of N / 128 blocks); beyond, they split the batch
-// (64 or 128 rows per group), which keeps the grid at one block per 128 weight rows and
-// 256 batch rows.
+// Batch tiles per wave and the wave groups: up to 64 batch rows the two groups split K (two
+// waves per SIMD on a grid of N / 128 blocks); beyond, they split the block's batch rows
+// (64 or 128 each), which keeps the grid at one block per 128 weight rows and 256 batch
+// rows. (One group with 8 tiles per wave, so each expanded operand feeds 8 MFMAs, measured
+// slower at M = 256: one wave per SIMD hides less than the halved expansion work saves.)
 template <typename TS, typename TY, int MODE, int KP>
 hipError_t launch_mt(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
                      int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
-  if (M <= 32) return launch_one<TS, TY, 1, MODE, KP, false>(planes, ldp, g, h, k, N, K, x, M, y, s);
-  if (M <= 64) return launch_one<TS, TY, 2, MODE, KP, false>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if (M <= 32) return launch_one<TS, TY, 1, MODE, KP, 2, false>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if (M <= 64) return launch_one<TS, TY, 2, MODE, KP, 2, false>(planes, ldp, g, h, k, N, K, x, M, y, s);
   // h mode stages h as well and keeps at most two batch tiles (four would spill registers)
-  if (M <= 128 || MODE == kModeH) return launch_one<TS, TY, 2, MODE, KP, true>(planes, ldp, g, h, k, N, K, x, M, y, s);
-  if constexpr (MODE != kModeH) return launch_one<TS, TY, 4, MODE, KP, true>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if (M <= 128 || MODE == kModeH) return launch_one<TS, TY, 2, MODE, KP, 2, true>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if constexpr (MODE != kModeH) return launch_one<TS, TY, 4, MODE, KP, 2, true>(planes, ldp, g, h, k, N, K, x, M, y, s);
   return hipErrorNotSupported;
 }
 

@@ -153,14 +153,46 @@ def roof(bound: str, achieved: float, peak: float, unit: str, us: float, **extra
     return d
 
 
-def measure_rows(torch, np, rb, wl, dev, pack_ms: float) -> dict:
+def time_oracle(fn, budget_s: float = 2.0, max_runs: int = 5) -> tuple[float, int]:
+    """Median wall time of repeated calls of an oracle function (at least one run)."""
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(times) >= max_runs:
+            break
+    return statistics.median(times), len(times)
+
+
+def oracle_rate(fn, amount: float, scale: float, unit: str, sample: str) -> dict:
+    """The CPU oracle on a bounded sample of a row's workload: `amount` units of the row's
+    metric per call (bytes, flops or operations), reported in the row's unit (`scale` units
+    each)."""
+    t, n = time_oracle(fn)
+    return {"value": round(amount / t / scale, 5), "unit": unit, "kind": "oracle",
+            "sample": f"{sample}; median of {n} runs, {t * 1e3:.0f} ms each"}
+
+
+def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = True) -> dict:
     """Every step of the path besides the metric product, each on its own workload, timed
-    on the GPU against the roofline that bounds it (inputs are seeded synthetic data)."""
+    on the GPU against the roofline that bounds it (inputs are seeded synthetic data). With
+    `with_oracle`, each row also carries the CPU oracle's rate on a bounded sample of the same
+    workload (`cpu_oracle`)."""
     rows = {}
     N, K, k = N_ROWS, K_COLS, K_PLANES
     pack_bytes = N * K * 4 + k * N * K // 8 + 2 * k * N      # W fp32 read once, planes + g written
     rows["a1_a2_pack_down_4096x11008_k2"] = roof("hbm", pack_bytes / (pack_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
                                                  pack_ms * 1e3, algorithmic_bytes=pack_bytes)
+    if with_oracle:
+        from oracle import rb_oracle as O
+        R = 512
+        Ws = wl.weights_for("down")[:R]
+        rows["a1_a2_pack_down_4096x11008_k2"]["cpu_oracle"] = oracle_rate(
+            lambda: O.binarize(Ws, k), R * pack_bytes / N, 1e9, "GB/s",
+            f"first {R} of the 4096 rows (k=2, fp16 g), bytes scaled per row")
+        del Ws
 
     # a6: the 28672x8192 layer on the matrix cores at M = 64 and 256, k = 1 and 2, and the
     # M = 1 product on the same weights; 8 weight copies rotate (470 MB > the 256 MB cache)
@@ -170,23 +202,37 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float) -> dict:
     del Wd
     torch.cuda.synchronize()
     copies = [planes2.clone() for _ in range(8)]
+    RS = 1024                                                 # oracle sample: rows of the layer
+    if with_oracle:
+        pl_s = np.ascontiguousarray(planes2[:, :RS].cpu().numpy().view(np.uint32)[:, :, :KW // 32])
+        g_s = g2[:, :RS].float().cpu().numpy().astype(np.float64).reshape(2, RS, 1)
     for kk in (1, 2):
         cps = [c[:kk] for c in copies]
         gk = g2[:kk].contiguous()
         for M in (64, 256):
-            x = torch.from_numpy(wl.activations_for("wide", M)).to(dev)
+            xh = wl.activations_for("wide", M)
+            x = torch.from_numpy(xh).to(dev)
             y = torch.empty((M, NW), dtype=torch.float16, device=dev)
             us = graph_us(torch, [lambda c=c: rb.gemm_small(c, gk, None, x, KW, y=y) for c in cps], 3)
             flops = 2.0 * M * NW * KW * kk
-            rows[f"a6_gemm_small_28672x8192_k{kk}_m{M}"] = roof("mfma", flops / (us * 1e-6) / 1e12, PEAK_FP16_MFMA_TFLOPS,
-                                                                "TFLOP/s", us, flops=flops)
-        x1 = torch.from_numpy(wl.activations_for("wide", 1)).to(dev)
+            row = rows[f"a6_gemm_small_28672x8192_k{kk}_m{M}"] = roof(
+                "mfma", flops / (us * 1e-6) / 1e12, PEAK_FP16_MFMA_TFLOPS, "TFLOP/s", us, flops=flops)
+            if with_oracle:
+                row["cpu_oracle"] = oracle_rate(
+                    lambda: O.gemv(pl_s[:kk], g_s[:kk], None, xh, KW), 2.0 * M * RS * KW * kk, 1e12, "TFLOP/s",
+                    f"first {RS} of the 28672 rows, same M and k, flops scaled per row")
+        x1h = wl.activations_for("wide", 1)
+        x1 = torch.from_numpy(x1h).to(dev)
         ws = rb.workspace(rb.RB_OP_GEMV, kk, NW, KW, 1, device=dev)
         y1 = torch.empty((1, NW), dtype=torch.float16, device=dev)
         us = graph_us(torch, [lambda c=c: rb.gemv(c, gk, None, x1, KW, ws=ws, y=y1) for c in cps], 5)
         byt = algorithmic_bytes(NW, KW, kk)
-        rows[f"gemv_m1_28672x8192_k{kk}"] = roof("hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us,
-                                                 algorithmic_bytes=byt)
+        row = rows[f"gemv_m1_28672x8192_k{kk}"] = roof("hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us,
+                                                       algorithmic_bytes=byt)
+        if with_oracle:
+            row["cpu_oracle"] = oracle_rate(
+                lambda: O.gemv(pl_s[:kk], g_s[:kk], None, x1h, KW), algorithmic_bytes(RS, KW, kk), 1e9, "GB/s",
+                f"first {RS} of the 28672 rows, M=1, bytes scaled per row")
     del copies, planes2
     torch.cuda.synchronize()
 
@@ -210,6 +256,13 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float) -> dict:
     rows["a7_codebook_encode_4096x11008_v20_c65536"] = roof(
         "alu", pairs * ENCODE_OPS_PER_PAIR / (us * 1e-6) / 1e12, PEAK_VALU_OPS / 1e12, "Tops/s", us,
         pairs=pairs, ops_per_pair=ENCODE_OPS_PER_PAIR)
+    if with_oracle:
+        RC = 16                                               # oracle sample: rows of the sign matrix
+        pat = O.sign_blocks(pl[0, :RC].cpu().numpy().view(np.uint32)[:, :(Kc + 31) // 32], Kc, 20)
+        Ch = C.cpu().numpy().view(np.uint32)
+        rows["a7_codebook_encode_4096x11008_v20_c65536"]["cpu_oracle"] = oracle_rate(
+            lambda: O.hamming_encode(pat, Ch), RC * nb * C.numel() * ENCODE_OPS_PER_PAIR, 1e12, "Tops/s",
+            f"first {RC} of the 4096 rows ({RC * nb} patterns x 65536 codewords), operations scaled per pair")
     s2 = sc[0].reshape(Nc, -1).contiguous()
     xc = torch.from_numpy(wl.activations_for("codebook", 1)).to(dev)
     yc = torch.empty((1, Nc), dtype=torch.float16, device=dev)
@@ -220,6 +273,15 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float) -> dict:
     rows["a8_codebook_gemv_4096x11008_m1"] = roof("hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us,
                                                   algorithmic_bytes=byt,
                                                   note="bound in practice by 2.26 M random codeword reads from L2")
+    if with_oracle:
+        RG = 1024
+        idx_s = idx[:RG].cpu().numpy().view(np.uint16)
+        s_s = s2[:RG].float().cpu().numpy()
+        xch = xc.cpu().numpy()
+        per_row = idx.shape[1] * 2 + s2.shape[1] * 2 + 2
+        rows["a8_codebook_gemv_4096x11008_m1"]["cpu_oracle"] = oracle_rate(
+            lambda: O.codebook_gemv(idx_s, Ch, 20, s_s, 16, xch, Kc), RG * per_row + C.numel() * 4 + 2 * Kc,
+            1e9, "GB/s", f"first {RG} of the 4096 rows, M=1, index and scale bytes scaled per row")
     del icp, scp
     torch.cuda.synchronize()
     return rows
@@ -411,7 +473,7 @@ def main() -> int:
         },
     }
     if not args.no_rows:
-        out["rows"] = measure_rows(torch, np, rb, wl, dev, pack_ms)
+        out["rows"] = measure_rows(torch, np, rb, wl, dev, pack_ms, with_oracle=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np.ascontiguousarray(planes.cpu().numpy().view(np.uint32)[:, :, :Kw]),
                                            g.float().cpu().numpy().astype(np.float64).reshape(k, N, 1),

@@ -196,13 +196,15 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
     // 3. the next phase's tables (activations only: no wait on the weight stream)
     if (p + 1 < NPH) build(p + 1);
     __builtin_amdgcn_sched_barrier(0);
-    // 4. lookups in this phase's buffer: one LDS read per 4 weight bits. Lanes past the row's
-    // last word add nothing and stay idle (only the last phase has such lanes)
+    // 4. lookups in this phase's buffer: one LDS read per 4 weight bits. A lane past the row's
+    // last word holds 0 (its load was out of range) and reads entry 0, which is 0 in every
+    // table; only a group of 64 words wholly past it is skipped (a wave-uniform test: a
+    // per-lane one would put the reads under exec masks and wait for them inside)
 #pragma unroll
     for (int r = 0; r < RW; ++r)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        if (p == NPH - 1 && (uint32_t)(kNibPhaseWords * p + 64 * j + lane) >= Kw) continue;
+        if (p == NPH - 1 && (uint32_t)(kNibPhaseWords * p + 64 * j) >= Kw) continue;
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
           const uint32_t w = wd[r][p][j][i];

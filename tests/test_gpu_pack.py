@@ -66,6 +66,18 @@ def test_pack_single_row_and_special_values():
         assert_pack_matches(W[5:6], k, None, "f16", 0, p1, g1)
 
 
+@pytest.mark.parametrize("K", [16384, 16385, 20001])
+def test_pack_register_row_limit(K):
+    # rows up to 16384 columns are held in registers by one block; longer rows take the
+    # per-plane traversal: both sides of the limit, with and without h
+    W = wl.heavy_tailed_weights(70, 5, K)
+    _, p, g = run_pack(W, 2)
+    assert_pack_matches(W, 2, None, "f16", 0, p, g)
+    h = wl.random_scales(14, 2, K, negative_frac=0.2, dtype=np.float16)
+    _, p, g = run_pack(W, 2, h=h)
+    assert_pack_matches(W, 2, h, "f16", 0, p, g)
+
+
 @pytest.mark.parametrize("fmt", ["f16", "f32"])
 def test_pack_general_h_with_negatives(fmt):
     K = 777

@@ -19,7 +19,7 @@
 // land in 32 different banks of a 32-bank LDS (lanes that share w mod 4 differ in a), and
 // the 64 lanes in 64 different banks of a 64-bank one, whatever the bit values. A lookup
 // address is (e << 12) | (32 l + 4 (i ^ a_l)), plus the immediate 2048 j (a does not
-// depend on j).
+// depend on j); it is assembled by one byte permute per nibble (see the lookups).
 //
 // A block is 16 waves with RW rows each. Instantiated for fp16 activations, scales and
 // outputs and k <= 2 (the byte-table kernel in rb_gemv.hip covers the other cases).
@@ -30,6 +30,7 @@ namespace rb {
 namespace {
 
 constexpr int kNibWaves = 16;  // waves per block, RW rows each (8 measured slower: fewer waves keep LDS less busy)
+constexpr int kNibB0Waves = 8;  // waves that build the first phase's tables
 constexpr uint32_t kNibOob = 0x80000000u;  // an offset past every resource below
 
 typedef uint32_t nib_u32x2 __attribute__((ext_vector_type(2)));
@@ -58,14 +59,6 @@ template <> struct NibScale<__half> {
 template <typename T> __device__ __forceinline__ void nib_store(T* p, float v);
 template <> __device__ __forceinline__ void nib_store<__half>(__half* p, float v) { *p = __float2half_rn(v); }
 
-// the entry field (e << SH) of nibble I of word w
-template <int I, int SH>
-__device__ __forceinline__ uint32_t nib_entry(uint32_t w) {
-  constexpr int at = 4 * I;
-  const uint32_t t = at <= SH ? (w << (SH - at)) : (w >> (at - SH));
-  return t & (15u << SH);
-}
-
 // Phases of 128 words (4096 columns): 16 entry rows of 4 KB = 64 KB of tables, two buffers
 // (buffer b at byte 65536 b). Phase p + 1 is built while phase p is looked up.
 constexpr int kNibPhaseWords = 128;
@@ -73,8 +66,7 @@ constexpr int kNibTables = 8 * kNibPhaseWords;  // 1024 nibble tables per phase:
 constexpr int kNibSH = 12;                      // entry row = 4 KB
 constexpr uint32_t kNibBuf = 65536u;
 
-// WV waves per block, RW rows per wave (row r of wave w of block b: (b * WV + w) * RW + r);
-// each thread builds 1024 / (64 WV) tables per phase
+// WV waves per block, RW rows per wave (row r of wave w of block b: (b * WV + w) * RW + r)
 template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, int64_t N, int64_t K,
@@ -85,7 +77,11 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int kThreads = 64 * WV;
-  constexpr int kTB = kNibTables / kThreads;  // tables per thread and phase
+  static_assert(kThreads == kNibTables, "one table per thread from phase 1 on");
+  // phase 0 is built by the first kNibB0Waves waves alone, kTB0 tables per thread
+  constexpr int kB0Threads = 64 * kNibB0Waves;
+  constexpr int kTB0 = kNibTables / kB0Threads;
+  const bool b0 = wave < kNibB0Waves;  // wave-uniform
   const int64_t n0 = ((int64_t)blockIdx.x * WV + wave) * RW;
   const uint32_t Kw = (uint32_t)((K + 31) >> 5);
   const uint32_t Kc = (uint32_t)K;
@@ -97,13 +93,17 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g, (uint32_t)((uint64_t)KP * N * sizeof(TS)));
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)((uint64_t)((K * sizeof(TX) + 3) & ~3ull)));
 
-  // 1. the activations of this thread's table (nibble tid) of every phase
-  typename NibX<TX>::raw xr[NPH][kTB];
+  // 1. the activations of this thread's tables: phase 0's nibbles b * kB0Threads + tid in the
+  // first waves (issued before anything else), then nibble tid of every later phase
+  typename NibX<TX>::raw x0[kTB0];
+  typename NibX<TX>::raw xr[NPH];
+  if (b0) {
 #pragma unroll
-  for (int p = 0; p < NPH; ++p)
+    for (int b = 0; b < kTB0; ++b)
+      x0[b] = NibX<TX>::load(rx, (uint32_t)(b * kB0Threads + tid) * NibX<TX>::bytes);
+  }
 #pragma unroll
-    for (int b = 0; b < kTB; ++b)
-      xr[p][b] = NibX<TX>::load(rx, (uint32_t)(p * kNibTables + b * kThreads + tid) * NibX<TX>::bytes);
+  for (int p = 1; p < NPH; ++p) xr[p] = NibX<TX>::load(rx, (uint32_t)(p * kNibTables + tid) * NibX<TX>::bytes);
   // activations first, in every wave: requests return in order, and the table build must not
   // queue behind the weight stream
   __builtin_amdgcn_sched_barrier(0);
@@ -134,45 +134,60 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
                                     (uint32_t)i * (uint32_t)N * (uint32_t)sizeof(TS));
   __builtin_amdgcn_sched_barrier(0);
 
-  // per-lane slot bases 32 l + 4 (i ^ a(l)) in each buffer
+  // Lookup addresses by byte splicing. Lane l's slot offset 32 l + 4 (i ^ a(l)) is
+  // 256 (l >> 3) + [32 (l & 7) + 4 (i ^ a(l))]: its low byte depends on i, its bits 8-10 are
+  // l >> 3. The address (e << 12) | offset | 65536 buffer therefore has byte 0 = the low byte,
+  // byte 1 = (e << 4) | (l >> 3), byte 2 = the buffer. Per word, nibble e of each byte's high
+  // half OR (l >> 3) gives every nibble's byte 1 (two words: odd nibbles w & 0xf0f0f0f0, even
+  // ones (w << 4) & 0xf0f0f0f0), and one v_perm per nibble joins it with cb[buffer][i] (bytes
+  // 0 and 2): 11 operations per word instead of 15.
   uint32_t cb[2][8];
   const int al = ((lane >> 2) ^ ((lane >> 5) & 1)) & 7;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    cb[0][i] = 32u * (uint32_t)lane + 4u * (uint32_t)(i ^ al);
+    cb[0][i] = 32u * (uint32_t)(lane & 7) + 4u * (uint32_t)(i ^ al);
     cb[1][i] = cb[0][i] | kNibBuf;
   }
+  const uint32_t lh4 = (uint32_t)(lane >> 3) * 0x01010101u;
 
   float xs = 0.0f;  // this thread's share of sum x
-  // table of nibble `tid` of phase p into buffer p % 2
-  auto build = [&](int p) {
+  // table q of phase p into buffer p % 2, from the 4 activations in `raw`
+  auto build_one = [&](int p, uint32_t q, typename NibX<TX>::raw raw) {
     typedef __attribute__((address_space(3))) float lds_f32p;
+    const uint32_t Q = (uint32_t)(p * kNibTables) + q;
+    float xv[4];
 #pragma unroll
-    for (int b = 0; b < kTB; ++b) {
-      const uint32_t q = (uint32_t)(b * kThreads + tid);  // table within the phase
-      const uint32_t Q = (uint32_t)(p * kNibTables) + q;
-      float xv[4];
+    for (int j = 0; j < 4; ++j) {
+      const float v = NibX<TX>::get(raw, j);
+      xv[j] = 4u * Q + (uint32_t)j < Kc ? v : 0.0f;
+    }
+    xs += (xv[0] + xv[1]) + (xv[2] + xv[3]);
+    const uint32_t w = q >> 3, i = q & 7;
+    const uint32_t slot = 8u * w + (i ^ (((w >> 2) ^ ((w >> 5) & 1u)) & 7u));
+    const uint32_t base = (uint32_t)(p & 1) * kNibBuf + slot * 4u;
+    const float lo[4] = {0.0f, xv[0], xv[1], xv[0] + xv[1]};
+    const float hi[4] = {0.0f, xv[2], xv[3], xv[2] + xv[3]};
+    // entry 0 is 0 for every table: written by each buffer's first build only. Tables wholly
+    // past K are read only at entry 0 (their words are 0), so they need no other entry.
+    if (p < 2) *(lds_f32p*)(size_t)base = 0.0f;
+    if (4u * Q < Kc) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = NibX<TX>::get(xr[p][b], j);
-        xv[j] = 4u * Q + (uint32_t)j < Kc ? v : 0.0f;
+      for (int e = 1; e < 16; ++e) {
+        const float v = (e & 3) == 0 ? hi[e >> 2] : ((e >> 2) == 0 ? lo[e & 3] : lo[e & 3] + hi[e >> 2]);
+        *(lds_f32p*)(size_t)(((uint32_t)e << kNibSH) + base) = v;
       }
-      xs += (xv[0] + xv[1]) + (xv[2] + xv[3]);
-      const uint32_t w = q >> 3, i = q & 7;
-      const uint32_t slot = 8u * w + (i ^ (((w >> 2) ^ ((w >> 5) & 1u)) & 7u));
-      const uint32_t base = (uint32_t)(p & 1) * kNibBuf + slot * 4u;
-      const float lo[4] = {0.0f, xv[0], xv[1], xv[0] + xv[1]};
-      const float hi[4] = {0.0f, xv[2], xv[3], xv[2] + xv[3]};
-      // entry 0 is 0 for every table: written by each buffer's first build only. Tables wholly
-      // past K are read only at entry 0 (their words are 0), so they need no other entry.
-      if (p < 2) *(lds_f32p*)(size_t)base = 0.0f;
-      if (4u * Q < Kc) {
+    }
+  };
+  // phase p's tables: phase 0 by the first waves (their activations arrive first: the
+  // memory returns to a block's waves in launch order), later phases one per thread
+  auto build = [&](int p) {
+    if (p == 0) {
+      if (b0) {
 #pragma unroll
-        for (int e = 1; e < 16; ++e) {
-          const float v = (e & 3) == 0 ? hi[e >> 2] : ((e >> 2) == 0 ? lo[e & 3] : lo[e & 3] + hi[e >> 2]);
-          *(lds_f32p*)(size_t)(((uint32_t)e << kNibSH) + base) = v;
-        }
+        for (int b = 0; b < kTB0; ++b) build_one(0, (uint32_t)(b * kB0Threads + tid), x0[b]);
       }
+    } else {
+      build_one(p, (uint32_t)tid, xr[p]);
     }
     if (p == NPH - 1) {
       // every column has been seen: publish this wave's share of sum x (a barrier follows)
@@ -210,10 +225,14 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
           const uint32_t w = wd[r][p][j][i];
           const uint32_t o = 2048u * (uint32_t)j;
           const uint32_t* c = cb[p & 1];
-          float t = (lds_f32((nib_entry<0, kNibSH>(w) | c[0]) + o) + lds_f32((nib_entry<1, kNibSH>(w) | c[1]) + o)) +
-                    (lds_f32((nib_entry<2, kNibSH>(w) | c[2]) + o) + lds_f32((nib_entry<3, kNibSH>(w) | c[3]) + o));
-          t += (lds_f32((nib_entry<4, kNibSH>(w) | c[4]) + o) + lds_f32((nib_entry<5, kNibSH>(w) | c[5]) + o)) +
-               (lds_f32((nib_entry<6, kNibSH>(w) | c[6]) + o) + lds_f32((nib_entry<7, kNibSH>(w) | c[7]) + o));
+          const uint32_t ev = ((w << 4) & 0xf0f0f0f0u) | lh4;  // byte m: nibble 2 m
+          const uint32_t od = (w & 0xf0f0f0f0u) | lh4;         // byte m: nibble 2 m + 1
+          // selector: byte 0 <- c byte 0, byte 1 <- word byte m, byte 2 <- c byte 2, byte 3 <- 0
+          auto at = [&](uint32_t src, uint32_t ci, uint32_t m) {
+            return lds_f32(__builtin_amdgcn_perm(src, ci, 0x0c020000u | ((4u + m) << 8)) + o);
+          };
+          float t = (at(ev, c[0], 0) + at(od, c[1], 0)) + (at(ev, c[2], 1) + at(od, c[3], 1));
+          t += (at(ev, c[4], 2) + at(od, c[5], 2)) + (at(ev, c[6], 3) + at(od, c[7], 3));
           acc[r][i] += t;
         }
       }

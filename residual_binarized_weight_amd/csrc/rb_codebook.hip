@@ -217,21 +217,51 @@ __global__ __launch_bounds__(kCbThreads) __attribute__((amdgpu_waves_per_eu(1, 4
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. indices and scales of this lane's units
-  uint32_t id[NPH][2][4], sc[NPH][2][5];
+  // 2. indices and scales of this lane's units: the 4 indices of a unit are one 8-byte load,
+  // its 5 scales one 12-byte load from the dword boundary at or below them. A dword that
+  // straddles the end of a row's indices or scales may read as 0, so the row's last index and
+  // last scale are also loaded alone and put in place (entries past the row's end meet
+  // columns past K, whose activations are 0, so their values do not matter).
+  typedef uint32_t cb_u32x3 __attribute__((ext_vector_type(3)));
+  cb_u32x2 idw[NPH][2];
+  cb_u32x3 scw[NPH][2];
 #pragma unroll
   for (int ph = 0; ph < NPH; ++ph)
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int ul = lane + 64 * it;
       const int64_t ug = (int64_t)ph * UP + ul;
-      const bool ok = ul < UP;  // units past the row end read 0 through the row resources
-#pragma unroll
-      for (int r = 0; r < 4; ++r) id[ph][it][r] = buf_u16(ri, ok ? (uint32_t)((4 * ug + r) * 2) : OOB, 0);
-#pragma unroll
-      for (int r = 0; r < 5; ++r) sc[ph][it][r] = buf_u16(rs, ok ? (uint32_t)((5 * ug + r) * 2) : OOB, 0);
+      const bool ok = ul < UP;  // units past the phase read 0 through the row resources
+      idw[ph][it] = __builtin_bit_cast(
+          cb_u32x2, __builtin_amdgcn_raw_buffer_load_b64(ri, ok ? (int)(ug * 8) : (int)OOB, 0, 0));
+      scw[ph][it] = __builtin_bit_cast(
+          cb_u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs, ok ? (int)((ug * 10) & ~3ll) : (int)OOB, 0, 0));
     }
+  const uint32_t id_last = buf_u16(ri, (uint32_t)((nb - 1) * 2), 0);
+  const uint32_t sc_last = buf_u16(rs, (uint32_t)((G - 1) * 2), 0);
   __builtin_amdgcn_sched_barrier(0);
+  uint32_t id[NPH][2][4], sc[NPH][2][5];
+#pragma unroll
+  for (int ph = 0; ph < NPH; ++ph)
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int64_t ug = (int64_t)ph * UP + lane + 64 * it;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t v = (idw[ph][it][r >> 1] >> (16 * (r & 1))) & 0xffffu;
+        id[ph][it][r] = 4 * ug + r == nb - 1 ? id_last : v;
+      }
+      // the unit's scales start 0 or 2 bytes into the loaded dwords
+      const uint32_t sh = (uint32_t)((ug * 10) & 3) * 8u;
+      const cb_u32x3 d = scw[ph][it];
+      const uint32_t q[3] = {__builtin_amdgcn_alignbit(d[1], d[0], sh), __builtin_amdgcn_alignbit(d[2], d[1], sh),
+                             d[2] >> sh};
+#pragma unroll
+      for (int r = 0; r < 5; ++r) {
+        const uint32_t v = (q[r >> 1] >> (16 * (r & 1))) & 0xffffu;
+        sc[ph][it][r] = 5 * ug + r == G - 1 ? sc_last : v;
+      }
+    }
 
   // 3. codewords (indices are < c by contract; clamped so a bad index cannot read past the codebook)
   uint32_t cw[NPH][2][4];

@@ -273,6 +273,27 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
     rows["a8_codebook_gemv_4096x11008_m1"] = roof("hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us,
                                                   algorithmic_bytes=byt,
                                                   note="bound in practice by 2.26 M random codeword reads from L2")
+    # the codeword reads against the rate of random 4-byte reads from the same 256 KB table
+    # (a plain gather kernel, timed here)
+    import ctypes
+    from residual_binarized_weight_amd import _lib
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    per_thread, blocks = 64, 1024
+    gcall = lambda: _lib.lib.rb_bench_gather(ctypes.c_void_p(C.data_ptr()), C.numel(), per_thread,
+                                              ctypes.c_void_p(sink.data_ptr()), blocks, None)
+    for _ in range(2):
+        assert gcall() == 0
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        gcall()
+    e1.record()
+    torch.cuda.synchronize()
+    gps = blocks * 256 * per_thread / (e0.elapsed_time(e1) * 1e-3 / 5) / 1e9
+    gathers = Nc * nb
+    rows["a8_codebook_gemv_4096x11008_m1"]["gather_roofline"] = {
+        "gathers": gathers, "achieved": round(gathers / (us * 1e-6) / 1e9, 2), "peak": round(gps, 2),
+        "unit": "G gathers/s", "frac": round(gathers / (us * 1e-6) / 1e9 / gps, 4)}
     if with_oracle:
         RG = 1024
         idx_s = idx[:RG].cpu().numpy().view(np.uint16)

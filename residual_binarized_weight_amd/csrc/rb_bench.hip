@@ -1,5 +1,6 @@
-// rb_bench.hip -- streaming-read probe: the HBM read rate a plain kernel reaches for a
-// given footprint, the ceiling against which the product kernels are read.
+// rb_bench.hip -- measurement probes, not part of the method: the HBM read rate a plain
+// kernel reaches for a given footprint, and the rate of random 4-byte reads from a small
+// table; the ceilings against which the product kernels are read.
 #include "rb_device.hpp"
 
 namespace {
@@ -51,5 +52,38 @@ __global__ void spin_kernel(uint64_t ticks) {
 extern "C" int rb_bench_spin(double microseconds, void* stream) {
   if (!(microseconds >= 0.0) || microseconds > 1.0e6) return 1;
   spin_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>((uint64_t)(microseconds * 100.0));
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+namespace {
+
+// Random 4-byte gathers from a table of `mask + 1` dwords (a power of two): each thread
+// makes `per_thread` reads at indices from its own linear congruential sequence. With a
+// 256 KB table this is the rate of the codeword reads of the codebook product.
+__global__ __launch_bounds__(256) void gather_kernel(const uint32_t* __restrict__ table, uint32_t mask,
+                                                     int32_t per_thread, uint32_t* __restrict__ sink) {
+  uint32_t h = (blockIdx.x * 256u + threadIdx.x) * 2654435761u + 12345u;
+  uint32_t acc = 0u;
+  for (int32_t g = 0; g < per_thread; g += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      h = h * 1664525u + 1013904223u;
+      v[u] = table[(h >> 7) & mask];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads alive; practically never taken
+}
+
+}  // namespace
+
+extern "C" int rb_bench_gather(const uint32_t* table, uint32_t entries, int32_t per_thread, uint32_t* sink,
+                               int32_t blocks, void* stream) {
+  if (!table || !sink || entries == 0 || (entries & (entries - 1)) != 0 || per_thread < 8 ||
+      per_thread % 8 != 0 || blocks < 1)
+    return 1;
+  gather_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(table, entries - 1, per_thread, sink);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }

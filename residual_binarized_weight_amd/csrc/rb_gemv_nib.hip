@@ -9,9 +9,9 @@
 // in the 4-bit pattern e (T_q[0] = 0). Per row and plane, Sum_c B x = 2 T - S with
 // T = sum over nibbles of T_q[bits] and S = sum of x (the masked-add identity), so
 //   y[n] = sum_i g_i[n] * (2 T_i[n] - S).
-// 16 entries per 4 columns is 4 table bytes per column, so the tables of a whole row fit in
-// LDS in at most two phases and a block can own complete rows: no cross-block reduction,
-// deterministic, no workspace.
+// 16 entries per 4 columns is 4 table bytes per column, so the tables of a whole row pass
+// through LDS in a few double-buffered phases of 4096 columns (up to four: K <= 16384) and a
+// block can own complete rows: no cross-block reduction, deterministic, no workspace.
 //
 // Layout: entry e of all tables of a phase is one 4 KB row of LDS (entry-major);
 // nibble i of word w sits in slot 8 w + (i ^ a(w)), a(w) = ((w >> 2) ^ ((w >> 5) & 1)) & 7.

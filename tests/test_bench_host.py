@@ -63,3 +63,15 @@ def test_multi_gpu_request_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_kernel_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    src = "// header\nint f(int a) {  // add one\n  return a + 1; /* block\n comment */\n}\n"
+    p = tmp_path / "k.hip"
+    p.write_text(src)
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(p)])
+    h0 = bench.kernel_source_hash()
+    p.write_text(src.replace("// add one", "// adds one to a").replace("block\n comment", "other"))
+    assert bench.kernel_source_hash() == h0
+    p.write_text(src.replace("a + 1", "a + 2"))
+    assert bench.kernel_source_hash() != h0

@@ -1,7 +1,7 @@
 """Plain, slow CPU oracle for residual binarized weights.
 
 TEST INFRASTRUCTURE ONLY. The parity tests (``tests/``), ``__graft_entry__.smoke()``
-and the ``cpu_baseline`` leg of ``bench.py`` are the only callers. Nothing under
+and the CPU baseline timings of ``bench.py`` are the only callers. Nothing under
 ``residual_binarized_weight_amd/`` imports, links or runs this file, and this file
 imports nothing from there: the two implementations share no code. Only the seeded
 input generators (``workloads/``, random draws only) feed both.
@@ -20,6 +20,9 @@ Sources (web pages on the method; cited by title and section):
   R_0 = W_FP, B_i = sign(R_{i-1}), W_i = g_i (.) B_i (.) h_i, R_i = R_{i-1} - W_i;
   deployment: derive B_i once, freeze, drop W_FP). Section "Technical novelty"
   (32 columns packed into one uint32). Section "Limitations" (2.02 effective bits).
+  Section "Method step details", Algorithm 1 (function-aware initialization: I/O
+  channel importance scaling W' = s_out^a_out (.) W (.) s_in^a_in, iterative residual
+  SVID over T_max = 20 Gauss-Seidel sweeps with rank-1 SVD scales, mapping back).
 * [BTC] "亚1比特大模型量化技术突破与实践" (BTC-LLM sub-1-bit binary codebook page).
   Section 2.1.1 (binary codebook; sign with 0 -> +1; Hamming distance by XOR +
   popcount), 2.1.2 (LUT-GEMM: precompute input-block x codeword sums, accumulate by
@@ -38,6 +41,12 @@ Readings taken where the pages are silent:
 5. Group mode (codebook scales): the same rule over 16-column groups, h = 1.
 6. Codebook blocks of v columns, the last one padded with +1 (signs of zero
    weights); ties in Hamming distance go to the lowest codeword index.
+7. Initialization (RaBiT Algorithm 1): the residual of path i subtracts the other
+   paths at their latest values (Gauss-Seidel, as the page names it; its formula's
+   subscript is garbled), the paths start at zero (the first sweep is the greedy
+   residual SVID), and the rank-1 fit of |R| is split evenly, ||g|| = ||h|| =
+   sqrt(sigma_1). I/O scaling multiplies rows by s_out^a_out and columns by
+   s_in^a_in before the sweeps and divides the scales by them afterwards.
 """
 from __future__ import annotations
 
@@ -337,3 +346,69 @@ def storage_bits_per_weight(N: int, K: int, k: int, scale_bits: int = 16, has_h:
     """
     per_plane_scales = N + (K if has_h else 0)
     return k + scale_bits * k * per_plane_scales / (N * K)
+
+
+# ---------------------------------------------------------------------------
+# initialization: I/O-importance scaling + iterative residual SVID
+# ---------------------------------------------------------------------------
+def svid_step(R: np.ndarray):
+    """One sign-value-independent decomposition of a residual R (N x K):
+    B = sign(R) (0 -> +1) and the top singular pair (sigma, u, v) of |R|, returned as
+    g = sqrt(sigma) u and h = sqrt(sigma) v, both >= 0, so that B (.) g h^T approximates R.
+
+    [RaBiT, "Method step details", Algorithm 1: each path's scales are extracted from its
+    target residual by a rank-1 SVD approximation] |R| is nonnegative, so its top singular
+    vectors can be taken nonnegative (Perron-Frobenius); the sign is fixed by making their
+    sums positive. The top pair is a library SVD (full SVD when min(N, K) <= 512, else
+    scipy's ARPACK svds from a deterministic start vector to machine precision).
+    """
+    R = np.asarray(R, dtype=np.float64)
+    A = np.abs(R)
+    N, K = A.shape
+    if min(N, K) <= 512:
+        U, S, Vt = np.linalg.svd(A, full_matrices=False)
+        u, s, v = U[:, 0], S[0], Vt[0]
+    else:
+        from scipy.sparse.linalg import svds
+        U, S, Vt = svds(A, k=1, tol=0, v0=np.ones(min(N, K)), random_state=0)
+        u, s, v = U[:, 0], S[0], Vt[0]
+    if u.sum() < 0:
+        u, v = -u, -v
+    B = np.where(R >= 0.0, 1.0, -1.0)          # -0.0 >= 0 holds: sign(0) = +1
+    return B, math.sqrt(s) * u, math.sqrt(s) * v
+
+
+def svid_init(W: np.ndarray, k: int, T: int = 20, s_in: np.ndarray | None = None,
+              s_out: np.ndarray | None = None, a_in: float = 0.0, a_out: float = 0.0):
+    """Function-aware initialization of k residual paths.
+
+    [RaBiT, "Method step details", Algorithm 1]
+      W' = s_out^a_out (.) W (.) s_in^a_in        (I/O channel importance scaling: s_in
+                                                    per input column, s_out per output row)
+      for t = 1..T, for path i = 1..k (Gauss-Seidel: the other paths at their latest values)
+        R_i = W' - sum_{j != i} What_j;  B_i, g'_i, h'_i = SVID(R_i);  What_i = g'_i (.) B_i (.) h'_i
+      g_i = s_out^-a_out (.) g'_i,  h_i = s_in^-a_in (.) h'_i  (back to the original domain)
+    The paths start at What_j = 0, so the first sweep is the greedy residual SVID. Returns the
+    sign planes (packed as in `pack_bits`), g [k][N], h [k][K] (original domain), the scaled-domain
+    g', h', and the objective ||W' - sum_i What_i||_F after every path update.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    N, K = W.shape
+    fo = np.ones(N) if s_out is None else np.asarray(s_out, dtype=np.float64) ** a_out
+    fi = np.ones(K) if s_in is None else np.asarray(s_in, dtype=np.float64) ** a_in
+    Wp = fo[:, None] * W * fi[None, :]
+    What = np.zeros((k, N, K))
+    B = np.ones((k, N, K))
+    gp = np.zeros((k, N))
+    hp = np.zeros((k, K))
+    history = []
+    for _ in range(T):
+        What_prev = What.copy()  # the previous sweep's paths (a Jacobi sweep would use these)
+        for i in range(k):
+            R = Wp - (What.sum(axis=0) - What[i])
+            B[i], gp[i], hp[i] = svid_step(R)
+            What[i] = gp[i][:, None] * B[i] * hp[i][None, :]
+            history.append(float(np.linalg.norm(Wp - What.sum(axis=0))))
+    planes = np.stack([pack_bits(B[i]) for i in range(k)])
+    return {"planes": planes, "B": B, "g": gp / fo[None, :], "h": hp / fi[None, :], "gp": gp, "hp": hp,
+            "history": np.array(history)}

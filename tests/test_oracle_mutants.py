@@ -27,6 +27,12 @@ MUTANTS = {
                                   "scol = np.repeat(np.asarray(s, dtype=np.float64), v, axis=1)[:, :K]"),
     "rounding_ties_away": ("(rem == Fraction(1, 2) and fl % 2 == 1)", "(rem == Fraction(1, 2))"),
     "scale_without_abs": ("absRh = np.abs(R) * hi", "absRh = R * hi"),
+    "svid_jacobi_sweep": ("R = Wp - (What.sum(axis=0) - What[i])",
+                          "R = Wp - (What_prev.sum(axis=0) - What_prev[i])"),
+    "svid_scales_without_sqrt": ("return B, math.sqrt(s) * u, math.sqrt(s) * v", "return B, s * u, v"),
+    "svid_sign_of_zero_is_minus": ("B = np.where(R >= 0.0, 1.0, -1.0)", "B = np.where(R > 0.0, 1.0, -1.0)"),
+    "svid_map_back_multiplies": ('"g": gp / fo[None, :]', '"g": gp * fo[None, :]'),
+    "svid_second_singular_pair": ("u, s, v = U[:, 0], S[0], Vt[0]\n    else:", "u, s, v = U[:, 1], S[1], Vt[1]\n    else:"),
 }
 
 

@@ -401,3 +401,114 @@ def test_group_scales_recover_blockwise_constants():
     res = O.binarize(W, 1, group=group)
     assert np.array_equal(res["g"][0], c)
     assert np.array_equal(O.unpack_bits(res["planes"][0], K), S)
+
+
+# ---------------------------------------------------------------------------
+# initialization: iterative residual SVID with I/O-importance scaling
+# ---------------------------------------------------------------------------
+def _obj(R, B, g, h):
+    return float(np.linalg.norm(R - B * np.outer(g, h)))
+
+
+def test_svid_recovers_sign_times_rank1_magnitude_exactly():
+    # W = S (.) a b^T with a, b > 0: one path, one sweep reproduces W, B = S (closed form)
+    rng = np.random.default_rng(300)
+    a, b = rng.uniform(0.5, 2.0, 23), rng.uniform(0.1, 3.0, 41)
+    S = np.where(rng.random((23, 41)) < 0.5, -1.0, 1.0)
+    W = S * np.outer(a, b)
+    r = O.svid_init(W, 1, T=1)
+    assert np.array_equal(r["B"][0], S)
+    assert np.allclose(np.outer(r["g"][0], r["h"][0]), np.outer(a, b), rtol=1e-12, atol=0)
+    assert r["history"][-1] <= 1e-12 * np.linalg.norm(W)
+    assert np.all(r["g"][0] > 0) and np.all(r["h"][0] > 0)
+    # the planes are the packed signs
+    assert np.array_equal(O.unpack_bits(r["planes"][0], 41), S)
+
+
+def test_svid_step_is_the_alternating_least_squares_optimum():
+    # for B = sign(R), g h^T is the best rank-1 fit of |R|: an independent alternating least
+    # squares solution (no SVD) reaches the same product, and neither a single sign flip nor
+    # a small change of g or h lowers ||R - B (.) g h^T||
+    rng = np.random.default_rng(301)
+    R = rng.standard_t(4, (17, 29))
+    B, g, h = O.svid_step(R)
+    A = np.abs(R)
+    ga, ha = np.ones(17), np.ones(29)
+    for _ in range(2000):
+        ga = A @ ha / (ha @ ha)
+        ha = A.T @ ga / (ga @ ga)
+    assert np.allclose(np.outer(g, h), np.outer(ga, ha), rtol=1e-9, atol=1e-12)
+    best = _obj(R, B, g, h)
+    for (n, c) in itertools.product(range(17), range(29)):
+        Bf = B.copy()
+        Bf[n, c] = -Bf[n, c]
+        assert _obj(R, Bf, g, h) >= best
+    for _ in range(50):
+        assert _obj(R, B, g * (1 + 1e-3 * rng.standard_normal(17)), h) >= best
+        assert _obj(R, B, g, h * (1 + 1e-3 * rng.standard_normal(29))) >= best
+
+
+def test_svid_balanced_split():
+    # only g h^T is determined by the fit; the split taken is the balanced one,
+    # ||g|| = ||h|| = sqrt(sigma_1(|R|)) (a reading: the pages give the rank-1 fit only)
+    R = np.random.default_rng(308).standard_normal((9, 14))
+    B, g, h = O.svid_step(R)
+    s1 = np.linalg.svd(np.abs(R), compute_uv=False)[0]
+    assert math.isclose(np.linalg.norm(g), math.sqrt(s1), rel_tol=1e-12)
+    assert math.isclose(np.linalg.norm(h), math.sqrt(s1), rel_tol=1e-12)
+
+
+def test_svid_sign_of_zero_and_nonnegative_scales():
+    W = wl.heavy_tailed_weights(302, 12, 40)
+    W[3] = 0.0
+    W[5, ::4] = -0.0
+    r = O.svid_init(W, 2, T=2)
+    assert np.all(r["B"][:, 3, :] == 1.0)
+    assert np.all(r["g"] >= 0) and np.all(r["h"] >= 0)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_svid_gauss_seidel_objective_never_increases(k, scaled):
+    # each path update minimises ||W' - sum What|| over that path's (B, g >= 0, h >= 0), so
+    # the objective after every update is non-increasing (block coordinate descent)
+    rng = np.random.default_rng(303 + k)
+    W = wl.heavy_tailed_weights(304 + k, 48, 90)
+    kw = {}
+    if scaled:
+        kw = dict(s_in=rng.lognormal(0, 0.7, 90), s_out=rng.lognormal(0, 0.5, 48), a_in=0.5, a_out=0.3)
+    r = O.svid_init(W, k, T=6, **kw)
+    hst = r["history"]
+    assert np.all(np.diff(hst) <= 1e-12 * hst[0])
+    if k > 1:
+        assert hst[-1] < hst[k - 1]        # the later sweeps improve on the greedy first one
+    else:
+        assert np.allclose(hst, hst[0], rtol=1e-12)   # one path: every sweep repeats the same step
+
+
+def test_svid_first_sweep_is_greedy_residual_svid():
+    # with one sweep, path i is the SVID of W minus the paths before it
+    W = wl.heavy_tailed_weights(305, 30, 70)
+    r = O.svid_init(W, 3, T=1)
+    R = W.copy()
+    for i in range(3):
+        B, g, h = O.svid_step(R)
+        assert np.array_equal(B, r["B"][i])
+        assert np.allclose(np.outer(g, h), np.outer(r["g"][i], r["h"][i]), rtol=1e-10, atol=1e-14)
+        R = R - B * np.outer(g, h)
+
+
+def test_svid_io_scaling_maps_back_consistently():
+    # the scales returned in the original domain rebuild s_out^-a (.) What' (.) s_in^-a, and
+    # zero exponents make the result independent of s_in and s_out
+    rng = np.random.default_rng(306)
+    W = wl.heavy_tailed_weights(307, 20, 50)
+    s_in, s_out = rng.lognormal(0, 1, 50), rng.lognormal(0, 1, 20)
+    r = O.svid_init(W, 2, T=3, s_in=s_in, s_out=s_out, a_in=0.7, a_out=0.4)
+    for i in range(2):
+        orig = r["B"][i] * np.outer(r["g"][i], r["h"][i])
+        scaled = r["B"][i] * np.outer(r["gp"][i], r["hp"][i])
+        assert np.allclose(orig, scaled / np.outer(s_out ** 0.4, s_in ** 0.7), rtol=1e-12, atol=0)
+    r0 = O.svid_init(W, 2, T=3, s_in=s_in, s_out=s_out, a_in=0.0, a_out=0.0)
+    r1 = O.svid_init(W, 2, T=3)
+    assert np.array_equal(r0["B"], r1["B"]) and np.allclose(r0["g"], r1["g"], rtol=1e-12)

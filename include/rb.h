@@ -62,7 +62,8 @@ typedef enum rb_op {
   RB_OP_GEMV = 1,
   RB_OP_GEMM_SMALL = 2,
   RB_OP_CODEBOOK_ENCODE = 3,
-  RB_OP_CODEBOOK_GEMV = 4
+  RB_OP_CODEBOOK_GEMV = 4,
+  RB_OP_SVID_INIT = 5
 } rb_op;
 
 /* Version of this ABI (major*10000 + minor*100 + patch). */
@@ -188,6 +189,36 @@ rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N,
 rb_status rb_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, int32_t c, int32_t v,
                            const void* s, int32_t group, int64_t N, int64_t K, const void* x,
                            int64_t M, void* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rb_svid_init -- function-aware initialization of k residual paths (deploy-time, before
+ * training or packing).
+ *   [RaBiT, "Method step details", Algorithm 1: I/O channel importance scaling, then
+ *   iterative residual SVID over T_max = 20 Gauss-Seidel sweeps with rank-1 SVD scales,
+ *   then the scales mapped back to the original domain]
+ *     W' = s_out^a_out (.) W (.) s_in^a_in; paths start at 0; T sweeps, in each path
+ *     i = 0..k-1 in turn: R_i = W' - sum_{j != i} g'_j (.) B_j (.) h'_j (the other paths at
+ *     their latest values), B_i = sign(R_i) (0 -> +1), (g'_i, h'_i) = (sqrt(s) u, sqrt(s) v)
+ *     for the top singular triple (s, u, v) of |R_i|; g_i = g'_i / s_out^a_out,
+ *     h_i = h'_i / s_in^a_in.
+ *   The singular pair is found by P power iterations (alternating |R| v and |R|^T u passes,
+ *   warm-started from the previous sweep), in fp32, deterministic.
+ *
+ *   W        [N][ldw] fp32 (w_dtype must be RB_F32), 16-byte aligned, ldw >= K a multiple of 4
+ *   k        1..4 paths;  T  sweeps, 1..1000;  P  power iterations per path update, 1..64
+ *   s_in     [K] fp32 input-column importance, > 0, or NULL (all ones);  a_in its exponent
+ *   s_out    [N] fp32 output-row importance, > 0, or NULL (all ones);  a_out its exponent
+ *   planes   output [k][N][ldp] uint32 sign planes (plane format above, padding bits 0), 16-byte
+ *            aligned, ldp >= ceil(K/32); words past ceil(K/32) are not written
+ *   g        output [k][N] fp32 row scales;  h  output [k][K] fp32 column scales (both >= 0)
+ *   ws       rb_workspace_bytes(RB_OP_SVID_INIT, k, N, K, 1) bytes, 16-byte aligned; no
+ *            zero-filling needed (every call writes what it reads); it holds scratch afterwards
+ *   The caller owns every buffer; the call only enqueues on `stream`.
+ */
+rb_status rb_svid_init(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, int32_t k,
+                       int32_t T, int32_t P, const float* s_in, const float* s_out, float a_in, float a_out,
+                       uint32_t* planes, int64_t ldp, float* g, float* h, void* ws, size_t ws_bytes,
+                       void* stream);
 
 #ifdef __cplusplus
 }

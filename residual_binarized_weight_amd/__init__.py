@@ -9,6 +9,7 @@ return CUDA (HIP) tensors on the current device and enqueue on the current strea
   y = gemm_small(planes, g, h, x, K)             same on the matrix cores, larger M
   idx = codebook_encode(sign_plane, K, C, v)     nearest binary codeword per v-block
   y = codebook_gemv(idx, C, v, s, group, x, K)   product on codebook indices
+  planes, g, h = svid_init(W, k)                 function-aware initialization of k paths
 """
 from __future__ import annotations
 
@@ -18,9 +19,9 @@ import torch
 
 from . import _lib
 from ._lib import (RB_F16, RB_F32, RB_BF16, RB_OP_CODEBOOK_GEMV, RB_OP_GEMM_SMALL, RB_OP_GEMV,
-                   RbError, check, lib)
+                   RB_OP_SVID_INIT, RbError, check, lib)
 
-__all__ = ["pack", "gemv", "gemm_small", "codebook_encode", "codebook_gemv", "workspace",
+__all__ = ["pack", "gemv", "gemm_small", "codebook_encode", "codebook_gemv", "svid_init", "workspace",
            "workspace_bytes", "storage_bits_per_weight", "version", "RbError", "lib"]
 
 _DT = {torch.float32: RB_F32, torch.float16: RB_F16, torch.bfloat16: RB_BF16}
@@ -130,3 +131,30 @@ def codebook_gemv(idx, codebook, v: int, s, group: int, x, K: int, ws=None, y=No
                                                    _ptr(ws), 0 if ws is None else ws.numel(),
                                                    _stream()))
     return y
+
+
+def svid_init(W: torch.Tensor, k: int, T: int = 20, P: int = 4, s_in: torch.Tensor | None = None,
+              s_out: torch.Tensor | None = None, a_in: float = 0.0, a_out: float = 0.0,
+              ldp: int | None = None, ws: torch.Tensor | None = None):
+    """Function-aware initialization of k residual paths of W [N][K] (fp32, row stride a
+    multiple of 4): sign planes [k][N][ldp] (int32 storage of the uint32 words) and fp32 scales
+    g [k][N], h [k][K], after T Gauss-Seidel sweeps of residual SVID with P power iterations
+    per path update; s_in [K] / s_out [N] (fp32, > 0) are the I/O importance vectors."""
+    N, K = W.shape
+    Kw = (K + 31) // 32
+    ldp = Kw if ldp is None else ldp
+    if K % 4 != 0 or not W.is_contiguous():
+        # rows of a multiple of 4 floats (16-byte rows), as the entry point requires
+        Wp = torch.zeros((N, (K + 3) // 4 * 4), dtype=W.dtype, device=W.device)
+        Wp[:, :K] = W
+        W = Wp
+    planes = torch.zeros((k, N, ldp), dtype=torch.int32, device=W.device)
+    g = torch.empty((k, N), dtype=torch.float32, device=W.device)
+    h = torch.empty((k, K), dtype=torch.float32, device=W.device)
+    if ws is None:
+        ws = torch.empty((workspace_bytes(RB_OP_SVID_INIT, k, N, K, 1) + 15) // 16 * 16, dtype=torch.uint8,
+                         device=W.device)
+    check("rb_svid_init", lib.rb_svid_init(_ptr(W), _dt(W.dtype), N, K, W.stride(0), k, T, P, _ptr(s_in),
+                                           _ptr(s_out), a_in, a_out, _ptr(planes), ldp, _ptr(g), _ptr(h),
+                                           _ptr(ws), ws.numel(), _stream()))
+    return planes, g, h

@@ -26,7 +26,7 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include")]
 
-SOURCES = ["rb_api.cpp", "rb_pack.hip", "rb_gemv.hip", "rb_gemv_nib.hip", "rb_gemm.hip", "rb_codebook.hip",
+SOURCES = ["rb_api.cpp", "rb_pack.hip", "rb_gemv.hip", "rb_gemv_nib.hip", "rb_gemm.hip", "rb_codebook.hip", "rb_svid.hip",
            "rb_bench.hip"]
 
 

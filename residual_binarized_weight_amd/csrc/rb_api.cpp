@@ -4,6 +4,7 @@
 // without touching the device (and can be tested on a machine with no GPU).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -74,6 +75,7 @@ size_t rb_workspace_bytes(rb_op op, int32_t k, int64_t N, int64_t K, int64_t M) 
     case RB_OP_GEMV: return rb::gemv_workspace_bytes(k, N, K, M);
     case RB_OP_GEMM_SMALL: return rb::gemm_small_workspace_bytes(k, N, K, M);
     case RB_OP_CODEBOOK_GEMV: return rb::codebook_gemv_workspace_bytes(N, K, M);
+    case RB_OP_SVID_INIT: return (N > kMaxDim || K > kMaxDim) ? 0 : rb::svid_workspace_bytes(k, N, K);
     default: return 0;
   }
 }
@@ -167,6 +169,29 @@ rb_status rb_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, int32_
   log_call("rb_codebook_gemv", N, K, M, 1);
   return from_hip(rb::launch_codebook_gemv(idx, codebook, c, v, s, group, N, K, x, M, y, ws,
                                            static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_svid_init(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, int32_t k,
+                       int32_t T, int32_t P, const float* s_in, const float* s_out, float a_in, float a_out,
+                       uint32_t* planes, int64_t ldp, float* g, float* h, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!W || !planes || !g || !h) return RB_ERR_INVALID_ARG;
+  if (!valid_dtype(w_dtype)) return RB_ERR_INVALID_ARG;
+  if (w_dtype != RB_F32) return RB_ERR_UNSUPPORTED;
+  // 16-byte column chunks address a row with 32-bit offsets: K <= 2^28
+  if (N < 1 || K < 1 || N > kMaxDim || K > (int64_t(1) << 28)) return RB_ERR_INVALID_ARG;
+  if (ldw < K || ldw % 4 != 0 || ldp < (K + 31) / 32) return RB_ERR_INVALID_ARG;
+  if (k < 1 || k > 4 || T < 1 || T > 1000 || P < 1 || P > 64) return RB_ERR_INVALID_ARG;
+  if (!std::isfinite(a_in) || !std::isfinite(a_out)) return RB_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(planes, 16) || !aligned(g, 4) || !aligned(h, 4) ||
+      !aligned(s_in, 4) || !aligned(s_out, 4))
+    return RB_ERR_MISALIGNED;
+  const size_t need = rb::svid_workspace_bytes(k, N, K);
+  if (!ws || ws_bytes < need) return RB_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return RB_ERR_MISALIGNED;
+  log_call("rb_svid_init", N, K, 1, k);
+  return from_hip(rb::launch_svid_init(static_cast<const float*>(W), N, K, ldw, k, T, P, s_in, s_out, a_in,
+                                       a_out, planes, ldp, g, h, ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

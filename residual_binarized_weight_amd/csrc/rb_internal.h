@@ -44,4 +44,10 @@ hipError_t launch_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, i
                                 const void* s, int group, int64_t N, int64_t K, const void* x,
                                 int64_t M, void* y, void* ws, hipStream_t st);
 
+// function-aware initialization (iterative residual SVID)
+size_t svid_workspace_bytes(int k, int64_t N, int64_t K);
+hipError_t launch_svid_init(const float* W, int64_t N, int64_t K, int64_t ldw, int k, int T, int P,
+                            const float* s_in, const float* s_out, float a_in, float a_out, uint32_t* planes,
+                            int64_t ldp, float* g, float* h, void* ws, hipStream_t s);
+
 }  // namespace rb

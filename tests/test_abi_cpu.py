@@ -167,3 +167,51 @@ def test_codebook_gemv_rejects(kw, status):
     a.update(kw)
     assert L.rb_codebook_gemv(a["idx"], a["C"], a["c"], a["v"], a["s"], a["group"], a["N"], a["K"], a["x"],
                               a["M"], a["y"], a["ws"], a["wsb"], a["stream"]) == status
+
+
+def _svid(**kw):
+    a = dict(W=P, wdt=_lib.RB_F32, N=16, K=64, ldw=64, k=2, T=3, Pi=4, s_in=None, s_out=None, a_in=0.5,
+             a_out=0.5, planes=P, ldp=2, g=P, h=P, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.rb_svid_init(a["W"], a["wdt"], a["N"], a["K"], a["ldw"], a["k"], a["T"], a["Pi"], a["s_in"],
+                          a["s_out"], a["a_in"], a["a_out"], a["planes"], a["ldp"], a["g"], a["h"], a["ws"],
+                          a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(planes=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(g=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(h=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(wdt=7), _lib.RB_ERR_INVALID_ARG),
+    (dict(wdt=_lib.RB_F16), _lib.RB_ERR_UNSUPPORTED),
+    (dict(N=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(K=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(K=(1 << 28) + 4, ldw=(1 << 28) + 4, ldp=(1 << 23) + 1), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldw=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(K=62, ldw=62), _lib.RB_ERR_INVALID_ARG),          # row stride not a multiple of 4
+    (dict(ldp=1), _lib.RB_ERR_INVALID_ARG),
+    (dict(k=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(k=5), _lib.RB_ERR_INVALID_ARG),
+    (dict(T=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(Pi=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(Pi=65), _lib.RB_ERR_INVALID_ARG),
+    (dict(a_in=float("nan")), _lib.RB_ERR_INVALID_ARG),
+    (dict(a_out=float("inf")), _lib.RB_ERR_INVALID_ARG),
+    (dict(W=P_MIS), _lib.RB_ERR_MISALIGNED),
+    (dict(planes=P_MIS), _lib.RB_ERR_MISALIGNED),
+    (dict(g=ctypes.c_void_p(0x100002)), _lib.RB_ERR_MISALIGNED),
+    (dict(s_in=ctypes.c_void_p(0x100002)), _lib.RB_ERR_MISALIGNED),
+    (dict(ws=None), _lib.RB_ERR_WORKSPACE),
+    (dict(wsb=16), _lib.RB_ERR_WORKSPACE),
+    (dict(ws=P_MIS), _lib.RB_ERR_MISALIGNED),
+])
+def test_svid_init_rejects(kw, status):
+    assert _svid(**kw) == status
+
+
+def test_svid_workspace_grows_with_the_problem():
+    small = L.rb_workspace_bytes(_lib.RB_OP_SVID_INIT, 2, 16, 64, 1)
+    assert small > 0
+    assert L.rb_workspace_bytes(_lib.RB_OP_SVID_INIT, 2, 4096, 11008, 1) > small
+    assert L.rb_workspace_bytes(_lib.RB_OP_SVID_INIT, 3, 16, 64, 1) > small

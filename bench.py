@@ -200,6 +200,37 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
             f"first {R} of the 4096 rows (k=2, fp16 g), bytes scaled per row")
         del Ws
 
+    # next row: function-aware initialization of the 4096x11008 layer, k = 2, T = 20 sweeps,
+    # P = 4 power iterations per path update (each update: 2P + 1 passes over W and the planes)
+    T_sw, P_it = 20, 4
+    Wsv = torch.from_numpy(wl.weights_for("down")).to(dev)
+    ws_sv = torch.empty(rb.workspace_bytes(rb.RB_OP_SVID_INIT, k, N, K, 1), dtype=torch.uint8, device=dev)
+    rb.svid_init(Wsv, k, T=1, P=P_it, ws=ws_sv)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    rb.svid_init(Wsv, k, T=T_sw, P=P_it, ws=ws_sv)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3
+    del Wsv, ws_sv
+
+    def svid_bytes(rows, T):
+        per_pass = rows * K * 4 + (k - 1) * rows * K // 8        # W and the other paths' planes
+        return T * k * ((2 * P_it + 1) * per_pass + rows * K // 8)  # + the new plane
+    byt = svid_bytes(N, T_sw)
+    rows["next_f1_svid_init_down_4096x11008_k2_T20"] = roof(
+        "hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us, algorithmic_bytes=byt, sweeps=T_sw,
+        power_iterations=P_it)
+    if with_oracle:
+        Rs = 256
+        Wso = wl.weights_for("down")[:Rs]
+        rows["next_f1_svid_init_down_4096x11008_k2_T20"]["cpu_oracle"] = oracle_rate(
+            lambda: O.svid_init(Wso, k, T=2), svid_bytes(Rs, 2), 1e9, "GB/s",
+            f"first {Rs} of the 4096 rows, 2 sweeps (exact fp64 SVD per path update), bytes counted as for "
+            f"the GPU's {2 * P_it + 1} passes per update")
+        del Wso
+
     # a6: the 28672x8192 layer on the matrix cores at M = 64 and 256, k = 1 and 2, and the
     # M = 1 product on the same weights; 8 weight copies rotate (470 MB > the 256 MB cache)
     Wd = torch.from_numpy(wl.weights_for("wide")).to(dev)

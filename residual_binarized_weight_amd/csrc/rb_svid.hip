@@ -12,8 +12,9 @@
 // The top singular pair comes from power iteration on |R_i|, which is never stored: every
 // pass forms R_i from W and the other paths' sign planes and scales on the fly.
 //   row pass     t = |R| v^        (one wave per row; v^ = v / ||v||)
-//   column pass  p_b = |R|^T t     over a 16-row tile (per-tile partial sums in the workspace)
-//   reduce       v = sum_b p_b     (fixed order; per-block partial sums of v^2)
+//   column pass  p_b = |R|^T t     over a 64-row tile, its columns split over 16 blocks
+//                                  (per-tile partial sums in the workspace)
+//   reduce       v = sum_b p_b     (fixed order; partial sums of v^2 per 64 columns)
 // P alternations of row + column pass, then a last row pass that also writes B_i's bits, and a
 // finalize step: sigma = ||t||, g'_i = t / sqrt(sigma), h'_i = sqrt(sigma) v^. Each step warm-
 // starts from the path's previous h'_i (ones in the first sweep). |R| is nonnegative and the
@@ -32,7 +33,10 @@ namespace {
 typedef float svid_f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSvidRowWaves = 4;   // rows per block of the row pass (one wave each)
-constexpr int kSvidTileRows = 16;  // rows per block of the column pass
+constexpr int kSvidTileRows = 64;  // rows per tile of the column pass
+constexpr int kSvidColSplit = 16;  // blocks per row tile of the column pass (each 1/16 of K)
+constexpr int kSvidRedCols = 64;   // columns per block of the reduction (and per norm partial)
+constexpr int kSvidRedGroups = 16; // tile groups per block of the reduction
 constexpr int kSvidThreads = 256;
 constexpr uint32_t kSvidOob = 0x80000000u;
 
@@ -52,7 +56,7 @@ __host__ __device__ inline int64_t svid_align64(int64_t n) { return (n + 63) & ~
 
 inline size_t svid_ws_floats(int k, int64_t N, int64_t K, SvidWs* w, float* base) {
   const int64_t K4 = svid_round4(K);
-  const int64_t nvb = (K4 + kSvidThreads - 1) / kSvidThreads;
+  const int64_t nvb = (K4 + kSvidRedCols - 1) / kSvidRedCols;
   const int64_t ntile = (N + kSvidTileRows - 1) / kSvidTileRows;
   int64_t off = 0;
   auto take = [&](int64_t n) {
@@ -136,6 +140,7 @@ __global__ __launch_bounds__(kSvidThreads) void svid_row_kernel(const float* __r
     rb[j] = buffer_rsrc(planes + ((int64_t)j * N + n) * ldp, Kw * 4u);
   }
   float acc = 0.0f;
+#pragma unroll 8
   for (int64_t q0 = 0; q0 < nq; q0 += 64) {
     const int64_t q = q0 + lane;
     const bool in = q < nq;
@@ -186,7 +191,10 @@ __global__ __launch_bounds__(kSvidThreads) void svid_col_kernel(const float* __r
   __amdgpu_buffer_rsrc_t rh[KP];
 #pragma unroll
   for (int j = 0; j < KP; ++j) rh[j] = buffer_rsrc(ws.hp + (int64_t)j * svid_align64(K4), (uint32_t)K4 * 4u);
-  for (int64_t q = threadIdx.x; q < nq; q += kSvidThreads) {
+  // this block's share of the columns: chunk range blockIdx.y of kSvidColSplit
+  const int64_t qper = (nq + kSvidColSplit - 1) / kSvidColSplit;
+  const int64_t qend = (blockIdx.y + 1) * qper < nq ? (blockIdx.y + 1) * qper : nq;
+  for (int64_t q = blockIdx.y * qper + threadIdx.x; q < qend; q += kSvidThreads) {
     const uint32_t off = (uint32_t)(q * 16);
     const uint32_t boff = (uint32_t)(q >> 3) * 4u;  // q < nq keeps q / 8 < Kw
     const uint32_t sh = 4u * (uint32_t)(q & 7);
@@ -195,6 +203,7 @@ __global__ __launch_bounds__(kSvidThreads) void svid_col_kernel(const float* __r
 #pragma unroll
     for (int j = 0; j < KP; ++j) hj[j] = svid_ld4(rh[j], off);
     svid_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
     for (int r = 0; r < rows; ++r) {
       const int64_t n = n0 + r;
       const svid_f32x4 w = svid_ld4(buffer_rsrc(W + n * ldw, (uint32_t)K * 4u), off);
@@ -214,42 +223,41 @@ __global__ __launch_bounds__(kSvidThreads) void svid_col_kernel(const float* __r
   }
 }
 
-// v[k] = sum over tiles of colpart[b][k] (fixed order); nrmv[block] = sum of v^2 in the block
-__global__ __launch_bounds__(kSvidThreads) void svid_reduce_kernel(int64_t K4, int64_t ntile, SvidWs ws) {
-  __shared__ float part[kSvidThreads / 64];
-  const int64_t k = (int64_t)blockIdx.x * kSvidThreads + threadIdx.x;
+// v[k] = sum over tiles of colpart[b][k]: 16 groups of tiles summed in order, then the groups in
+// order; nrmv[block] = sum of v^2 over the block's 64 columns (a fixed butterfly)
+__global__ __launch_bounds__(kSvidRedCols * kSvidRedGroups) void svid_reduce_kernel(int64_t K4, int64_t ntile,
+                                                                                    SvidWs ws) {
+  __shared__ float part[kSvidRedGroups][kSvidRedCols];
+  const int tx = threadIdx.x & (kSvidRedCols - 1), ty = threadIdx.x / kSvidRedCols;
+  const int64_t k = (int64_t)blockIdx.x * kSvidRedCols + tx;
+  const int64_t per = (ntile + kSvidRedGroups - 1) / kSvidRedGroups;
+  const int64_t b0 = ty * per, b1 = (ty + 1) * per < ntile ? (ty + 1) * per : ntile;
   float s = 0.0f;
   if (k < K4)
-    for (int64_t b = 0; b < ntile; ++b) s += ws.colpart[b * K4 + k];
-  if (k < K4) ws.v[k] = s;
-  float s2 = wave_sum(s * s);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s2;
+    for (int64_t b = b0; b < b1; ++b) s += ws.colpart[b * K4 + k];
+  part[ty][tx] = s;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float tot = 0.0f;
-    for (int wv = 0; wv < kSvidThreads / 64; ++wv) tot += part[wv];
-    ws.nrmv[blockIdx.x] = tot;
+  if (ty == 0) {  // wave 0: one column per lane
+    float v = 0.0f;
+#pragma unroll
+    for (int gq = 0; gq < kSvidRedGroups; ++gq) v += part[gq][tx];
+    if (k < K4) ws.v[k] = v;
+    const float s2 = wave_sum(k < K4 ? v * v : 0.0f);
+    if (tx == 0) ws.nrmv[blockIdx.x] = s2;
   }
 }
 
 // start vector: ones over the K columns (first sweep) or the path's previous h'_i; nrmv as above
-__global__ __launch_bounds__(kSvidThreads) void svid_vinit_kernel(int64_t K, int i, int first, SvidWs ws) {
-  __shared__ float part[kSvidThreads / 64];
+__global__ __launch_bounds__(kSvidRedCols) void svid_vinit_kernel(int64_t K, int i, int first, SvidWs ws) {
   const int64_t K4 = svid_round4(K);
-  const int64_t k = (int64_t)blockIdx.x * kSvidThreads + threadIdx.x;
+  const int64_t k = (int64_t)blockIdx.x * kSvidRedCols + threadIdx.x;
   float s = 0.0f;
   if (k < K4) {
     s = first ? (k < K ? 1.0f : 0.0f) : ws.hp[(int64_t)i * svid_align64(K4) + k];
     ws.v[k] = s;
   }
-  float s2 = wave_sum(s * s);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s2;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float tot = 0.0f;
-    for (int wv = 0; wv < kSvidThreads / 64; ++wv) tot += part[wv];
-    ws.nrmv[blockIdx.x] = tot;
-  }
+  const float s2 = wave_sum(s * s);
+  if (threadIdx.x == 0) ws.nrmv[blockIdx.x] = s2;
 }
 
 // sigma = ||t|| (every block sums all of t in the same order), g'_i = t / sqrt(sigma),
@@ -307,7 +315,7 @@ hipError_t run_svid(const float* W, int64_t N, int64_t K, int64_t ldw, int T, in
   SvidWs ws;
   svid_ws_floats(KP, N, K, &ws, static_cast<float*>(wsp));
   const int64_t K4 = svid_round4(K);
-  const int nvb = (int)((K4 + kSvidThreads - 1) / kSvidThreads);
+  const int nvb = (int)((K4 + kSvidRedCols - 1) / kSvidRedCols);
   const int64_t ntile = (N + kSvidTileRows - 1) / kSvidTileRows;
   const int64_t nmax = N > K4 ? N : K4;
   const unsigned gvec = (unsigned)((nmax + kSvidThreads - 1) / kSvidThreads);
@@ -315,11 +323,12 @@ hipError_t run_svid(const float* W, int64_t N, int64_t K, int64_t ldw, int T, in
   svid_prep_kernel<<<gvec, kSvidThreads, 0, s>>>(N, K, KP, s_in, s_out, a_in, a_out, ws);
   for (int t = 0; t < T; ++t) {
     for (int i = 0; i < KP; ++i) {
-      svid_vinit_kernel<<<nvb, kSvidThreads, 0, s>>>(K, i, t == 0, ws);
+      svid_vinit_kernel<<<nvb, kSvidRedCols, 0, s>>>(K, i, t == 0, ws);
       for (int p = 0; p < P; ++p) {
         svid_row_kernel<KP, false><<<grow, kSvidThreads, 0, s>>>(W, N, K, ldw, i, planes, ldp, ws, nvb);
-        svid_col_kernel<KP><<<(unsigned)ntile, kSvidThreads, 0, s>>>(W, N, K, ldw, i, planes, ldp, ws);
-        svid_reduce_kernel<<<nvb, kSvidThreads, 0, s>>>(K4, ntile, ws);
+        svid_col_kernel<KP><<<dim3((unsigned)ntile, kSvidColSplit), kSvidThreads, 0, s>>>(W, N, K, ldw, i, planes,
+                                                                                    ldp, ws);
+        svid_reduce_kernel<<<nvb, kSvidRedCols * kSvidRedGroups, 0, s>>>(K4, ntile, ws);
       }
       svid_row_kernel<KP, true><<<grow, kSvidThreads, 0, s>>>(W, N, K, ldw, i, planes, ldp, ws, nvb);
       svid_finalize_kernel<<<gvec, kSvidThreads, 0, s>>>(N, K, i, nvb, ws);

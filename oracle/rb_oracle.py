@@ -23,6 +23,9 @@ Sources (web pages on the method; cited by title and section):
   Section "Method step details", Algorithm 1 (function-aware initialization: I/O
   channel importance scaling W' = s_out^a_out (.) W (.) s_in^a_in, iterative residual
   SVID over T_max = 20 Gauss-Seidel sweeps with rank-1 SVD scales, mapping back).
+  Algorithm 2 also gives the coupled-training step: the forward derives the paths from
+  the shared weight with the learnable scales, the backward passes the effective-weight
+  gradient to the shared weight and differentiates the scales with B held constant.
 * [BTC] "亚1比特大模型量化技术突破与实践" (BTC-LLM sub-1-bit binary codebook page).
   Section 2.1.1 (binary codebook; sign with 0 -> +1; Hamming distance by XOR +
   popcount), 2.1.2 (LUT-GEMM: precompute input-block x codeword sums, accumulate by
@@ -412,3 +415,53 @@ def svid_init(W: np.ndarray, k: int, T: int = 20, s_in: np.ndarray | None = None
     planes = np.stack([pack_bits(B[i]) for i in range(k)])
     return {"planes": planes, "B": B, "g": gp / fo[None, :], "h": hp / fi[None, :], "gp": gp, "hp": hp,
             "history": np.array(history)}
+
+
+# ---------------------------------------------------------------------------
+# coupled training step (forward with dynamically derived paths, straight-through backward)
+# ---------------------------------------------------------------------------
+def qat_forward(W: np.ndarray, g: np.ndarray, h: np.ndarray, X: np.ndarray):
+    """Forward pass of a coupled-training layer.
+
+    [RaBiT, "Method step details", Algorithm 2, forward] R_0 = W_FP; for each path i:
+    B_i = sign(R_{i-1}) (0 -> +1), What_i = g_i (.) B_i (.) h_i, R_i = R_{i-1} - What_i; the
+    layer multiplies by the effective weight What = sum_i What_i: Y = X What^T for X [M][K].
+    g [k][N] and h [k][K] are the learnable scales (not recomputed from R). Returns Y, What,
+    B [k][N][K] and the packed planes.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    k = g.shape[0]
+    R = W.copy()
+    What = np.zeros_like(W)
+    B = np.empty((k,) + W.shape)
+    for i in range(k):
+        B[i] = np.where(R >= 0.0, 1.0, -1.0)
+        Wi = (g[i][:, None] * B[i]) * h[i][None, :]
+        R = R - Wi
+        What = What + Wi
+    Y = np.atleast_2d(np.asarray(X, dtype=np.float64)) @ What.T
+    planes = np.stack([pack_bits(B[i]) for i in range(k)])
+    return Y, What, B, planes
+
+
+def qat_backward(dY: np.ndarray, X: np.ndarray, What: np.ndarray, B: np.ndarray, g: np.ndarray,
+                 h: np.ndarray):
+    """Backward pass of the same layer.
+
+    [RaBiT, "Method step details", Algorithm 2, backward] the shared weight takes the
+    effective-weight gradient, grad W_FP = grad_What L = dY^T X (straight-through: the
+    derivation of the paths is not differentiated); the scales follow the chain rule with the
+    binary cores B_i held constant: dg_i[n] = sum_c dWhat[n, c] B_i[n, c] h_i[c] and
+    dh_i[c] = sum_n dWhat[n, c] B_i[n, c] g_i[n]. Also dX = dY What for the layer below.
+    """
+    dY = np.atleast_2d(np.asarray(dY, dtype=np.float64))
+    X = np.atleast_2d(np.asarray(X, dtype=np.float64))
+    dW = dY.T @ X
+    dX = dY @ np.asarray(What, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    dg = np.stack([(dW * B[i]) @ h[i] for i in range(g.shape[0])])
+    dh = np.stack([g[i] @ (dW * B[i]) for i in range(g.shape[0])])
+    return dW, dX, dg, dh

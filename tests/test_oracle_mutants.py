@@ -32,6 +32,12 @@ MUTANTS = {
     "svid_scales_without_sqrt": ("return B, math.sqrt(s) * u, math.sqrt(s) * v", "return B, s * u, v"),
     "svid_sign_of_zero_is_minus": ("B = np.where(R >= 0.0, 1.0, -1.0)", "B = np.where(R > 0.0, 1.0, -1.0)"),
     "svid_map_back_multiplies": ('"g": gp / fo[None, :]', '"g": gp * fo[None, :]'),
+    "qat_paths_from_w_not_residual": ("        B[i] = np.where(R >= 0.0, 1.0, -1.0)\n        Wi =",
+                                      "        B[i] = np.where(W >= 0.0, 1.0, -1.0)\n        Wi ="),
+    "qat_residual_sign_flipped": ("        R = R - Wi\n", "        R = R + Wi\n"),
+    "qat_dg_without_h": ("dg = np.stack([(dW * B[i]) @ h[i]", "dg = np.stack([(dW * B[i]) @ np.ones_like(h[i])"),
+    "qat_dh_without_signs": ("dh = np.stack([g[i] @ (dW * B[i])", "dh = np.stack([g[i] @ dW"),
+    "qat_dx_uses_w_not_effective": ("dX = dY @ np.asarray(What, dtype=np.float64)", "dX = dY @ np.sign(np.asarray(What, dtype=np.float64))"),
     "svid_second_singular_pair": ("u, s, v = U[:, 0], S[0], Vt[0]\n    else:", "u, s, v = U[:, 1], S[1], Vt[1]\n    else:"),
 }
 

@@ -512,3 +512,85 @@ def test_svid_io_scaling_maps_back_consistently():
     r0 = O.svid_init(W, 2, T=3, s_in=s_in, s_out=s_out, a_in=0.0, a_out=0.0)
     r1 = O.svid_init(W, 2, T=3)
     assert np.array_equal(r0["B"], r1["B"]) and np.allclose(r0["g"], r1["g"], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# coupled training step: forward derivation and straight-through backward
+# ---------------------------------------------------------------------------
+def _qat_case(seed, N=6, K=9, M=4, k=2):
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((N, K))
+    g = rng.uniform(0.2, 0.6, (k, N))
+    h = rng.uniform(0.5, 1.5, (k, K))
+    X = rng.standard_normal((M, K))
+    dY = rng.standard_normal((M, N))
+    return W, g, h, X, dY
+
+
+def _loss(W, g, h, X, dY):
+    return float(np.sum(dY * O.qat_forward(W, g, h, X)[0]))
+
+
+def test_qat_forward_matches_the_pack_derivation():
+    # with the pack's own (L2-optimal, rounded) scales the forward derives the same planes,
+    # and its effective weight is the pack's dequantized matrix
+    W = wl.heavy_tailed_weights(500, 20, 70)
+    for k in (1, 2, 3):
+        res = O.binarize(W, k)
+        g = res["g"].reshape(k, 20)
+        Y, What, B, planes = O.qat_forward(W, g, np.ones((k, 70)), np.eye(70))
+        assert np.array_equal(planes, res["planes"])
+        assert np.allclose(What, O.dequantize(res["planes"], res["g"], None, 70), rtol=0, atol=1e-15)
+        assert np.allclose(Y, What.T, rtol=0, atol=1e-15)
+
+
+def test_qat_scale_gradients_match_finite_differences():
+    # a small change of one scale flips no sign of any residual here, so B is locally constant
+    # and the chain rule with B fixed is the exact derivative of the loss sum(dY * Y)
+    W, g, h, X, dY = _qat_case(501)
+    _, What, B, _ = O.qat_forward(W, g, h, X)
+    dW, dX, dg, dh = O.qat_backward(dY, X, What, B, g, h)
+    eps = 1e-6
+    for (i, n) in itertools.product(range(2), range(6)):
+        gp, gm = g.copy(), g.copy()
+        gp[i, n] += eps
+        gm[i, n] -= eps
+        assert np.array_equal(O.qat_forward(W, gp, h, X)[2], B)
+        num = (_loss(W, gp, h, X, dY) - _loss(W, gm, h, X, dY)) / (2 * eps)
+        assert math.isclose(num, dg[i, n], rel_tol=1e-6, abs_tol=1e-8)
+    for (i, c) in itertools.product(range(2), range(9)):
+        hp, hm = h.copy(), h.copy()
+        hp[i, c] += eps
+        hm[i, c] -= eps
+        num = (_loss(W, g, hp, X, dY) - _loss(W, g, hm, X, dY)) / (2 * eps)
+        assert math.isclose(num, dh[i, c], rel_tol=1e-6, abs_tol=1e-8)
+
+
+def test_qat_weight_and_input_gradients_match_finite_differences():
+    # dW is the gradient with respect to the effective weight (straight-through), dX the
+    # gradient with respect to the input
+    W, g, h, X, dY = _qat_case(502)
+    _, What, B, _ = O.qat_forward(W, g, h, X)
+    dW, dX, _, _ = O.qat_backward(dY, X, What, B, g, h)
+    eps = 1e-6
+    f = lambda Wh, Xv: float(np.sum(dY * (Xv @ Wh.T)))
+    for (n, c) in itertools.product(range(6), range(9)):
+        E = np.zeros_like(What)
+        E[n, c] = eps
+        assert math.isclose((f(What + E, X) - f(What - E, X)) / (2 * eps), dW[n, c], rel_tol=1e-6, abs_tol=1e-8)
+    for (m, c) in itertools.product(range(4), range(9)):
+        E = np.zeros_like(X)
+        E[m, c] = eps
+        assert math.isclose((f(What, X + E) - f(What, X - E)) / (2 * eps), dX[m, c], rel_tol=1e-6, abs_tol=1e-8)
+
+
+def test_qat_later_paths_fit_the_residual():
+    # path i's signs are those of the residual left by the paths before it (sign(0) = +1)
+    W, g, h, X, _ = _qat_case(503, k=3)
+    W[2, 3] = 0.0
+    _, What, B, _ = O.qat_forward(W, g, h, X)
+    R = W.copy()
+    for i in range(3):
+        assert np.array_equal(B[i], np.where(R >= 0, 1.0, -1.0))
+        R = R - g[i][:, None] * B[i] * h[i][None, :]
+    assert np.allclose(What, W - R, rtol=0, atol=1e-14)

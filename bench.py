@@ -181,6 +181,84 @@ def oracle_rate(fn, amount: float, scale: float, unit: str, sample: str) -> dict
             "sample": f"{sample}; median of {n} runs, {t * 1e3:.0f} ms each"}
 
 
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+
+
+def measure_qat_step(torch, np, rb, wl, dev, with_oracle: bool, M: int = 2048) -> dict:
+    N, K, k = N_ROWS, K_COLS, K_PLANES
+    W = torch.from_numpy(wl.weights_for("down")).to(dev)
+    g, h = (torch.from_numpy(a).to(dev) for a in wl.training_scales(wl.CFG_MLP, k, N, K))
+    X = torch.from_numpy(wl.activations(wl.CFG_MLP, M, K, dtype=np.float32)).to(dev).to(torch.bfloat16)
+    dY = torch.from_numpy(wl.output_grads(wl.CFG_MLP, M, N)).to(dev).to(torch.bfloat16)
+    C = 2
+    Ws = [W] + [W.clone() for _ in range(C - 1)]
+    pls = [torch.zeros((k, N, K // 32), dtype=torch.int32, device=dev) for _ in range(C)]
+    Whs = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(C)]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((N, K), dtype=torch.float32, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dg = torch.empty((k, N), dtype=torch.float32, device=dev)
+    dh = torch.empty((k, K), dtype=torch.float32, device=dev)
+    ws = torch.empty(rb.workspace_bytes(rb.RB_OP_QAT_BACKWARD, k, N, K, M), dtype=torch.uint8, device=dev)
+    rb.qat_forward(Ws[0], g, h, X, planes=pls[0], What=Whs[0], Y=Y)
+    t0 = time.perf_counter()
+    rb.qat_autotune(X, dY, Whs[0], Y, dW, dX)
+    tune_s = time.perf_counter() - t0
+
+    def fwd(i):
+        rb.qat_forward(Ws[i % C], g, h, X, planes=pls[i % C], What=Whs[i % C], Y=Y)
+
+    def bwd(i):
+        rb.qat_backward(dY, X, Whs[i % C], pls[i % C], g, h, ws=ws, dW=dW, dX=dX, dg=dg, dh=dh)
+
+    def step(i):
+        fwd(i)
+        bwd(i)
+
+    def timed(fn, reps=10):
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    der_us = timed(lambda i: rb.qat_derive(Ws[i % C], g, h, planes=pls[i % C], What=Whs[i % C]))
+    fwd_us, bwd_us, step_us = timed(fwd), timed(bwd), timed(step)
+    flops = 3 * 2.0 * M * N * K
+    der_bytes = N * K * (4 + 2) + k * N * K // 8 + 4 * k * (N + K)   # W read, What + planes written
+    row = roof("mfma", flops / (step_us * 1e-6) / 1e12, PEAK_BF16_MFMA_TFLOPS, "TFLOP/s", step_us, flops=flops,
+               tokens=M, dtype="bf16 operands, fp32 accumulation, fp32 dW",
+               forward_us=round(fwd_us, 2), backward_us=round(bwd_us, 2), autotune_s=round(tune_s, 2),
+               derive={"us": round(der_us, 2), "algorithmic_bytes": der_bytes, "bound": "hbm",
+                       "achieved": round(der_bytes / (der_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": round(der_bytes / (der_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+               derive_share_of_rest=round(der_us / (step_us - der_us), 4))
+    out = {f"next_f2_qat_step_down_4096x11008_k2_m{M}": row}
+    if with_oracle:
+        from oracle import rb_oracle as O
+        RQ, MQ = 64, 256
+        Wq = wl.weights_for("down")[:RQ]
+        gq, hq = (a.astype(np.float64) for a in wl.training_scales(wl.CFG_MLP, k, N, K))
+        gq = gq[:, :RQ]
+        Xq = X[:MQ].float().cpu().numpy().astype(np.float64)
+        dYq = dY[:MQ, :RQ].float().cpu().numpy().astype(np.float64)
+
+        def oracle_step():
+            _, Wh_q, B_q, _ = O.qat_forward(Wq, gq, hq, Xq)
+            O.qat_backward(dYq, Xq, Wh_q, B_q, gq, hq)
+        row["cpu_oracle"] = oracle_rate(oracle_step, 3 * 2.0 * MQ * RQ * K, 1e12, "TFLOP/s",
+                                        f"first {RQ} of the 4096 rows, {MQ} of the {M} tokens (fp64), flops "
+                                        f"scaled to the sample")
+    del Ws, pls, Whs, W, X, dY, dW, dX, ws
+    torch.cuda.synchronize()
+    return out
+
+
 def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = True) -> dict:
     """Every step of the path besides the metric product, each on its own workload, timed
     on the GPU against the roofline that bounds it (inputs are seeded synthetic data). With
@@ -230,6 +308,12 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
             f"first {Rs} of the 4096 rows, 2 sweeps (exact fp64 SVD per path update), bytes counted as for "
             f"the GPU's {2 * P_it + 1} passes per update")
         del Wso
+
+    # next row: one coupled-training step of the 4096x11008 layer, k = 2, 2048 tokens in bf16:
+    # forward (derive planes + What from the fp32 weight, Y = X What^T) and backward (dW, dX,
+    # dg, dh); the GEMM kernels are chosen for the shape first (untimed setup); two weight
+    # copies rotate so W is read from HBM
+    rows.update(measure_qat_step(torch, np, rb, wl, dev, with_oracle))
 
     # a6: the 28672x8192 layer on the matrix cores at M = 64 and 256, k = 1 and 2, and the
     # M = 1 product on the same weights; 8 weight copies rotate (470 MB > the 256 MB cache)

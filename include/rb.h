@@ -63,7 +63,8 @@ typedef enum rb_op {
   RB_OP_GEMM_SMALL = 2,
   RB_OP_CODEBOOK_ENCODE = 3,
   RB_OP_CODEBOOK_GEMV = 4,
-  RB_OP_SVID_INIT = 5
+  RB_OP_SVID_INIT = 5,
+  RB_OP_QAT_BACKWARD = 6
 } rb_op;
 
 /* Version of this ABI (major*10000 + minor*100 + patch). */
@@ -219,6 +220,73 @@ rb_status rb_svid_init(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, in
                        int32_t T, int32_t P, const float* s_in, const float* s_out, float a_in, float a_out,
                        uint32_t* planes, int64_t ldp, float* g, float* h, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Coupled training of one layer: the paths are derived from one shared full-precision weight
+ * on every forward; the backward is straight-through with scale gradients.
+ *   [RaBiT, "Method step details", Algorithm 2]
+ *     forward:  R_0 = W; for i = 1..k: B_i = sign(R_{i-1}) (0 -> +1),
+ *               What_i = g_i (.) B_i (.) h_i, R_i = R_{i-1} - What_i; What = sum_i What_i and
+ *               Y = X What^T.
+ *     backward: dW = dY^T X (the shared weight's gradient; the derivation itself is not
+ *               differentiated), dX = dY What, and with the B_i held constant
+ *               dg_i[n] = sum_c dW[n,c] B_i[n,c] h_i[c], dh_i[c] = sum_n dW[n,c] B_i[n,c] g_i[n].
+ *   The residual and the sum What are evaluated in fp64 in the order above (so the signs are
+ *   those of an fp64 evaluation); What is rounded once to the activation type. The dense
+ *   products run on the matrix cores through rocBLAS (fp16/bf16 operands, fp32 accumulation)
+ *   on one rocBLAS handle per device, created on the first call on that device; rocBLAS keeps
+ *   its own device workspace with the handle. These are the only entry points that allocate
+ *   (once per device, on first use) and they serialise their rocBLAS calls on a lock.
+ * Shapes and types shared by the three calls
+ *   W        [N][ldw] fp32 shared weight, ldw >= K; W must be finite
+ *   g, h     [k][N], [k][K] fp32 learnable scales;  k = 1..4;  1 <= N, K <= 2^28
+ *   a_dtype  RB_F16 or RB_BF16: the type of X, dY, What and the GEMM operands
+ *   X        [M][ldx] activations (ldx >= K);  dY [M][lddy] gradient of Y (lddy >= N);
+ *            1 <= M <= 2^31 - 1; every leading dimension <= 2^31 - 1
+ *   planes   [k][N][ldp] uint32 sign planes (plane format above), ldp >= ceil(K/32)
+ *   What     [N][ldwh] effective weight in a_dtype, ldwh >= K
+ *   All 4-byte (fp32, planes) and 2-byte (fp16/bf16) buffers must be aligned to their element
+ *   size; fp32 and fp16/bf16 outputs must not overlap any input.
+ * --------------------------------------------------------------------------------------- */
+
+/* rb_qat_derive -- the forward derivation alone: planes (padding bits 0; words past
+ * ceil(K/32) not written) and What (columns past K not written), one pass over W. */
+rb_status rb_qat_derive(const float* W, int64_t N, int64_t K, int64_t ldw, int32_t k, const float* g,
+                        const float* h, uint32_t* planes, int64_t ldp, void* What, rb_dtype a_dtype,
+                        int64_t ldwh, void* stream);
+
+/* rb_qat_forward -- rb_qat_derive, then Y [M][ldy] = X What^T (ldy >= N) with y_dtype RB_F32
+ * or a_dtype. Planes and What are outputs kept for the backward. */
+rb_status rb_qat_forward(const float* W, int64_t N, int64_t K, int64_t ldw, int32_t k, const float* g,
+                         const float* h, const void* X, rb_dtype a_dtype, int64_t M, int64_t ldx,
+                         uint32_t* planes, int64_t ldp, void* What, int64_t ldwh, void* Y, rb_dtype y_dtype,
+                         int64_t ldy, void* stream);
+
+/* rb_qat_backward -- from the forward's X, What and planes and the incoming dY:
+ *   dW   output [N][lddw] fp32 (lddw >= K), the shared weight's gradient
+ *   dX   output [M][lddx] (lddx >= K), dx_dtype RB_F32 or a_dtype
+ *   dg   output [k][N] fp32;  dh  output [k][K] fp32 (fixed-order fp32 sums: deterministic for
+ *        a given dW)
+ *   ws   rb_workspace_bytes(RB_OP_QAT_BACKWARD, k, N, K, M) bytes, 16-byte aligned, for the
+ *        partial sums of dg and dh; no zero-filling needed. */
+rb_status rb_qat_backward(const void* dY, rb_dtype a_dtype, int64_t M, int64_t lddy, const void* X, int64_t ldx,
+                          const void* What, int64_t ldwh, const uint32_t* planes, int64_t ldp, const float* g,
+                          const float* h, int32_t k, int64_t N, int64_t K, float* dW, int64_t lddw, void* dX,
+                          rb_dtype dx_dtype, int64_t lddx, float* dg, float* dh, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* rb_qat_autotune -- choose the GEMM kernels of the training layer for one shape: for each of
+ * the three products of rb_qat_forward / rb_qat_backward with these sizes, leading dimensions
+ * and types, times rocBLAS's default and every kernel rocBLAS lists for the problem on the
+ * caller's buffers, and records the fastest for this device (process-wide; later calls with
+ * the same shape use it). A setup call: it runs a few thousand products and synchronises
+ * `stream` before returning. X, dY and What are read; Y, dW and dX are overwritten with
+ * unspecified values. Arguments as in rb_qat_forward / rb_qat_backward. Different kernels
+ * may round differently (all accumulate in fp32). */
+rb_status rb_qat_autotune(const void* X, const void* dY, rb_dtype a_dtype, int64_t M, int64_t ldx, int64_t lddy,
+                          const void* What, int64_t ldwh, int64_t N, int64_t K, void* Y, rb_dtype y_dtype,
+                          int64_t ldy, float* dW, int64_t lddw, void* dX, rb_dtype dx_dtype, int64_t lddx,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,10 @@ return CUDA (HIP) tensors on the current device and enqueue on the current strea
   idx = codebook_encode(sign_plane, K, C, v)     nearest binary codeword per v-block
   y = codebook_gemv(idx, C, v, s, group, x, K)   product on codebook indices
   planes, g, h = svid_init(W, k)                 function-aware initialization of k paths
+  planes, What = qat_derive(W, g, h)             coupled training: paths derived from W
+  Y, planes, What = qat_forward(W, g, h, X)      ... and the layer's product Y = X What^T
+  dW, dX, dg, dh = qat_backward(dY, X, What, planes, g, h)   straight-through backward
+  qat_autotune(X, dY, What, Y, dW, dX)           pick the fastest GEMM kernels for a shape
 """
 from __future__ import annotations
 
@@ -19,9 +23,10 @@ import torch
 
 from . import _lib
 from ._lib import (RB_F16, RB_F32, RB_BF16, RB_OP_CODEBOOK_GEMV, RB_OP_GEMM_SMALL, RB_OP_GEMV,
-                   RB_OP_SVID_INIT, RbError, check, lib)
+                   RB_OP_QAT_BACKWARD, RB_OP_SVID_INIT, RbError, check, lib)
 
-__all__ = ["pack", "gemv", "gemm_small", "codebook_encode", "codebook_gemv", "svid_init", "workspace",
+__all__ = ["pack", "gemv", "gemm_small", "codebook_encode", "codebook_gemv", "svid_init", "qat_derive",
+           "qat_forward", "qat_backward", "qat_autotune", "workspace",
            "workspace_bytes", "storage_bits_per_weight", "version", "RbError", "lib"]
 
 _DT = {torch.float32: RB_F32, torch.float16: RB_F16, torch.bfloat16: RB_BF16}
@@ -40,6 +45,20 @@ def _ptr(t: torch.Tensor | None):
         raise ValueError("librb takes device tensors")
     if not t.is_contiguous():
         raise ValueError("librb takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ptr_rows(t: torch.Tensor | None):
+    """A matrix whose rows may be strided (unit stride within a row; the row stride is passed
+    to the library as the leading dimension)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("librb takes device tensors")
+    if t.dim() < 1 or t.stride(-1) != 1 or any(t.stride(d) < 0 for d in range(t.dim())):
+        raise ValueError("librb takes matrices with unit stride along rows")
+    if t.dim() == 3 and t.stride(0) != t.shape[1] * t.stride(1):
+        raise ValueError("librb takes plane stacks with planes stored back to back")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -158,3 +177,73 @@ def svid_init(W: torch.Tensor, k: int, T: int = 20, P: int = 4, s_in: torch.Tens
                                            _ptr(s_out), a_in, a_out, _ptr(planes), ldp, _ptr(g), _ptr(h),
                                            _ptr(ws), ws.numel(), _stream()))
     return planes, g, h
+
+
+def qat_derive(W: torch.Tensor, g: torch.Tensor, h: torch.Tensor, a_dtype=torch.bfloat16,
+               planes: torch.Tensor | None = None, What: torch.Tensor | None = None):
+    """Coupled-training derivation: from the shared fp32 weight W [N][K] (rows may be strided)
+    and fp32 scales g [k][N], h [k][K], the k sign planes [k][N][ceil(K/32)] (int32 storage)
+    and the effective weight What [N][K] in a_dtype (fp16 or bf16)."""
+    N, K = W.shape
+    k = g.shape[0]
+    planes = torch.zeros((k, N, (K + 31) // 32), dtype=torch.int32, device=W.device) if planes is None else planes
+    What = torch.empty((N, K), dtype=a_dtype, device=W.device) if What is None else What
+    check("rb_qat_derive", lib.rb_qat_derive(_ptr_rows(W), N, K, W.stride(0), k, _ptr(g), _ptr(h), _ptr_rows(planes),
+                                             planes.stride(1), _ptr_rows(What), _dt(What.dtype), What.stride(0),
+                                             _stream()))
+    return planes, What
+
+
+def qat_forward(W: torch.Tensor, g: torch.Tensor, h: torch.Tensor, X: torch.Tensor, y_dtype=None,
+                planes: torch.Tensor | None = None, What: torch.Tensor | None = None,
+                Y: torch.Tensor | None = None):
+    """Coupled-training forward: the derivation, then Y [M][N] = X What^T for X [M][K] (fp16 or
+    bf16, rows may be strided); y_dtype fp32 or X's type (default). Returns (Y, planes, What)."""
+    N, K = W.shape
+    M = X.shape[0]
+    k = g.shape[0]
+    planes = torch.zeros((k, N, (K + 31) // 32), dtype=torch.int32, device=W.device) if planes is None else planes
+    What = torch.empty((N, K), dtype=X.dtype, device=W.device) if What is None else What
+    Y = torch.empty((M, N), dtype=y_dtype or X.dtype, device=W.device) if Y is None else Y
+    check("rb_qat_forward", lib.rb_qat_forward(_ptr_rows(W), N, K, W.stride(0), k, _ptr(g), _ptr(h), _ptr_rows(X),
+                                               _dt(X.dtype), M, X.stride(0), _ptr_rows(planes), planes.stride(1),
+                                               _ptr_rows(What), What.stride(0), _ptr_rows(Y), _dt(Y.dtype), Y.stride(0),
+                                               _stream()))
+    return Y, planes, What
+
+
+def qat_backward(dY: torch.Tensor, X: torch.Tensor, What: torch.Tensor, planes: torch.Tensor, g: torch.Tensor,
+                 h: torch.Tensor, dx_dtype=None, ws: torch.Tensor | None = None, dW: torch.Tensor | None = None,
+                 dX: torch.Tensor | None = None, dg: torch.Tensor | None = None, dh: torch.Tensor | None = None):
+    """Coupled-training backward from dY [M][N]: dW = dY^T X (fp32 [N][K]), dX = dY What
+    ([M][K], dx_dtype fp32 or the activation type), dg [k][N] and dh [k][K] (fp32)."""
+    M, N = dY.shape
+    K = X.shape[1]
+    k = g.shape[0]
+    dev = dY.device
+    dW = torch.empty((N, K), dtype=torch.float32, device=dev) if dW is None else dW
+    dX = torch.empty((M, K), dtype=dx_dtype or X.dtype, device=dev) if dX is None else dX
+    dg = torch.empty((k, N), dtype=torch.float32, device=dev) if dg is None else dg
+    dh = torch.empty((k, K), dtype=torch.float32, device=dev) if dh is None else dh
+    if ws is None:
+        ws = torch.empty(max(16, workspace_bytes(RB_OP_QAT_BACKWARD, k, N, K, M)), dtype=torch.uint8, device=dev)
+    check("rb_qat_backward", lib.rb_qat_backward(_ptr_rows(dY), _dt(dY.dtype), M, dY.stride(0), _ptr_rows(X), X.stride(0),
+                                                 _ptr_rows(What), What.stride(0), _ptr_rows(planes), planes.stride(1),
+                                                 _ptr(g), _ptr(h), k, N, K, _ptr_rows(dW), dW.stride(0), _ptr_rows(dX),
+                                                 _dt(dX.dtype), dX.stride(0), _ptr(dg), _ptr(dh), _ptr(ws),
+                                                 ws.numel(), _stream()))
+    return dW, dX, dg, dh
+
+
+def qat_autotune(X: torch.Tensor, dY: torch.Tensor, What: torch.Tensor, Y: torch.Tensor, dW: torch.Tensor,
+                 dX: torch.Tensor):
+    """Time the GEMM kernels rocBLAS offers for this layer shape on these buffers and keep the
+    fastest for later qat_forward / qat_backward calls of the same shape (synchronising; Y, dW
+    and dX are overwritten)."""
+    M, K = X.shape
+    N = What.shape[0]
+    check("rb_qat_autotune", lib.rb_qat_autotune(_ptr_rows(X), _ptr_rows(dY), _dt(X.dtype), M, X.stride(0),
+                                                 dY.stride(0), _ptr_rows(What), What.stride(0), N, K, _ptr_rows(Y),
+                                                 _dt(Y.dtype), Y.stride(0), _ptr_rows(dW), dW.stride(0),
+                                                 _ptr_rows(dX), _dt(dX.dtype), dX.stride(0), _stream()))
+

@@ -11,7 +11,8 @@ LIB_PATH = os.path.join(HERE, "librb.so")
 
 RB_OK, RB_ERR_INVALID_ARG, RB_ERR_UNSUPPORTED, RB_ERR_MISALIGNED, RB_ERR_WORKSPACE, RB_ERR_HIP = range(6)
 RB_F32, RB_F16, RB_BF16 = 0, 1, 2
-RB_OP_PACK, RB_OP_GEMV, RB_OP_GEMM_SMALL, RB_OP_CODEBOOK_ENCODE, RB_OP_CODEBOOK_GEMV, RB_OP_SVID_INIT = range(6)
+(RB_OP_PACK, RB_OP_GEMV, RB_OP_GEMM_SMALL, RB_OP_CODEBOOK_ENCODE, RB_OP_CODEBOOK_GEMV, RB_OP_SVID_INIT,
+ RB_OP_QAT_BACKWARD) = range(7)
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -35,6 +36,15 @@ SIGNATURES = {
                                         _vp, _sz, _vp]),
     "rb_svid_init": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp,
                                     ctypes.c_float, ctypes.c_float, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "rb_qat_derive": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp, ctypes.c_int,
+                                     _i64, _vp]),
+    "rb_qat_forward": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, ctypes.c_int, _i64, _i64,
+                                      _vp, _i64, _vp, _i64, _vp, ctypes.c_int, _i64, _vp]),
+    "rb_qat_backward": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                       _vp, _i32, _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _i64, _vp, _vp,
+                                       _vp, _sz, _vp]),
+    "rb_qat_autotune": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp,
+                                       ctypes.c_int, _i64, _vp, _i64, _vp, ctypes.c_int, _i64, _vp]),
     # streaming-read probe used by the bench (not part of the method)
     "rb_bench_stream_read": (ctypes.c_int, [_vp, _i64, _vp, _i32, _vp]),
     "rb_bench_spin": (ctypes.c_int, [ctypes.c_double, _vp]),

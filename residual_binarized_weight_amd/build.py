@@ -27,7 +27,7 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-I", os.path.join(ROOT, "include")]
 
 SOURCES = ["rb_api.cpp", "rb_pack.hip", "rb_gemv.hip", "rb_gemv_nib.hip", "rb_gemm.hip", "rb_codebook.hip", "rb_svid.hip",
-           "rb_bench.hip"]
+           "rb_qat.hip", "rb_bench.hip"]
 
 
 def _compile(src: str) -> str:
@@ -49,7 +49,7 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs, "-L/opt/rocm/lib", "-lrocblas"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -23,6 +23,23 @@ bool is_pow2_in(int32_t v, int32_t lo, int32_t hi) {
 }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kQatMaxDim = int64_t(1) << 28;  // N and K of the training layer (32-bit byte offsets)
+
+bool act_dtype(rb_dtype d) { return d == RB_F16 || d == RB_BF16; }
+bool elem_aligned(const void* p, rb_dtype d) { return aligned(p, d == RB_F32 ? 4 : 2); }
+
+// shapes shared by the training-layer calls
+rb_status check_qat_layer(int64_t N, int64_t K, int32_t k, const float* g, const float* h,
+                          const uint32_t* planes, int64_t ldp, const void* What, int64_t ldwh, rb_dtype a_dtype) {
+  if (!g || !h || !planes || !What) return RB_ERR_INVALID_ARG;
+  if (k < 1 || k > 4 || N < 1 || K < 1 || N > kQatMaxDim || K > kQatMaxDim) return RB_ERR_INVALID_ARG;
+  if (ldp < (K + 31) / 32 || ldwh < K || ldwh > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (!valid_dtype(a_dtype)) return RB_ERR_INVALID_ARG;
+  if (!act_dtype(a_dtype)) return RB_ERR_UNSUPPORTED;
+  if (!aligned(g, 4) || !aligned(h, 4) || !aligned(planes, 4) || !elem_aligned(What, a_dtype))
+    return RB_ERR_MISALIGNED;
+  return RB_OK;
+}
 
 rb_status from_hip(hipError_t e) {
   if (e == hipSuccess) return RB_OK;
@@ -76,6 +93,7 @@ size_t rb_workspace_bytes(rb_op op, int32_t k, int64_t N, int64_t K, int64_t M) 
     case RB_OP_GEMM_SMALL: return rb::gemm_small_workspace_bytes(k, N, K, M);
     case RB_OP_CODEBOOK_GEMV: return rb::codebook_gemv_workspace_bytes(N, K, M);
     case RB_OP_SVID_INIT: return (N > kMaxDim || K > kMaxDim) ? 0 : rb::svid_workspace_bytes(k, N, K);
+    case RB_OP_QAT_BACKWARD: return (N > kQatMaxDim || K > kQatMaxDim) ? 0 : rb::qat_backward_workspace_bytes(k, N, K);
     default: return 0;
   }
 }
@@ -192,6 +210,83 @@ rb_status rb_svid_init(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, in
   log_call("rb_svid_init", N, K, 1, k);
   return from_hip(rb::launch_svid_init(static_cast<const float*>(W), N, K, ldw, k, T, P, s_in, s_out, a_in,
                                        a_out, planes, ldp, g, h, ws, static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_qat_derive(const float* W, int64_t N, int64_t K, int64_t ldw, int32_t k, const float* g,
+                        const float* h, uint32_t* planes, int64_t ldp, void* What, rb_dtype a_dtype,
+                        int64_t ldwh, void* stream) {
+  if (!W) return RB_ERR_INVALID_ARG;
+  rb_status st = check_qat_layer(N, K, k, g, h, planes, ldp, What, ldwh, a_dtype);
+  if (st != RB_OK) return st;
+  if (ldw < K) return RB_ERR_INVALID_ARG;
+  if (!aligned(W, 4)) return RB_ERR_MISALIGNED;
+  log_call("rb_qat_derive", N, K, 0, k);
+  return from_hip(rb::launch_qat_derive(W, N, K, ldw, k, g, h, planes, ldp, What, a_dtype, ldwh,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_qat_forward(const float* W, int64_t N, int64_t K, int64_t ldw, int32_t k, const float* g,
+                         const float* h, const void* X, rb_dtype a_dtype, int64_t M, int64_t ldx,
+                         uint32_t* planes, int64_t ldp, void* What, int64_t ldwh, void* Y, rb_dtype y_dtype,
+                         int64_t ldy, void* stream) {
+  if (!W || !X || !Y) return RB_ERR_INVALID_ARG;
+  rb_status st = check_qat_layer(N, K, k, g, h, planes, ldp, What, ldwh, a_dtype);
+  if (st != RB_OK) return st;
+  if (ldw < K || M < 1 || M > kMaxDim || ldx < K || ldx > kMaxDim || ldy < N || ldy > kMaxDim)
+    return RB_ERR_INVALID_ARG;
+  if (!valid_dtype(y_dtype)) return RB_ERR_INVALID_ARG;
+  if (y_dtype != RB_F32 && y_dtype != a_dtype) return RB_ERR_UNSUPPORTED;
+  if (!aligned(W, 4) || !elem_aligned(X, a_dtype) || !elem_aligned(Y, y_dtype)) return RB_ERR_MISALIGNED;
+  log_call("rb_qat_forward", N, K, M, k);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  rb_status r = from_hip(rb::launch_qat_derive(W, N, K, ldw, k, g, h, planes, ldp, What, a_dtype, ldwh, s));
+  if (r != RB_OK) return r;
+  return from_hip(rb::launch_qat_forward_gemm(X, a_dtype, M, ldx, What, ldwh, N, K, Y, y_dtype, ldy, s));
+}
+
+rb_status rb_qat_backward(const void* dY, rb_dtype a_dtype, int64_t M, int64_t lddy, const void* X, int64_t ldx,
+                          const void* What, int64_t ldwh, const uint32_t* planes, int64_t ldp, const float* g,
+                          const float* h, int32_t k, int64_t N, int64_t K, float* dW, int64_t lddw, void* dX,
+                          rb_dtype dx_dtype, int64_t lddx, float* dg, float* dh, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!dY || !X || !dW || !dX || !dg || !dh) return RB_ERR_INVALID_ARG;
+  rb_status st = check_qat_layer(N, K, k, g, h, planes, ldp, What, ldwh, a_dtype);
+  if (st != RB_OK) return st;
+  if (M < 1 || M > kMaxDim || lddy < N || lddy > kMaxDim || ldx < K || ldx > kMaxDim || lddw < K ||
+      lddw > kMaxDim || lddx < K || lddx > kMaxDim)
+    return RB_ERR_INVALID_ARG;
+  if (!valid_dtype(dx_dtype)) return RB_ERR_INVALID_ARG;
+  if (dx_dtype != RB_F32 && dx_dtype != a_dtype) return RB_ERR_UNSUPPORTED;
+  if (!elem_aligned(dY, a_dtype) || !elem_aligned(X, a_dtype) || !aligned(dW, 4) || !elem_aligned(dX, dx_dtype) ||
+      !aligned(dg, 4) || !aligned(dh, 4))
+    return RB_ERR_MISALIGNED;
+  const size_t need = rb::qat_backward_workspace_bytes(k, N, K);
+  if (!ws || ws_bytes < need) return RB_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return RB_ERR_MISALIGNED;
+  log_call("rb_qat_backward", N, K, M, k);
+  return from_hip(rb::launch_qat_backward(dY, a_dtype, M, lddy, X, ldx, What, ldwh, planes, ldp, g, h, k, N, K, dW,
+                                          lddw, dX, dx_dtype, lddx, dg, dh, ws, static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_qat_autotune(const void* X, const void* dY, rb_dtype a_dtype, int64_t M, int64_t ldx, int64_t lddy,
+                          const void* What, int64_t ldwh, int64_t N, int64_t K, void* Y, rb_dtype y_dtype,
+                          int64_t ldy, float* dW, int64_t lddw, void* dX, rb_dtype dx_dtype, int64_t lddx,
+                          void* stream) {
+  if (!X || !dY || !What || !Y || !dW || !dX) return RB_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N > kQatMaxDim || K > kQatMaxDim || M < 1 || M > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (ldx < K || ldx > kMaxDim || lddy < N || lddy > kMaxDim || ldwh < K || ldwh > kMaxDim || ldy < N ||
+      ldy > kMaxDim || lddw < K || lddw > kMaxDim || lddx < K || lddx > kMaxDim)
+    return RB_ERR_INVALID_ARG;
+  if (!valid_dtype(a_dtype) || !valid_dtype(y_dtype) || !valid_dtype(dx_dtype)) return RB_ERR_INVALID_ARG;
+  if (!act_dtype(a_dtype)) return RB_ERR_UNSUPPORTED;
+  if ((y_dtype != RB_F32 && y_dtype != a_dtype) || (dx_dtype != RB_F32 && dx_dtype != a_dtype))
+    return RB_ERR_UNSUPPORTED;
+  if (!elem_aligned(X, a_dtype) || !elem_aligned(dY, a_dtype) || !elem_aligned(What, a_dtype) ||
+      !elem_aligned(Y, y_dtype) || !aligned(dW, 4) || !elem_aligned(dX, dx_dtype))
+    return RB_ERR_MISALIGNED;
+  log_call("rb_qat_autotune", N, K, M, 0);
+  return from_hip(rb::launch_qat_autotune(X, dY, a_dtype, M, ldx, lddy, What, ldwh, N, K, Y, y_dtype, ldy, dW, lddw,
+                                          dX, dx_dtype, lddx, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

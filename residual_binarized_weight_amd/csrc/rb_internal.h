@@ -50,4 +50,20 @@ hipError_t launch_svid_init(const float* W, int64_t N, int64_t K, int64_t ldw, i
                             const float* s_in, const float* s_out, float a_in, float a_out, uint32_t* planes,
                             int64_t ldp, float* g, float* h, void* ws, hipStream_t s);
 
+size_t qat_backward_workspace_bytes(int k, int64_t N, int64_t K);
+hipError_t launch_qat_derive(const float* W, int64_t N, int64_t K, int64_t ldw, int k, const float* g,
+                             const float* h, uint32_t* planes, int64_t ldp, void* What, rb_dtype what_dtype,
+                             int64_t ldwh, hipStream_t stream);
+hipError_t launch_qat_forward_gemm(const void* X, rb_dtype a_dtype, int64_t M, int64_t ldx, const void* What,
+                                   int64_t ldwh, int64_t N, int64_t K, void* Y, rb_dtype y_dtype, int64_t ldy,
+                                   hipStream_t stream);
+hipError_t launch_qat_backward(const void* dY, rb_dtype a_dtype, int64_t M, int64_t lddy, const void* X, int64_t ldx,
+                               const void* What, int64_t ldwh, const uint32_t* planes, int64_t ldp, const float* g,
+                               const float* h, int k, int64_t N, int64_t K, float* dW, int64_t lddw, void* dX,
+                               rb_dtype dx_dtype, int64_t lddx, float* dg, float* dh, void* ws, hipStream_t stream);
+hipError_t launch_qat_autotune(const void* X, const void* dY, rb_dtype a_dtype, int64_t M, int64_t ldx, int64_t lddy,
+                               const void* What, int64_t ldwh, int64_t N, int64_t K, void* Y, rb_dtype y_dtype,
+                               int64_t ldy, float* dW, int64_t lddw, void* dX, rb_dtype dx_dtype, int64_t lddx,
+                               hipStream_t stream);
+
 }  // namespace rb

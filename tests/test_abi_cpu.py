@@ -215,3 +215,149 @@ def test_svid_workspace_grows_with_the_problem():
     assert small > 0
     assert L.rb_workspace_bytes(_lib.RB_OP_SVID_INIT, 2, 4096, 11008, 1) > small
     assert L.rb_workspace_bytes(_lib.RB_OP_SVID_INIT, 3, 16, 64, 1) > small
+
+
+P2 = ctypes.c_void_p(0x100002)   # 2-byte aligned only
+
+
+def _qat_derive(**kw):
+    a = dict(W=P, N=16, K=64, ldw=64, k=2, g=P, h=P, planes=P, ldp=2, What=P, adt=_lib.RB_BF16, ldwh=64,
+             stream=None)
+    a.update(kw)
+    return L.rb_qat_derive(a["W"], a["N"], a["K"], a["ldw"], a["k"], a["g"], a["h"], a["planes"], a["ldp"],
+                           a["What"], a["adt"], a["ldwh"], a["stream"])
+
+
+def _qat_forward(**kw):
+    a = dict(W=P, N=16, K=64, ldw=64, k=2, g=P, h=P, X=P, adt=_lib.RB_F16, M=8, ldx=64, planes=P, ldp=2,
+             What=P, ldwh=64, Y=P, ydt=_lib.RB_F32, ldy=16, stream=None)
+    a.update(kw)
+    return L.rb_qat_forward(a["W"], a["N"], a["K"], a["ldw"], a["k"], a["g"], a["h"], a["X"], a["adt"], a["M"],
+                            a["ldx"], a["planes"], a["ldp"], a["What"], a["ldwh"], a["Y"], a["ydt"], a["ldy"],
+                            a["stream"])
+
+
+def _qat_backward(**kw):
+    a = dict(dY=P, adt=_lib.RB_BF16, M=8, lddy=16, X=P, ldx=64, What=P, ldwh=64, planes=P, ldp=2, g=P, h=P,
+             k=2, N=16, K=64, dW=P, lddw=64, dX=P, dxdt=_lib.RB_F32, lddx=64, dg=P, dh=P, ws=P, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return L.rb_qat_backward(a["dY"], a["adt"], a["M"], a["lddy"], a["X"], a["ldx"], a["What"], a["ldwh"],
+                             a["planes"], a["ldp"], a["g"], a["h"], a["k"], a["N"], a["K"], a["dW"], a["lddw"],
+                             a["dX"], a["dxdt"], a["lddx"], a["dg"], a["dh"], a["ws"], a["wsb"], a["stream"])
+
+
+# checks shared by the three training-layer calls
+_QAT_COMMON = [
+    (dict(g=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(h=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(planes=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(What=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(k=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(k=5), _lib.RB_ERR_INVALID_ARG),
+    (dict(N=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(K=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(N=(1 << 28) + 1), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldp=1), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldwh=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(adt=9), _lib.RB_ERR_INVALID_ARG),
+    (dict(adt=_lib.RB_F32), _lib.RB_ERR_UNSUPPORTED),
+    (dict(g=P2), _lib.RB_ERR_MISALIGNED),
+    (dict(h=P2), _lib.RB_ERR_MISALIGNED),
+    (dict(planes=P2), _lib.RB_ERR_MISALIGNED),
+    (dict(What=P_ODD), _lib.RB_ERR_MISALIGNED),
+]
+
+
+@pytest.mark.parametrize("kw,status", _QAT_COMMON + [
+    (dict(W=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldw=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(W=P2), _lib.RB_ERR_MISALIGNED),
+])
+def test_qat_derive_rejects(kw, status):
+    assert _qat_derive(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", _QAT_COMMON + [
+    (dict(W=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(X=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(Y=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(M=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(M=1 << 31), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldx=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldy=15), _lib.RB_ERR_INVALID_ARG),
+    (dict(ydt=_lib.RB_BF16), _lib.RB_ERR_UNSUPPORTED),   # neither fp32 nor the activation type
+    (dict(ydt=5), _lib.RB_ERR_INVALID_ARG),
+    (dict(X=P_ODD), _lib.RB_ERR_MISALIGNED),
+    (dict(Y=P2), _lib.RB_ERR_MISALIGNED),                 # fp32 output
+])
+def test_qat_forward_rejects(kw, status):
+    assert _qat_forward(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", _QAT_COMMON + [
+    (dict(dY=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(X=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(dW=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(dX=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(dg=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(dh=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(M=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(lddy=15), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldx=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(lddw=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(lddx=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(dxdt=_lib.RB_F16), _lib.RB_ERR_UNSUPPORTED),   # activations are bf16 here
+    (dict(dY=P_ODD), _lib.RB_ERR_MISALIGNED),
+    (dict(dW=P2), _lib.RB_ERR_MISALIGNED),
+    (dict(dg=P2), _lib.RB_ERR_MISALIGNED),
+    (dict(ws=None), _lib.RB_ERR_WORKSPACE),
+    (dict(wsb=16), _lib.RB_ERR_WORKSPACE),
+    (dict(ws=P_MIS), _lib.RB_ERR_MISALIGNED),
+])
+def test_qat_backward_rejects(kw, status):
+    assert _qat_backward(**kw) == status
+
+
+def test_qat_workspace_covers_the_partial_sums():
+    # strips of 256 columns x k x N row partials + tiles of 256 rows x k x K column partials
+    ws = L.rb_workspace_bytes(_lib.RB_OP_QAT_BACKWARD, 2, 4096, 11008, 2048)
+    assert ws >= 4 * (43 * 2 * 4096 + 16 * 2 * 11008)
+    assert ws < 4 * (43 * 2 * 4096 + 16 * 2 * 11008) + 512
+    assert L.rb_workspace_bytes(_lib.RB_OP_QAT_BACKWARD, 2, (1 << 28) + 1, 64, 1) == 0
+
+
+def _qat_autotune(**kw):
+    a = dict(X=P, dY=P, adt=_lib.RB_BF16, M=8, ldx=64, lddy=16, What=P, ldwh=64, N=16, K=64, Y=P,
+             ydt=_lib.RB_F32, ldy=16, dW=P, lddw=64, dX=P, dxdt=_lib.RB_BF16, lddx=64, stream=None)
+    a.update(kw)
+    return L.rb_qat_autotune(a["X"], a["dY"], a["adt"], a["M"], a["ldx"], a["lddy"], a["What"], a["ldwh"], a["N"],
+                             a["K"], a["Y"], a["ydt"], a["ldy"], a["dW"], a["lddw"], a["dX"], a["dxdt"], a["lddx"],
+                             a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(dY=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(What=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(Y=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(dW=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(dX=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(M=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(N=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(K=(1 << 28) + 1), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldx=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(lddy=15), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldwh=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldy=15), _lib.RB_ERR_INVALID_ARG),
+    (dict(lddw=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(lddx=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(adt=4), _lib.RB_ERR_INVALID_ARG),
+    (dict(adt=_lib.RB_F32), _lib.RB_ERR_UNSUPPORTED),
+    (dict(ydt=_lib.RB_F16), _lib.RB_ERR_UNSUPPORTED),
+    (dict(dxdt=_lib.RB_F16), _lib.RB_ERR_UNSUPPORTED),
+    (dict(X=P_ODD), _lib.RB_ERR_MISALIGNED),
+    (dict(dW=P2), _lib.RB_ERR_MISALIGNED),
+])
+def test_qat_autotune_rejects(kw, status):
+    assert _qat_autotune(**kw) == status

@@ -5,7 +5,8 @@ arithmetic (no signs, scales, packing or products), so that the oracle under
 ``oracle/`` and the HIP path can both be fed from it without sharing code.
 
 Every draw uses ``numpy.random.default_rng([cfg_id, role, variant])`` with
-role 0 = weights, 1 = outlier columns, 2 = activations, 3 = codebook, so each
+role 0 = weights, 1 = outlier columns, 2 = activations, 3 = codebook, 4 = learnable
+scales, 5 = output gradients, so each
 tensor of each workload is reproducible on its own.
 
 Workloads (stand-ins for the layers the pages measure: the 4096x4096 q_proj of the
@@ -21,12 +22,16 @@ trained weights are not available, so the weight statistics are synthetic):
 * ``wide``     28672x8192, same weight law, k in {1,2}, M in {64,256} fp16 activations.
 * ``codebook`` 4096x11008 sign source of the same weight law, v=20, c=65536 distinct
                seeded 20-bit codewords, fp16 scale per 16 weights, M=1.
+* coupled training of the ``down`` layer: the same weights as the shared fp32 weight,
+  learnable scales g_i ~ 0.8 * 0.02 * 2^-i * U(0.5, 1.5) per row and h_i ~ U(0.5, 1.5) per
+  column (fp32), activations X ~ N(0,1) and output gradients dY ~ N(0, 0.01^2) for M tokens
+  (drawn in fp32; the caller rounds them to bf16 or fp16).
 """
 from __future__ import annotations
 
 import numpy as np
 
-ROLE_W, ROLE_OUTLIER, ROLE_X, ROLE_CODEBOOK = 0, 1, 2, 3
+ROLE_W, ROLE_OUTLIER, ROLE_X, ROLE_CODEBOOK, ROLE_SCALES, ROLE_GRAD = 0, 1, 2, 3, 4, 5
 
 # cfg ids used in the seeds: one per workload family.
 CFG_TINY, CFG_SQUARE, CFG_MLP, CFG_WIDE, CFG_CODEBOOK = 1, 2, 3, 4, 5
@@ -125,3 +130,19 @@ def random_scales(seed: int, k: int, L: int, lo: float = 0.25, hi: float = 2.0,
     if negative_frac > 0:
         h *= np.where(g.random((k, L)) < negative_frac, -1.0, 1.0)
     return h.astype(dtype)
+
+
+def training_scales(cfg_id: int, k: int, N: int, K: int, variant: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Learnable scales of a coupled-training layer: g (k, N) ~ 0.016 * 2^-i * U(0.5, 1.5) and
+    h (k, K) ~ U(0.5, 1.5), fp32 (path i's magnitude halves with i, as residual paths do)."""
+    g_ = rng(cfg_id, ROLE_SCALES, variant)
+    g = g_.uniform(0.5, 1.5, size=(k, N)) * (0.016 * 0.5 ** np.arange(k))[:, None]
+    h = g_.uniform(0.5, 1.5, size=(k, K))
+    return g.astype(np.float32), h.astype(np.float32)
+
+
+def output_grads(cfg_id: int, M: int, N: int, std: float = 0.01, variant: int = 0) -> np.ndarray:
+    """dY ~ N(0, std^2) of shape (M, N), fp32."""
+    g = rng(cfg_id, ROLE_GRAD, variant * 1000 + M)
+    return (g.standard_normal((M, N)) * std).astype(np.float32)
+

@@ -28,7 +28,9 @@ Sources (web pages on the method; cited by title and section):
   gradient to the shared weight and differentiates the scales with B held constant.
 * [BTC] "亚1比特大模型量化技术突破与实践" (BTC-LLM sub-1-bit binary codebook page).
   Section 2.1.1 (binary codebook; sign with 0 -> +1; Hamming distance by XOR +
-  popcount), 2.1.2 (LUT-GEMM: precompute input-block x codeword sums, accumulate by
+  popcount; binary K-means whose M-step sets each centroid to the sign of its members'
+  sum with 0 -> +1; the codebook shrinks to the distinct vectors when there are fewer of
+  them than its preset size), 2.1.2 (LUT-GEMM: precompute input-block x codeword sums, accumulate by
   index), 3.2.1 (index | scale | offset layout, one scale group per 16 weights),
   5.1 (v=20, c=65536 for 13B+ models), 5.2 (index width ceil(log2 c) <= 16).
 
@@ -50,6 +52,12 @@ Readings taken where the pages are silent:
    residual SVID), and the rank-1 fit of |R| is split evenly, ||g|| = ||h|| =
    sqrt(sigma_1). I/O scaling multiplies rows by s_out^a_out and columns by
    s_in^a_in before the sweeps and divides the scales by them afterwards.
+8. Binary K-means (BTC 2.1.1): a codeword that no pattern chose keeps its value; the
+   distinct patterns replace the codebook in ascending order when they number fewer
+   than its size (the entries past them repeat the last distinct pattern, which never
+   wins a tie, so an index still points at a distinct pattern); the caller supplies the
+   initial codebook; an iteration is an E-step (nearest codeword) then an M-step, and
+   a final E-step gives the indices of the returned codebook.
 """
 from __future__ import annotations
 
@@ -312,6 +320,68 @@ def hamming_encode(patterns: np.ndarray, codebook: np.ndarray, chunk: int = 64) 
         d = np.bitwise_count(p[:, None] ^ C[None, :])          # (chunk, c)
         out[s:s + chunk] = np.argmin(d, axis=1)                  # first minimum = lowest index
     return out.reshape(np.shape(patterns)).astype(np.uint16 if C.shape[0] <= 65536 else np.int64)
+
+
+def codebook_mstep(patterns: np.ndarray, idx: np.ndarray, codebook: np.ndarray, v: int):
+    """M-step of binary K-means: each codeword becomes the elementwise sign of the sum of
+    its members' +-1 vectors, a zero sum giving +1; a codeword without members keeps its
+    value. Returns (new codebook as uint32, member count per codeword).
+
+    [BTC 2.1.1: centroid update = sign(sum of the cluster's binary vectors), zeros -> +1]
+    """
+    P = np.asarray(patterns, dtype=np.int64).reshape(-1)
+    I = np.asarray(idx, dtype=np.int64).reshape(-1)
+    C = np.asarray(codebook, dtype=np.uint32)
+    c = C.shape[0]
+    count = np.bincount(I, minlength=c)
+    out = C.copy()
+    word = np.zeros(c, dtype=np.int64)
+    for t in range(v):
+        pm = 2.0 * ((P >> t) & 1) - 1.0                      # bit t of every pattern as +-1
+        total = np.bincount(I, weights=pm, minlength=c)      # sum over each cluster
+        word |= (total >= 0).astype(np.int64) << t
+    has = count > 0
+    out[has] = word[has].astype(np.uint32)
+    return out, count
+
+
+def codebook_distinct(patterns: np.ndarray) -> np.ndarray:
+    """The distinct patterns in ascending order. [BTC 2.1.1: when the number M of distinct
+    vectors is below the preset codebook size, the codebook size becomes M]"""
+    return np.unique(np.asarray(patterns, dtype=np.int64).reshape(-1)).astype(np.uint32)
+
+
+def total_hamming(patterns: np.ndarray, idx: np.ndarray, codebook: np.ndarray) -> int:
+    """Sum over patterns of the Hamming distance to their assigned codeword."""
+    P = np.asarray(patterns, dtype=np.uint32).reshape(-1)
+    I = np.asarray(idx, dtype=np.int64).reshape(-1)
+    return int(np.bitwise_count(P ^ np.asarray(codebook, dtype=np.uint32)[I]).sum())
+
+
+def codebook_learn(patterns: np.ndarray, codebook: np.ndarray, v: int, iters: int):
+    """Binary K-means on v-bit sign patterns from an initial codebook.
+
+    [BTC 2.1.1] If the M distinct patterns are fewer than the c codewords, they become
+    the codebook (ascending, then the last one repeated up to c: the effective size is
+    M). Then `iters` iterations of E-step (nearest codeword by Hamming distance, ties to
+    the lowest index) and M-step (codebook_mstep), and a final E-step. Returns
+    (codebook, idx, M, history of the total Hamming distance after each E-step).
+    """
+    C = np.asarray(codebook, dtype=np.uint32).copy()
+    c = C.shape[0]
+    distinct = codebook_distinct(patterns)
+    M = distinct.shape[0]
+    if M < c:
+        C[:M] = distinct
+        C[M:] = distinct[-1]
+    history = []
+    for _ in range(iters):
+        idx = hamming_encode(patterns, C)
+        history.append(total_hamming(patterns, idx, C))
+        C, _ = codebook_mstep(patterns, idx, C, v)
+    idx = hamming_encode(patterns, C)
+    history.append(total_hamming(patterns, idx, C))
+    return C, idx, M, history
 
 
 def codebook_gemv(idx: np.ndarray, codebook: np.ndarray, v: int, s: np.ndarray, group: int,

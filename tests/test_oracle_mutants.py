@@ -38,6 +38,11 @@ MUTANTS = {
     "qat_dg_without_h": ("dg = np.stack([(dW * B[i]) @ h[i]", "dg = np.stack([(dW * B[i]) @ np.ones_like(h[i])"),
     "qat_dh_without_signs": ("dh = np.stack([g[i] @ (dW * B[i])", "dh = np.stack([g[i] @ dW"),
     "qat_dx_uses_w_not_effective": ("dX = dY @ np.asarray(What, dtype=np.float64)", "dX = dY @ np.sign(np.asarray(What, dtype=np.float64))"),
+    "kmeans_ties_to_minus": ("word |= (total >= 0).astype(np.int64) << t", "word |= (total > 0).astype(np.int64) << t"),
+    "kmeans_empty_cluster_rewritten": ("out[has] = word[has].astype(np.uint32)", "out = word.astype(np.uint32)"),
+    "kmeans_msb_first_bits": ("pm = 2.0 * ((P >> t) & 1) - 1.0", "pm = 2.0 * ((P >> (v - 1 - t)) & 1) - 1.0"),
+    "kmeans_shrinks_when_equal": ("    if M < c:\n        C[:M] = distinct", "    if M <= c:\n        C[:M] = distinct"),
+    "kmeans_shrink_pads_with_first": ("C[M:] = distinct[-1]", "C[M:] = distinct[0]"),
     "svid_second_singular_pair": ("u, s, v = U[:, 0], S[0], Vt[0]\n    else:", "u, s, v = U[:, 1], S[1], Vt[1]\n    else:"),
 }
 

@@ -594,3 +594,84 @@ def test_qat_later_paths_fit_the_residual():
         assert np.array_equal(B[i], np.where(R >= 0, 1.0, -1.0))
         R = R - g[i][:, None] * B[i] * h[i][None, :]
     assert np.allclose(What, W - R, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# binary codebook learning (binary K-means)
+# ---------------------------------------------------------------------------
+def test_codebook_mstep_hand_example():
+    # v = 4; cluster 0: 1010, 1000, 0010 (bit sums -3, +1, -3, +1 -> 1010); cluster 1: 0001 and
+    # 0110 tie on bits 0..2 (-> +1) and agree on bit 3 = 0 (-> 0111); cluster 2 has no member and
+    # keeps its codeword
+    P = np.array([0b1010, 0b1000, 0b0010, 0b0001, 0b0110])
+    idx = np.array([0, 0, 0, 1, 1])
+    C = np.array([0b0000, 0b0000, 0b1001], dtype=np.uint32)
+    newC, count = O.codebook_mstep(P, idx, C, 4)
+    assert newC.tolist() == [0b1010, 0b0111, 0b1001]
+    assert count.tolist() == [3, 2, 0]
+
+
+def test_codebook_mstep_majority_minimizes_hamming():
+    # brute force over all 2^v codewords: the M-step word has the least total Hamming distance to
+    # its cluster, and among the minimizers (which differ only in tied bits) it is the one with
+    # every tied bit +1, i.e. the bitwise OR of all minimizers
+    rng = np.random.default_rng(600)
+    v, c = 6, 5
+    P = rng.integers(0, 1 << v, size=60)
+    idx = rng.integers(0, c, size=60)
+    idx[:4] = [0, 0, 1, 1]
+    P[:4] = [0b000111, 0b111000, 0b101010, 0b010101]       # cluster members forcing ties
+    newC, _ = O.codebook_mstep(P, idx, np.zeros(c, np.uint32), v)
+    allw = np.arange(1 << v, dtype=np.uint32)
+    for j in range(c):
+        mem = P[idx == j].astype(np.uint32)
+        d = np.bitwise_count(mem[None, :] ^ allw[:, None]).sum(axis=1)
+        mins = allw[d == d.min()]
+        assert d[newC[j]] == d.min()
+        assert newC[j] == np.bitwise_or.reduce(mins)
+
+
+def test_codebook_learn_never_increases_distortion():
+    rng = np.random.default_rng(601)
+    v = 8
+    P = rng.integers(0, 1 << v, size=(30, 17)) & rng.integers(0, 1 << v, size=(30, 17))   # skewed
+    C0 = rng.choice(1 << v, size=24, replace=False).astype(np.uint32)
+    C, idx, M, hist = O.codebook_learn(P, C0, v, 6)
+    assert M > 24                                          # no shrinking here
+    assert all(a >= b for a, b in zip(hist, hist[1:]))
+    assert hist[-1] < hist[0]
+    # the returned indices are the nearest codewords of the returned codebook
+    d = np.bitwise_count(P.reshape(-1, 1).astype(np.uint32) ^ C[None, :])
+    assert np.array_equal(d[np.arange(d.shape[0]), idx.reshape(-1).astype(np.int64)], d.min(axis=1))
+
+
+def test_codebook_learn_shrinks_to_the_distinct_patterns():
+    # 5 distinct patterns, 8 codewords: the codebook becomes them (ascending, the last repeated),
+    # every pattern is encoded exactly and by its first occurrence
+    rng = np.random.default_rng(602)
+    vals = np.array([37, 3, 900, 511, 64])
+    P = rng.choice(vals, size=(12, 9))
+    C, idx, M, hist = O.codebook_learn(P, np.arange(8, dtype=np.uint32) * 101, 10, 3)
+    assert M == 5
+    assert C.tolist() == [3, 37, 64, 511, 900, 900, 900, 900]
+    assert np.array_equal(C[idx.astype(np.int64)], P.astype(np.uint32))
+    assert idx.max() <= 4 and hist[-1] == 0
+
+
+def test_codebook_learn_keeps_the_codebook_when_not_fewer_patterns():
+    # exactly c distinct patterns: no replacement; with no iteration the initial codebook comes back
+    P = np.array([[5, 9, 12, 9], [12, 5, 7, 7]])
+    C0 = np.array([12, 9, 7, 5], dtype=np.uint32)
+    C, idx, M, _ = O.codebook_learn(P, C0, 4, 0)
+    assert M == 4 and C.tolist() == [12, 9, 7, 5]
+    assert np.array_equal(C[idx.astype(np.int64)], P.astype(np.uint32))
+
+
+def test_codebook_learn_on_layer_signs():
+    # signs of a heavy-tailed layer cut into v = 10 blocks: distortion falls over the iterations
+    W = wl.heavy_tailed_weights(603, 40, 200)
+    words = O.pack_bits(O.sign_pm1(W))
+    P = O.sign_blocks(words, 200, 10)
+    C0 = np.random.default_rng(603).choice(1 << 10, 64, replace=False).astype(np.uint32)
+    _, _, M, hist = O.codebook_learn(P, C0, 10, 4)
+    assert M > 64 and hist[-1] < hist[0]

@@ -32,7 +32,10 @@ Sources (web pages on the method; cited by title and section):
   sum with 0 -> +1; the codebook shrinks to the distinct vectors when there are fewer of
   them than its preset size), 2.1.2 (LUT-GEMM: precompute input-block x codeword sums, accumulate by
   index), 3.2.1 (index | scale | offset layout, one scale group per 16 weights),
-  5.1 (v=20, c=65536 for 13B+ models), 5.2 (index width ceil(log2 c) <= 16).
+  5.1 (v=20, c=65536 for 13B+ models), 5.2 (index width ceil(log2 c) <= 16). Also
+  the zero-mean preprocessing of 2.1.1 (each row shifted by its mean before binarization).
+* [SigmoidBitLinear] the SigmoidBitLinear blog page: weights binarize to {0, scale_row}
+  (a bit keeps the row's scale or gives 0).
 
 Readings taken where the pages are silent:
 
@@ -287,6 +290,36 @@ def gemv(planes: np.ndarray, g: np.ndarray, h: np.ndarray | None, x: np.ndarray,
             y[:, r0:r1] += gg[i, r0:r1][None, :] * (xh @ B.T)
             sabs[:, r0:r1] += np.abs(gg[i, r0:r1])[None, :] * habs[:, None]
     return y, sabs
+
+
+def gemv_variant(planes: np.ndarray, g: np.ndarray, h: np.ndarray | None, mu: np.ndarray | None,
+                 x: np.ndarray, K: int, zero_one: bool):
+    """The product of the cheap weight variants, y = x W_hat^T, with
+    W_hat[n, k] = sum_i g_i[n] * b_i[n, k] * h_i[k] + mu[n], where b is the plane bit read as
+    {-1, +1} (zero_one False) or as {0, 1} (zero_one True), and mu an optional per-row offset.
+
+    [SigmoidBitLinear blog: weights binarize to {0, scale_row}: bit 1 keeps the row's scale,
+    bit 0 gives 0. BTC 2.1.1, zero-mean preprocessing: each row is shifted by its mean mu before
+    binarization, so the row is mu + (binarized W - mu).] Dense float64 product on the
+    dequantized matrix. Returns (y, sum|terms|) with sum|terms|[m, n] =
+    sum_i |g_i[n]| sum_k |h_i[k] x[m, k]| + |mu[n]| sum_k |x[m, k]|.
+    """
+    k, N, _ = planes.shape
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    gg = np.asarray(g, dtype=np.float64).reshape(k, N, -1)[:, :, 0]
+    What = np.zeros((N, K))
+    sabs = np.zeros((x.shape[0], N))
+    for i in range(k):
+        B = unpack_bits(planes[i], K)                         # +-1
+        b = (B > 0).astype(np.float64) if zero_one else B
+        hi = np.ones(K) if h is None else np.asarray(h[i], dtype=np.float64)
+        What += gg[i][:, None] * b * hi[None, :]
+        sabs += np.abs(gg[i])[None, :] * (np.abs(x) @ np.abs(hi))[:, None]
+    if mu is not None:
+        mu = np.asarray(mu, dtype=np.float64)
+        What += mu[:, None]
+        sabs += np.abs(mu)[None, :] * np.abs(x).sum(axis=1)[:, None]
+    return x @ What.T, sabs
 
 
 # ---------------------------------------------------------------------------

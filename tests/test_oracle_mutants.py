@@ -43,6 +43,8 @@ MUTANTS = {
     "kmeans_msb_first_bits": ("pm = 2.0 * ((P >> t) & 1) - 1.0", "pm = 2.0 * ((P >> (v - 1 - t)) & 1) - 1.0"),
     "kmeans_shrinks_when_equal": ("    if M < c:\n        C[:M] = distinct", "    if M <= c:\n        C[:M] = distinct"),
     "kmeans_shrink_pads_with_first": ("C[M:] = distinct[-1]", "C[M:] = distinct[0]"),
+    "variant_zero_one_ignored": ("b = (B > 0).astype(np.float64) if zero_one else B", "b = B"),
+    "variant_offset_dropped": ("        What += mu[:, None]\n", "        What += 0.0\n"),
     "svid_second_singular_pair": ("u, s, v = U[:, 0], S[0], Vt[0]\n    else:", "u, s, v = U[:, 1], S[1], Vt[1]\n    else:"),
 }
 

@@ -675,3 +675,44 @@ def test_codebook_learn_on_layer_signs():
     C0 = np.random.default_rng(603).choice(1 << 10, 64, replace=False).astype(np.uint32)
     _, _, M, hist = O.codebook_learn(P, C0, 10, 4)
     assert M > 64 and hist[-1] < hist[0]
+
+
+# ---------------------------------------------------------------------------
+# cheap product variants: {0, s} planes and a per-row offset
+# ---------------------------------------------------------------------------
+def test_gemv_variant_hand_example():
+    # bits [[1,0,1],[0,1,1]], g = [2, 3], x = [1, 10, 100]
+    planes = O.pack_bits(np.array([[1.0, -1.0, 1.0], [-1.0, 1.0, 1.0]]))[None]
+    g = np.array([[2.0, 3.0]])
+    x = np.array([[1.0, 10.0, 100.0]])
+    y01, _ = O.gemv_variant(planes, g, None, None, x, 3, True)
+    ypm, _ = O.gemv_variant(planes, g, None, None, x, 3, False)
+    ymu, sabs = O.gemv_variant(planes, g, None, np.array([0.5, -1.0]), x, 3, True)
+    assert y01.tolist() == [[202.0, 330.0]]
+    assert ypm.tolist() == [[182.0, 327.0]]
+    assert ymu.tolist() == [[257.5, 219.0]]
+    assert sabs.tolist() == [[2 * 111 + 0.5 * 111, 3 * 111 + 1 * 111]]
+
+
+def test_gemv_variant_matches_loops_and_the_masked_add_identity():
+    rng = np.random.default_rng(610)
+    k, N, K, M = 2, 5, 37, 3
+    Bpm = np.where(rng.random((k, N, K)) < 0.5, -1.0, 1.0)
+    planes = np.stack([O.pack_bits(Bpm[i]) for i in range(k)])
+    g = rng.uniform(0.1, 1.0, (k, N))
+    h = rng.uniform(-1.0, 2.0, (k, K))
+    mu = rng.standard_normal(N)
+    x = rng.standard_normal((M, K))
+    y01, _ = O.gemv_variant(planes, g, h, mu, x, K, True)
+    ypm, _ = O.gemv_variant(planes, g, h, None, x, K, False)
+    for m in range(M):
+        for n in range(N):
+            acc = mu[n] * sum(x[m, c] for c in range(K))
+            for i in range(k):
+                acc += g[i, n] * sum(h[i, c] * x[m, c] for c in range(K) if Bpm[i, n, c] > 0)
+            assert math.isclose(y01[m, n], acc, rel_tol=1e-12, abs_tol=1e-12)
+    # {0,1} bits = (+-1 bits + 1) / 2: y01 = (ypm + sum_i g_i (h_i . x)) / 2 + mu sum x
+    extra = sum(g[i][None, :] * (x @ h[i])[:, None] for i in range(k))
+    assert np.allclose(y01, (ypm + extra) / 2 + mu[None, :] * x.sum(axis=1)[:, None], rtol=0, atol=1e-12)
+    # with no offset and +-1 bits the variant is the plain product
+    assert np.allclose(ypm, O.gemv(planes, g.reshape(k, N, 1), h, x, K)[0], rtol=0, atol=1e-12)

@@ -259,6 +259,41 @@ def measure_qat_step(torch, np, rb, wl, dev, with_oracle: bool, M: int = 2048) -
     return out
 
 
+def measure_variants(torch, np, rb, wl, dev, with_oracle: bool) -> dict:
+    N, K = N_ROWS, K_COLS
+    Kw = (K + 31) // 32
+    ldp = (Kw + 31) // 32 * 32
+    W = torch.from_numpy(wl.weights_for("down")).to(dev)
+    planes, g = rb.pack(W, 2, ldp=ldp)
+    del W
+    x = torch.from_numpy(wl.activations_for("down", 1)).to(dev)
+    mu = torch.from_numpy(np.random.default_rng([900, 1]).normal(0, 0.002, N).astype(np.float16)).to(dev)
+    ws = rb.workspace(rb.RB_OP_GEMV, 2, N, K, 1, device=dev)
+    y = torch.empty((1, N), dtype=torch.float16, device=dev)
+    out = {}
+    for name, kk, use_mu, zo in (("zero_one_k1", 1, False, True), ("offset_mu_k2", 2, True, False)):
+        copies = [planes[:kk].clone() for _ in range(COPIES)]
+        gk = g[:kk].contiguous()
+        m = mu if use_mu else None
+        us = graph_us(torch, [lambda c=c: rb.gemv_variant(c, gk, None, x, K, mu=m, zero_one=zo, ws=ws, y=y)
+                              for c in copies], 5)
+        byt = algorithmic_bytes(N, K, kk) + (2 * N if use_mu else 0)
+        row = out[name] = roof("hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us, algorithmic_bytes=byt)
+        if with_oracle:
+            from oracle import rb_oracle as O
+            RS = 512
+            pl_s = np.ascontiguousarray(planes[:kk, :RS].cpu().numpy().view(np.uint32)[:, :, :Kw])
+            g_s = g[:kk, :RS].float().cpu().numpy().astype(np.float64)
+            mu_s = mu[:RS].float().cpu().numpy().astype(np.float64) if use_mu else None
+            xh = x.float().cpu().numpy().astype(np.float64)
+            row["cpu_oracle"] = oracle_rate(lambda: O.gemv_variant(pl_s, g_s, None, mu_s, xh, K, zo),
+                                            algorithmic_bytes(RS, K, kk) + (2 * RS if use_mu else 0), 1e9, "GB/s",
+                                            f"first {RS} of the 4096 rows, bytes scaled per row")
+        del copies
+    torch.cuda.synchronize()
+    return {"next_f4_gemv_variants_down_4096x11008_m1": out}
+
+
 def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = True) -> dict:
     """Every step of the path besides the metric product, each on its own workload, timed
     on the GPU against the roofline that bounds it (inputs are seeded synthetic data). With
@@ -314,6 +349,11 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
     # dg, dh); the GEMM kernels are chosen for the shape first (untimed setup); two weight
     # copies rotate so W is read from HBM
     rows.update(measure_qat_step(torch, np, rb, wl, dev, with_oracle))
+
+    # next row: the cheap product variants on the metric's layer and launch shape (M = 1, fp16,
+    # the nibble-table kernel, rotated weight copies): {0, s} bits on one plane, and k = 2 planes
+    # with a per-row offset mu
+    rows.update(measure_variants(torch, np, rb, wl, dev, with_oracle))
 
     # a6: the 28672x8192 layer on the matrix cores at M = 64 and 256, k = 1 and 2, and the
     # M = 1 product on the same weights; 8 weight copies rotate (470 MB > the 256 MB cache)
@@ -424,6 +464,45 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
         rows["a8_codebook_gemv_4096x11008_m1"]["cpu_oracle"] = oracle_rate(
             lambda: O.codebook_gemv(idx_s, Ch, 20, s_s, 16, xch, Kc), RG * per_row + C.numel() * 4 + 2 * Kc,
             1e9, "GB/s", f"first {RG} of the 4096 rows, M=1, index and scale bytes scaled per row")
+    # next row: binary codebook learning on the same sign matrix (v = 20, c = 65536): one M-step
+    # (member counters by integer atomics, then the majority vote), the distinct-block count, and
+    # a whole learning call with one iteration (distinct + E-step + M-step + final E-step)
+    ws_l = torch.empty(rb.lib.rb_codebook_learn_workspace_bytes(C.numel(), 20), dtype=torch.uint8, device=dev)
+    Cl = C.clone()
+
+    def ev_us(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+    ms_us = ev_us(lambda: rb.codebook_mstep(pl[0], Kc, idx, Cl, 20, counts=False, ws=ws_l), 10)
+    ds_us = ev_us(lambda: rb.codebook_distinct(pl[0], Kc, Cl, 20, ws=ws_l), 10)
+    lr_us = ev_us(lambda: rb.codebook_learn(pl[0], Kc, C.clone(), 20, 1, ws=ws_l), 2)
+    words_np = pl[0].cpu().numpy().view(np.uint32)[:, :(Kc + 31) // 32]
+    idx_np = idx.cpu().numpy().view(np.uint16)
+    set_bits = int(np.bitwise_count(np.ascontiguousarray(words_np)).sum())
+    # one per block (member) + one per +1 bit, the last block's padding columns counting as +1
+    atomics = Nc * nb + set_bits + Nc * (nb * 20 - Kc)
+    ms_bytes = pl[0].numel() * 4 + idx.numel() * 2 + 2 * C.numel() * 21 * 4 + 2 * C.numel() * 4
+    rows["next_f3_codebook_learn_4096x11008_v20_c65536"] = {
+        "mstep": roof("hbm", ms_bytes / (ms_us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", ms_us, algorithmic_bytes=ms_bytes,
+                      atomics=atomics, atomic_rate_G_per_s=round(atomics / (ms_us * 1e-6) / 1e9, 2),
+                      note="bound in practice by the L2 atomic adds on the member counters"),
+        "distinct_us": round(ds_us, 2),
+        "learn_1_iteration_us": round(lr_us, 1),
+        "note": "one iteration = distinct + 2 E-steps (the a7 search, twice) + 1 M-step",
+    }
+    if with_oracle:
+        pats = O.sign_blocks(words_np, Kc, 20)
+        Cn = C.cpu().numpy().view(np.uint32)
+        rows["next_f3_codebook_learn_4096x11008_v20_c65536"]["mstep"]["cpu_oracle"] = oracle_rate(
+            lambda: O.codebook_mstep(pats, idx_np, Cn, 20), ms_bytes, 1e9, "GB/s",
+            "the whole M-step (all 2.26 M blocks), bytes as for the GPU")
+    del ws_l, Cl
     del icp, scp
     torch.cuda.synchronize()
     return rows

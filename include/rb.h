@@ -13,6 +13,7 @@
  *           "Method step details" (Algorithm 2) and "Technical novelty".
  *   [BTC]   "亚1比特大模型量化技术突破与实践" (BTC-LLM binary codebook page):
  *           sections 2.1.1, 2.1.2, 3.2.1, 3.2.2, 5.1, 5.2.
+ *   [SigmoidBitLinear] the SigmoidBitLinear blog page ({0, scale_row} weights).
  *
  * Conventions shared by every call
  *   - Matrices are row-major. W is N x K (output x input), y = W x.
@@ -139,6 +140,22 @@ rb_status rb_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void
                   void* stream);
 
 /*
+ * rb_gemv_variant -- rb_gemv for two cheap weight variants:
+ *   zero_one = 1: the plane bits are {0, 1} instead of {-1, +1}, W_hat = sum_i g_i (.) B01_i (.) h_i
+ *     [SigmoidBitLinear blog: a weight binarizes to {0, scale_row}: a set bit keeps the row's
+ *     scale, a clear bit gives 0], so y = sum_i g_i (.) T_i with T_i the masked sum of h_i (.) x
+ *     over the set bits (the +-1 product's 2 T - S without the 2 and the S);
+ *   mu (optional, [N] in scale_dtype): a per-row offset, W_hat += mu 1^T, y += mu (.) sum_k x
+ *     [BTC 2.1.1: zero-mean preprocessing shifts each row by its mean before binarizing].
+ *   zero_one = 0 and mu = NULL is rb_gemv. mu requires h = NULL (else RB_ERR_UNSUPPORTED); zero_one
+ *   must be 0 or 1. Other arguments, limits, workspace and errors as rb_gemv.
+ */
+rb_status rb_gemv_variant(const uint32_t* planes, int64_t ldp, const void* g, const void* h, const void* mu,
+                          int32_t zero_one, rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,
+                          rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
  * rb_gemm_small -- the same product for larger batches, on the matrix cores: the bits
  *   of each plane are expanded to +-h_i fp16 tiles and multiplied with the fp16
  *   activations (fp32 accumulation); y = sum_i g_i (.) acc_i.
@@ -171,6 +188,46 @@ rb_status rb_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, cons
 rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K,
                              const uint32_t* codebook, int32_t c, int32_t v, uint16_t* idx,
                              void* stream);
+
+/*
+ * Binary codebook learning (binary K-means over the v-column sign blocks of one plane).
+ *   [BTC 2.1.1: E-step = nearest codeword in Hamming distance (rb_codebook_encode); M-step =
+ *   each codeword becomes the sign of the sum of its members' +-1 vectors, zeros -> +1; when
+ *   the number M of distinct blocks is below the codebook size c, the size becomes M]
+ * Blocks are cut as in rb_codebook_encode (columns >= K count as +1). Everything is integer:
+ * results are exact and deterministic.
+ *
+ * rb_codebook_learn_workspace_bytes -- workspace of the three calls below for c codewords of
+ *   v bits (the member counters, c (v + 1) uint32, or the 2^v-bit pattern bitmap).
+ */
+size_t rb_codebook_learn_workspace_bytes(int32_t c, int32_t v);
+
+/* rb_codebook_mstep -- one M-step: codeword j = majority vote, bit by bit, of the blocks with
+ *   idx == j (a tie gives 1, i.e. +1); a codeword no block chose keeps its value.
+ *   sign_plane [N][ldp] as in rb_codebook_encode;  v 1..32;  c 1..65536
+ *   idx        [N][ceil(K/v)] uint16, each < c (an entry >= c is skipped)
+ *   codebook   [c] uint32, read and updated in place (low v bits)
+ *   counts     optional output [c] uint32: blocks per codeword (NULL: not written)
+ *   ws         rb_codebook_learn_workspace_bytes(c, v) bytes, 4-byte aligned */
+rb_status rb_codebook_mstep(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K, int32_t v,
+                            const uint16_t* idx, uint32_t* codebook, int32_t c, uint32_t* counts, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* rb_codebook_distinct -- M = the number of distinct blocks, written to *n_distinct (device
+ *   int32). If M < c the codebook becomes the distinct blocks in ascending order, entries M..c-1
+ *   repeating the largest (a repeat never wins a tie, so the effective size is M); otherwise the
+ *   codebook is not touched. v 1..24 (the bitmap of 2^v patterns lives in ws). */
+rb_status rb_codebook_distinct(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K, int32_t v,
+                               uint32_t* codebook, int32_t c, int32_t* n_distinct, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* rb_codebook_learn -- rb_codebook_distinct, then `iters` iterations (0..1000) of E-step
+ *   (rb_codebook_encode) and M-step (rb_codebook_mstep), then a final E-step: codebook holds
+ *   the caller's initial codebook on entry and the learned one on return, idx (output
+ *   [N][ceil(K/v)] uint16) the nearest codeword of every block. v 1..24. */
+rb_status rb_codebook_learn(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K, int32_t v,
+                            uint32_t* codebook, int32_t c, int32_t iters, uint16_t* idx, int32_t* n_distinct,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /*
  * rb_codebook_gemv -- product with codebook-compressed signs and group scales.

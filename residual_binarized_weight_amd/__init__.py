@@ -7,8 +7,10 @@ return CUDA (HIP) tensors on the current device and enqueue on the current strea
   planes, g = pack(W, k)                         residual sign planes + row scales
   y = gemv(planes, g, h, x, K)                   y = sum_i g_i (.) (B_i (h_i (.) x)), M <= 16
   y = gemm_small(planes, g, h, x, K)             same on the matrix cores, larger M
+  y = gemv_variant(planes, g, h, x, K, mu=, zero_one=)   {0, s} planes / per-row offset
   idx = codebook_encode(sign_plane, K, C, v)     nearest binary codeword per v-block
   y = codebook_gemv(idx, C, v, s, group, x, K)   product on codebook indices
+  C, idx, M = codebook_learn(sign_plane, K, C0, v, iters)   binary K-means codebook learning
   planes, g, h = svid_init(W, k)                 function-aware initialization of k paths
   planes, What = qat_derive(W, g, h)             coupled training: paths derived from W
   Y, planes, What = qat_forward(W, g, h, X)      ... and the layer's product Y = X What^T
@@ -25,7 +27,8 @@ from . import _lib
 from ._lib import (RB_F16, RB_F32, RB_BF16, RB_OP_CODEBOOK_GEMV, RB_OP_GEMM_SMALL, RB_OP_GEMV,
                    RB_OP_QAT_BACKWARD, RB_OP_SVID_INIT, RbError, check, lib)
 
-__all__ = ["pack", "gemv", "gemm_small", "codebook_encode", "codebook_gemv", "svid_init", "qat_derive",
+__all__ = ["pack", "gemv", "gemv_variant", "gemm_small", "codebook_encode", "codebook_gemv", "codebook_mstep",
+           "codebook_distinct", "codebook_learn", "svid_init", "qat_derive",
            "qat_forward", "qat_backward", "qat_autotune", "workspace",
            "workspace_bytes", "storage_bits_per_weight", "version", "RbError", "lib"]
 
@@ -123,6 +126,22 @@ def gemv(planes, g, h, x, K: int, y_dtype=torch.float16, ws=None, y=None):
     return _product("rb_gemv", planes, g, h, x, K, y_dtype, ws, y, RB_OP_GEMV)
 
 
+def gemv_variant(planes, g, h, x, K: int, mu=None, zero_one: bool = False, y_dtype=torch.float16, ws=None,
+                 y=None):
+    """rb_gemv with {0, 1} planes (zero_one) and/or a per-row offset mu [N] (scale dtype, h None)."""
+    k, N, ldp = planes.shape
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype, device=x.device)
+    if ws is None:
+        ws = workspace(RB_OP_GEMV, k, N, K, M, device=x.device)
+    check("rb_gemv_variant", lib.rb_gemv_variant(_ptr(planes), ldp, _ptr(g), _ptr(h), _ptr(mu), int(zero_one),
+                                                 _dt(g.dtype), k, N, K, _ptr(x), _dt(x.dtype), M, _ptr(y),
+                                                 _dt(y.dtype), _ptr(ws), 0 if ws is None else ws.numel(),
+                                                 _stream()))
+    return y
+
+
 def gemm_small(planes, g, h, x, K: int, y_dtype=torch.float16, ws=None, y=None):
     """Same product on the matrix cores, for larger batches (x fp16)."""
     return _product("rb_gemm_small", planes, g, h, x, K, y_dtype, ws, y, RB_OP_GEMM_SMALL)
@@ -150,6 +169,53 @@ def codebook_gemv(idx, codebook, v: int, s, group: int, x, K: int, ws=None, y=No
                                                    _ptr(ws), 0 if ws is None else ws.numel(),
                                                    _stream()))
     return y
+
+
+def _learn_ws(c: int, v: int, device, ws):
+    if ws is None:
+        ws = torch.empty(max(4, lib.rb_codebook_learn_workspace_bytes(c, v)), dtype=torch.uint8, device=device)
+    return ws
+
+
+def codebook_mstep(sign_plane: torch.Tensor, K: int, idx: torch.Tensor, codebook: torch.Tensor, v: int,
+                   counts: bool = True, ws: torch.Tensor | None = None):
+    """One M-step of binary K-means, in place on `codebook` ([c] int32 storage of the words);
+    returns the member count per codeword ([c] int32 storage) or None."""
+    N, ldp = sign_plane.shape
+    c = codebook.numel()
+    cnt = torch.empty(c, dtype=torch.int32, device=codebook.device) if counts else None
+    ws = _learn_ws(c, v, codebook.device, ws)
+    check("rb_codebook_mstep", lib.rb_codebook_mstep(_ptr(sign_plane), ldp, N, K, v, _ptr(idx), _ptr(codebook), c,
+                                                     _ptr(cnt), _ptr(ws), ws.numel(), _stream()))
+    return cnt
+
+
+def codebook_distinct(sign_plane: torch.Tensor, K: int, codebook: torch.Tensor, v: int,
+                      ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Number of distinct v-column blocks (a device int32 tensor); if below the codebook size,
+    the codebook (in place) becomes those blocks in ascending order."""
+    N, ldp = sign_plane.shape
+    c = codebook.numel()
+    nd = torch.empty(1, dtype=torch.int32, device=codebook.device)
+    ws = _learn_ws(c, v, codebook.device, ws)
+    check("rb_codebook_distinct", lib.rb_codebook_distinct(_ptr(sign_plane), ldp, N, K, v, _ptr(codebook), c,
+                                                           _ptr(nd), _ptr(ws), ws.numel(), _stream()))
+    return nd
+
+
+def codebook_learn(sign_plane: torch.Tensor, K: int, codebook: torch.Tensor, v: int, iters: int,
+                   idx: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Binary K-means from the initial `codebook` (updated in place): returns (codebook, idx
+    [N][ceil(K/v)] uint16 as int16 storage, number of distinct blocks as a device int32)."""
+    N, ldp = sign_plane.shape
+    c = codebook.numel()
+    nb = (K + v - 1) // v
+    idx = torch.empty((N, nb), dtype=torch.int16, device=codebook.device) if idx is None else idx
+    nd = torch.empty(1, dtype=torch.int32, device=codebook.device)
+    ws = _learn_ws(c, v, codebook.device, ws)
+    check("rb_codebook_learn", lib.rb_codebook_learn(_ptr(sign_plane), ldp, N, K, v, _ptr(codebook), c, iters,
+                                                     _ptr(idx), _ptr(nd), _ptr(ws), ws.numel(), _stream()))
+    return codebook, idx, nd
 
 
 def svid_init(W: torch.Tensor, k: int, T: int = 20, P: int = 4, s_in: torch.Tensor | None = None,

@@ -29,11 +29,17 @@ SIGNATURES = {
                                _vp, _i64, _vp, _vp, _vp]),
     "rb_gemv": (ctypes.c_int, [_vp, _i64, _vp, _vp, ctypes.c_int, _i32, _i64, _i64, _vp, ctypes.c_int,
                                _i64, _vp, ctypes.c_int, _vp, _sz, _vp]),
+    "rb_gemv_variant": (ctypes.c_int, [_vp, _i64, _vp, _vp, _vp, _i32, ctypes.c_int, _i32, _i64, _i64, _vp,
+                                       ctypes.c_int, _i64, _vp, ctypes.c_int, _vp, _sz, _vp]),
     "rb_gemm_small": (ctypes.c_int, [_vp, _i64, _vp, _vp, ctypes.c_int, _i32, _i64, _i64, _vp,
                                      ctypes.c_int, _i64, _vp, ctypes.c_int, _vp, _sz, _vp]),
     "rb_codebook_encode": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _vp]),
     "rb_codebook_gemv": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _i32, _i64, _i64, _vp, _i64, _vp,
                                         _vp, _sz, _vp]),
+    "rb_codebook_learn_workspace_bytes": (_sz, [_i32, _i32]),
+    "rb_codebook_mstep": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "rb_codebook_distinct": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "rb_codebook_learn": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "rb_svid_init": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp,
                                     ctypes.c_float, ctypes.c_float, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "rb_qat_derive": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp, ctypes.c_int,

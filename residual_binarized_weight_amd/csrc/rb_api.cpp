@@ -140,6 +140,24 @@ rb_status rb_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void
                                   ws, static_cast<hipStream_t>(stream)));
 }
 
+rb_status rb_gemv_variant(const uint32_t* planes, int64_t ldp, const void* g, const void* h, const void* mu,
+                          int32_t zero_one, rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,
+                          rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws, size_t ws_bytes,
+                          void* stream) {
+  rb_status st = check_product_args(planes, ldp, g, scale_dtype, k, N, K, x, x_dtype, M, y, y_dtype, 16);
+  if (st != RB_OK) return st;
+  if (zero_one != 0 && zero_one != 1) return RB_ERR_INVALID_ARG;
+  if (mu && h) return RB_ERR_UNSUPPORTED;
+  if (h && !aligned(h, scale_dtype == RB_F32 ? 4 : 2)) return RB_ERR_MISALIGNED;
+  if (mu && !aligned(mu, scale_dtype == RB_F32 ? 4 : 2)) return RB_ERR_MISALIGNED;
+  const size_t need = rb::gemv_workspace_bytes(k, N, K, M);
+  if (need > 0 && (!ws || ws_bytes < need)) return RB_ERR_WORKSPACE;
+  if (ws && !aligned(ws, 16)) return RB_ERR_MISALIGNED;
+  log_call("rb_gemv_variant", N, K, M, k);
+  return from_hip(rb::launch_gemv_variant(planes, ldp, g, h, mu, zero_one, scale_dtype, k, N, K, x, x_dtype, M, y,
+                                          y_dtype, ws, static_cast<hipStream_t>(stream)));
+}
+
 rb_status rb_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                         rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,
                         rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,
@@ -169,6 +187,62 @@ rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N,
   log_call("rb_codebook_encode", N, K, 0, 1);
   return from_hip(rb::launch_codebook_encode(sign_plane, ldp, N, K, codebook, c, v, idx,
                                              static_cast<hipStream_t>(stream)));
+}
+
+size_t rb_codebook_learn_workspace_bytes(int32_t c, int32_t v) {
+  if (c < 1 || c > 65536 || v < 1 || v > 32) return 0;
+  return rb::codebook_learn_workspace_bytes(c, v);
+}
+
+namespace {
+rb_status check_learn_args(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int32_t v, int32_t max_v,
+                           const uint32_t* codebook, int32_t c, void* ws, size_t ws_bytes) {
+  if (!plane || !codebook) return RB_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (ldp < (K + 31) / 32) return RB_ERR_INVALID_ARG;
+  if (c < 1 || c > 65536 || v < 1 || v > max_v) return RB_ERR_INVALID_ARG;
+  if (!aligned(plane, 16) || !aligned(codebook, 4)) return RB_ERR_MISALIGNED;
+  if (!ws || ws_bytes < rb::codebook_learn_workspace_bytes(c, v)) return RB_ERR_WORKSPACE;
+  if (!aligned(ws, 4)) return RB_ERR_MISALIGNED;
+  return RB_OK;
+}
+}  // namespace
+
+rb_status rb_codebook_mstep(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K, int32_t v,
+                            const uint16_t* idx, uint32_t* codebook, int32_t c, uint32_t* counts, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!idx) return RB_ERR_INVALID_ARG;
+  rb_status st = check_learn_args(sign_plane, ldp, N, K, v, 32, codebook, c, ws, ws_bytes);
+  if (st != RB_OK) return st;
+  if (!aligned(idx, 2) || (counts && !aligned(counts, 4))) return RB_ERR_MISALIGNED;
+  log_call("rb_codebook_mstep", N, K, 0, 1);
+  return from_hip(rb::launch_codebook_mstep(sign_plane, ldp, N, K, v, idx, codebook, c, counts, ws,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_codebook_distinct(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K, int32_t v,
+                               uint32_t* codebook, int32_t c, int32_t* n_distinct, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (!n_distinct) return RB_ERR_INVALID_ARG;
+  rb_status st = check_learn_args(sign_plane, ldp, N, K, v, 24, codebook, c, ws, ws_bytes);
+  if (st != RB_OK) return st;
+  if (!aligned(n_distinct, 4)) return RB_ERR_MISALIGNED;
+  log_call("rb_codebook_distinct", N, K, 0, 1);
+  return from_hip(rb::launch_codebook_distinct(sign_plane, ldp, N, K, v, codebook, c, n_distinct, ws,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+rb_status rb_codebook_learn(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K, int32_t v,
+                            uint32_t* codebook, int32_t c, int32_t iters, uint16_t* idx, int32_t* n_distinct,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (!idx || !n_distinct) return RB_ERR_INVALID_ARG;
+  if (iters < 0 || iters > 1000) return RB_ERR_INVALID_ARG;
+  rb_status st = check_learn_args(sign_plane, ldp, N, K, v, 24, codebook, c, ws, ws_bytes);
+  if (st != RB_OK) return st;
+  if (!aligned(idx, 2) || !aligned(n_distinct, 4)) return RB_ERR_MISALIGNED;
+  log_call("rb_codebook_learn", N, K, 0, 1);
+  return from_hip(rb::launch_codebook_learn(sign_plane, ldp, N, K, v, codebook, c, iters, idx, n_distinct, ws,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 rb_status rb_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, int32_t c, int32_t v,

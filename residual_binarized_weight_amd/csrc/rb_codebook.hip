@@ -317,6 +317,115 @@ __global__ __launch_bounds__(kCbThreads) __attribute__((amdgpu_waves_per_eu(1, 4
   if (lane == 63 && n < N) y[n] = __float2half_rn(acc);
 }
 
+// ---------------------------------------------------------------------------------------------
+// binary K-means: M-step and the distinct patterns
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t val) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = val;
+}
+
+// cnt[c][v + 1]: entry t < v counts the members of codeword c whose bit t is 1, entry v counts
+// the members. One thread per pattern; integer atomics, so the totals do not depend on order.
+__global__ __launch_bounds__(256) void mstep_count_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
+                                                          int64_t N, int64_t K, int v,
+                                                          const uint16_t* __restrict__ idx, int c,
+                                                          uint32_t* __restrict__ cnt) {
+  const int64_t nb = (K + v - 1) / v;
+  const int64_t total = N * nb;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const uint32_t id = idx[e];
+    if (id >= (uint32_t)c) continue;  // indices must be < c; any other entry is skipped
+    const int64_t n = e / nb;
+    uint32_t b = extract_block(plane + n * ldp, K, (e - n * nb) * v, v);
+    uint32_t* __restrict__ row = cnt + (int64_t)id * (v + 1);
+    atomicAdd(row + v, 1u);
+    while (b) {
+      atomicAdd(row + __builtin_ctz(b), 1u);
+      b &= b - 1u;
+    }
+  }
+}
+
+// codeword c = the bits t with 2 ones >= members (sum of +-1 >= 0: ties go to +1); a codeword
+// with no member keeps its value. counts (optional) receives the member counts.
+__global__ __launch_bounds__(256) void mstep_vote_kernel(const uint32_t* __restrict__ cnt, int c, int v,
+                                                         uint32_t* __restrict__ codebook,
+                                                         uint32_t* __restrict__ counts) {
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id >= c) return;
+  const uint32_t* __restrict__ row = cnt + (int64_t)id * (v + 1);
+  const uint64_t n = row[v];
+  if (counts) counts[id] = (uint32_t)n;
+  if (n == 0) return;
+  uint32_t w = 0u;
+  for (int t = 0; t < v; ++t) w |= (2ull * row[t] >= n ? 1u : 0u) << t;
+  codebook[id] = w;
+}
+
+// bitmap of the 2^v possible patterns: bit p set when pattern p occurs
+__global__ __launch_bounds__(256) void distinct_mark_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
+                                                            int64_t N, int64_t K, int v,
+                                                            uint32_t* __restrict__ bitmap) {
+  const int64_t nb = (K + v - 1) / v;
+  const int64_t total = N * nb;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t n = e / nb;
+    const uint32_t b = extract_block(plane + n * ldp, K, (e - n * nb) * v, v);
+    atomicOr(bitmap + (b >> 5), 1u << (b & 31u));
+  }
+}
+
+constexpr int kDistinctThreads = 1024;
+
+// One block: M = number of set bits -> *n_distinct. If M < c, the patterns in ascending order
+// go to codebook[0..M) and codebook[M..c) repeats the largest one. Thread t owns a contiguous
+// range of bitmap words; its first output position is the exclusive scan of the ranges' counts.
+__global__ __launch_bounds__(kDistinctThreads) void distinct_compact_kernel(const uint32_t* __restrict__ bitmap,
+                                                                            int64_t nwords, int c,
+                                                                            uint32_t* __restrict__ codebook,
+                                                                            int32_t* __restrict__ n_distinct) {
+  __shared__ uint32_t scan[2][kDistinctThreads];
+  __shared__ int32_t top;
+  const int t = threadIdx.x;
+  const int64_t per = (nwords + kDistinctThreads - 1) / kDistinctThreads;
+  const int64_t lo = (int64_t)t * per < nwords ? (int64_t)t * per : nwords;
+  const int64_t hi = lo + per < nwords ? lo + per : nwords;
+  uint32_t mine = 0u;
+  int32_t last = -1;
+  for (int64_t w = lo; w < hi; ++w) {
+    const uint32_t b = bitmap[w];
+    mine += (uint32_t)__popc(b);
+    if (b) last = (int32_t)(w * 32 + 31 - __builtin_clz(b));
+  }
+  if (t == 0) top = -1;
+  scan[0][t] = mine;
+  __syncthreads();
+  if (last >= 0) atomicMax(&top, last);
+  int src = 0;
+  for (int off = 1; off < kDistinctThreads; off <<= 1) {  // inclusive scan, double-buffered
+    scan[src ^ 1][t] = scan[src][t] + (t >= off ? scan[src][t - off] : 0u);
+    src ^= 1;
+    __syncthreads();
+  }
+  const uint32_t total = scan[src][kDistinctThreads - 1];
+  if (t == 0) *n_distinct = (int32_t)total;
+  if (total >= (uint32_t)c) return;
+  uint32_t pos = scan[src][t] - mine;
+  for (int64_t w = lo; w < hi; ++w) {
+    uint32_t b = bitmap[w];
+    while (b) {
+      codebook[pos++] = (uint32_t)(w * 32) + (uint32_t)__builtin_ctz(b);
+      b &= b - 1u;
+    }
+  }
+  for (int64_t i = (int64_t)total + t; i < c; i += kDistinctThreads) codebook[i] = (uint32_t)top;
+}
+
+unsigned stride_grid(int64_t items) {
+  const int64_t b = (items + 255) / 256;
+  return (unsigned)(b < 1 ? 1 : b > (1 << 20) ? (1 << 20) : b);
+}
+
 }  // namespace
 
 hipError_t launch_codebook_encode(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K,
@@ -367,6 +476,47 @@ hipError_t launch_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, i
                                              N, K, static_cast<const __half*>(x), M,
                                              static_cast<__half*>(y));
   return hipGetLastError();
+}
+
+size_t codebook_learn_workspace_bytes(int c, int v) {
+  const size_t counters = (size_t)c * (size_t)(v + 1) * 4u;
+  const size_t bitmap = v <= 24 ? ((size_t)1 << (v > 5 ? v - 3 : 2)) : 0u;
+  return counters > bitmap ? counters : bitmap;
+}
+
+hipError_t launch_codebook_mstep(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
+                                 const uint16_t* idx, uint32_t* codebook, int c, uint32_t* counts, void* ws,
+                                 hipStream_t s) {
+  uint32_t* cnt = static_cast<uint32_t*>(ws);
+  const int64_t ncnt = (int64_t)c * (v + 1);
+  fill_u32_kernel<<<stride_grid(ncnt), 256, 0, s>>>(cnt, ncnt, 0u);
+  const int64_t total = N * ((K + v - 1) / v);
+  mstep_count_kernel<<<stride_grid(total), 256, 0, s>>>(plane, ldp, N, K, v, idx, c, cnt);
+  mstep_vote_kernel<<<(unsigned)((c + 255) / 256), 256, 0, s>>>(cnt, c, v, codebook, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_codebook_distinct(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
+                                    uint32_t* codebook, int c, int32_t* n_distinct, void* ws, hipStream_t s) {
+  uint32_t* bitmap = static_cast<uint32_t*>(ws);
+  const int64_t nwords = v > 5 ? (int64_t)1 << (v - 5) : 1;
+  fill_u32_kernel<<<stride_grid(nwords), 256, 0, s>>>(bitmap, nwords, 0u);
+  const int64_t total = N * ((K + v - 1) / v);
+  distinct_mark_kernel<<<stride_grid(total), 256, 0, s>>>(plane, ldp, N, K, v, bitmap);
+  distinct_compact_kernel<<<1, kDistinctThreads, 0, s>>>(bitmap, nwords, c, codebook, n_distinct);
+  return hipGetLastError();
+}
+
+hipError_t launch_codebook_learn(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
+                                 uint32_t* codebook, int c, int iters, uint16_t* idx, int32_t* n_distinct,
+                                 void* ws, hipStream_t s) {
+  hipError_t e = launch_codebook_distinct(plane, ldp, N, K, v, codebook, c, n_distinct, ws, s);
+  for (int it = 0; it < iters && e == hipSuccess; ++it) {
+    e = launch_codebook_encode(plane, ldp, N, K, codebook, c, v, idx, s);
+    if (e == hipSuccess) e = launch_codebook_mstep(plane, ldp, N, K, v, idx, codebook, c, nullptr, ws, s);
+  }
+  if (e == hipSuccess) e = launch_codebook_encode(plane, ldp, N, K, codebook, c, v, idx, s);
+  return e;
 }
 
 }  // namespace rb

@@ -34,7 +34,7 @@ template <typename TX, typename TS, typename TY, int MB>
 __global__ __launch_bounds__(256) void gemv_direct_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g,
     const TS* __restrict__ h, int k, int64_t N, int64_t K, const TX* __restrict__ x, int64_t M,
-    TY* __restrict__ y) {
+    TY* __restrict__ y, const TS* __restrict__ mu, int zero_one) {
   __shared__ __align__(16) float xs[MB][(kChunkCols / 32) * kSegStride];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -111,7 +111,9 @@ __global__ __launch_bounds__(256) void gemv_direct_kernel(
         const float T = wave_sum(Tacc[r][m]);
         const int64_t row = row0 + r;
         const float gi = row < N ? to_f32(g[(int64_t)i * N + row]) : 0.0f;
-        yacc[r][m] += gi * (2.0f * T - S);
+        // a +-1 plane contributes 2 T - S, a {0, 1} plane T; a row offset mu adds mu S (h = 1)
+        yacc[r][m] += gi * (zero_one ? T : 2.0f * T - S);
+        if (i == 0 && mu && row < N) yacc[r][m] += to_f32(mu[row]) * S;
       }
     }
   }
@@ -499,17 +501,18 @@ hipError_t launch_lut(const uint32_t* planes, int64_t ldp, const void* g, int k,
 
 template <typename TX, typename TS, typename TY>
 hipError_t launch_direct(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k,
-                         int64_t N, int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
+                         int64_t N, int64_t K, const void* x, int64_t M, void* y, const void* mu, int zero_one,
+                         hipStream_t s) {
   const int64_t rows_per_block = (int64_t)kRowsPerWave * kWavesPerBlock;
   const unsigned gx = (unsigned)((N + rows_per_block - 1) / rows_per_block);
   if (M == 1) {
     gemv_direct_kernel<TX, TS, TY, 1><<<dim3(gx, 1), dim3(256), 0, s>>>(
         planes, ldp, static_cast<const TS*>(g), static_cast<const TS*>(h), k, N, K,
-        static_cast<const TX*>(x), M, static_cast<TY*>(y));
+        static_cast<const TX*>(x), M, static_cast<TY*>(y), static_cast<const TS*>(mu), zero_one);
   } else {
     gemv_direct_kernel<TX, TS, TY, 4><<<dim3(gx, (unsigned)((M + 3) / 4)), dim3(256), 0, s>>>(
         planes, ldp, static_cast<const TS*>(g), static_cast<const TS*>(h), k, N, K,
-        static_cast<const TX*>(x), M, static_cast<TY*>(y));
+        static_cast<const TX*>(x), M, static_cast<TY*>(y), static_cast<const TS*>(mu), zero_one);
   }
   return hipGetLastError();
 }
@@ -517,21 +520,22 @@ hipError_t launch_direct(const uint32_t* planes, int64_t ldp, const void* g, con
 template <typename TX, typename TS>
 hipError_t launch_y(rb_dtype y_dtype, const uint32_t* planes, int64_t ldp, const void* g,
                     const void* h, int k, int64_t N, int64_t K, const void* x, int64_t M, void* y,
-                    void* ws, hipStream_t s) {
-  if (M == 1 && h == nullptr && lut_fits(k, N, K, ldp, sizeof(TX), sizeof(TS))) {
+                    void* ws, const void* mu, int zero_one, hipStream_t s) {
+  if (M == 1 && h == nullptr && mu == nullptr && !zero_one && lut_fits(k, N, K, ldp, sizeof(TX), sizeof(TS))) {
     if (y_dtype == RB_F16) return launch_lut<TX, TS, __half>(planes, ldp, g, k, N, K, x, y, ws, s);
     return launch_lut<TX, TS, float>(planes, ldp, g, k, N, K, x, y, ws, s);
   }
-  if (y_dtype == RB_F16) return launch_direct<TX, TS, __half>(planes, ldp, g, h, k, N, K, x, M, y, s);
-  return launch_direct<TX, TS, float>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if (y_dtype == RB_F16) return launch_direct<TX, TS, __half>(planes, ldp, g, h, k, N, K, x, M, y, mu, zero_one, s);
+  return launch_direct<TX, TS, float>(planes, ldp, g, h, k, N, K, x, M, y, mu, zero_one, s);
 }
 
 template <typename TX>
 hipError_t launch_s(rb_dtype scale_dtype, rb_dtype y_dtype, const uint32_t* planes, int64_t ldp,
                     const void* g, const void* h, int k, int64_t N, int64_t K, const void* x,
-                    int64_t M, void* y, void* ws, hipStream_t s) {
-  if (scale_dtype == RB_F16) return launch_y<TX, __half>(y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, s);
-  return launch_y<TX, float>(y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+                    int64_t M, void* y, void* ws, const void* mu, int zero_one, hipStream_t s) {
+  if (scale_dtype == RB_F16)
+    return launch_y<TX, __half>(y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, mu, zero_one, s);
+  return launch_y<TX, float>(y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, mu, zero_one, s);
 }
 
 }  // namespace
@@ -553,18 +557,26 @@ int device_cu_count() {
 // for it whatever M is, so one workspace serves every batch size of a layer.
 size_t gemv_workspace_bytes(int, int64_t N, int64_t K, int64_t) { return lut_workspace_bytes(N, K); }
 
-hipError_t launch_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
-                       rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x,
-                       rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws, hipStream_t s) {
+hipError_t launch_gemv_variant(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                               const void* mu, int zero_one, rb_dtype scale_dtype, int k, int64_t N, int64_t K,
+                               const void* x, rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,
+                               hipStream_t s) {
   // one activation row, h = 1: the whole-row nibble-table kernel where it applies (fp16
-  // data, k <= 2), else the byte-table kernel below
+  // data, k <= 2), else the byte-table kernel (plain product only) or the direct kernel
   if (M == 1 && h == nullptr && gemv_nib_fits(k, N, K, ldp, x_dtype, scale_dtype, y_dtype)) {
-    const hipError_t e = launch_gemv_nib(planes, ldp, g, scale_dtype, k, N, K, x, x_dtype, y, y_dtype, s);
+    const hipError_t e =
+        launch_gemv_nib(planes, ldp, g, scale_dtype, k, N, K, x, x_dtype, y, y_dtype, mu, zero_one, s);
     if (e != hipErrorNotSupported) return e;
   }
   if (x_dtype == RB_F16)
-    return launch_s<__half>(scale_dtype, y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, s);
-  return launch_s<float>(scale_dtype, y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+    return launch_s<__half>(scale_dtype, y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, mu, zero_one, s);
+  return launch_s<float>(scale_dtype, y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, mu, zero_one, s);
+}
+
+hipError_t launch_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                       rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x,
+                       rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws, hipStream_t s) {
+  return launch_gemv_variant(planes, ldp, g, h, nullptr, 0, scale_dtype, k, N, K, x, x_dtype, M, y, y_dtype, ws, s);
 }
 
 }  // namespace rb

@@ -67,10 +67,12 @@ constexpr int kNibSH = 12;                      // entry row = 4 KB
 constexpr uint32_t kNibBuf = 65536u;
 
 // WV waves per block, RW rows per wave (row r of wave w of block b: (b * WV + w) * RW + r)
-template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV>
+// VAR: the product variants (a {0, 1} reading of the bits, a row offset); the plain product is
+// compiled without them.
+template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV, bool VAR>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, int64_t N, int64_t K,
-    const TX* __restrict__ x, TY* __restrict__ y) {
+    const TX* __restrict__ x, TY* __restrict__ y, const TS* __restrict__ mu, int zero_one) {
   extern __shared__ __align__(16) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds + (NPH == 1 ? 1 : 2) * kNibBuf);  // after the table buffers
   const int tid = threadIdx.x;
@@ -132,6 +134,13 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
     for (int i = 0; i < KP; ++i)
       gr[r][i] = NibScale<TS>::load(rg, (uint32_t)(n0 + r) * (uint32_t)sizeof(TS),
                                     (uint32_t)i * (uint32_t)N * (uint32_t)sizeof(TS));
+  // the row offsets (if any) are loaded with the scales, well before the epilogue needs them
+  uint32_t mr[RW];
+  if constexpr (VAR) {
+    const __amdgpu_buffer_rsrc_t rmu = buffer_rsrc(mu, mu ? (uint32_t)N * (uint32_t)sizeof(TS) : 0u);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) mr[r] = NibScale<TS>::load(rmu, (uint32_t)(n0 + r) * (uint32_t)sizeof(TS), 0u);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // Lookup addresses by byte splicing. Lane l's slot offset 32 l + 4 (i ^ a(l)) is
@@ -244,34 +253,43 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
     }
   }
 
-  // 5. row sums; sum x over the block, read in the same order by every wave
+  // 5. row sums; sum x over the block, read in the same order by every wave. A +-1 plane
+  // contributes 2 T - S, a {0, 1} plane T; a row offset mu adds mu S.
   float S = 0.0f;
 #pragma unroll
   for (int w = 0; w < WV; ++w) S += red[w];
+  const float ta = VAR && zero_one ? 1.0f : 2.0f;
+  const float ts = VAR && zero_one ? 0.0f : S;
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     float v = 0.0f;
 #pragma unroll
-    for (int i = 0; i < KP; ++i) v += NibScale<TS>::f32(gr[r][i]) * (2.0f * wave_sum_dpp(acc[r][i]) - S);
-    if (lane == 63 && n0 + r < N) nib_store<TY>(&y[n0 + r], v);
+    for (int i = 0; i < KP; ++i) v += NibScale<TS>::f32(gr[r][i]) * (ta * wave_sum_dpp(acc[r][i]) - ts);
+    if (lane == 63 && n0 + r < N) {
+      if constexpr (VAR) {
+        if (mu) v += NibScale<TS>::f32(mr[r]) * S;
+      }
+      nib_store<TY>(&y[n0 + r], v);
+    }
   }
 }
 
-template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV = kNibWaves>
+template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, bool VAR, int WV = kNibWaves>
 hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
-                            const void* x, void* y, hipStream_t s) {
+                            const void* x, void* y, const void* mu, int zero_one, hipStream_t s) {
   // one phase needs one table buffer (two blocks fit on a compute unit), more need two
   constexpr size_t lds = (NPH == 1 ? 1 : 2) * (size_t)kNibBuf + 64;
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib_kernel<TX, TS, TY, KP, NPH, RW, WV>,
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib_kernel<TX, TS, TY, KP, NPH, RW, WV, VAR>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const unsigned grid = (unsigned)((N + WV * RW - 1) / (WV * RW));
-  gemv_nib_kernel<TX, TS, TY, KP, NPH, RW, WV><<<grid, 64 * WV, lds, s>>>(
-      planes, ldp, static_cast<const TS*>(g), N, K, static_cast<const TX*>(x), static_cast<TY*>(y));
+  gemv_nib_kernel<TX, TS, TY, KP, NPH, RW, WV, VAR><<<grid, 64 * WV, lds, s>>>(
+      planes, ldp, static_cast<const TS*>(g), N, K, static_cast<const TX*>(x), static_cast<TY*>(y),
+      static_cast<const TS*>(mu), zero_one);
   return hipGetLastError();
 }
 
@@ -280,23 +298,23 @@ hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, 
 // 16 waves per block (larger counts spill)
 constexpr int nib_max_rows(int kp, int nph) { return kp == 1 ? (nph <= 3 ? 3 : 2) : (nph == 1 ? 3 : nph <= 3 ? 2 : 1); }
 
-template <typename TX, typename TS, typename TY, int KP, int NPH>
+template <typename TX, typename TS, typename TY, int KP, int NPH, bool VAR>
 hipError_t launch_nib_rows(int rw, const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
-                           const void* x, void* y, hipStream_t s) {
+                           const void* x, void* y, const void* mu, int zero_one, hipStream_t s) {
   constexpr int kMax = nib_max_rows(KP, NPH);
   if (rw > kMax) rw = kMax;
   if constexpr (kMax >= 3) {
-    if (rw == 3) return launch_nib_shape<TX, TS, TY, KP, NPH, 3>(planes, ldp, g, N, K, x, y, s);
+    if (rw == 3) return launch_nib_shape<TX, TS, TY, KP, NPH, 3, VAR>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
   }
   if constexpr (kMax >= 2) {
-    if (rw == 2) return launch_nib_shape<TX, TS, TY, KP, NPH, 2>(planes, ldp, g, N, K, x, y, s);
+    if (rw == 2) return launch_nib_shape<TX, TS, TY, KP, NPH, 2, VAR>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
   }
-  return launch_nib_shape<TX, TS, TY, KP, NPH, 1>(planes, ldp, g, N, K, x, y, s);
+  return launch_nib_shape<TX, TS, TY, KP, NPH, 1, VAR>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
 }
 
-template <typename TX, typename TS, typename TY, int KP>
+template <typename TX, typename TS, typename TY, int KP, bool VAR>
 hipError_t launch_nib_kp(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
-                         const void* x, void* y, hipStream_t s) {
+                         const void* x, void* y, const void* mu, int zero_one, hipStream_t s) {
   const int64_t phases = ((K + 31) / 32 + kNibPhaseWords - 1) / kNibPhaseWords;
   const int64_t cus = device_cu_count();
   int rw = 3;
@@ -306,10 +324,10 @@ hipError_t launch_nib_kp(const uint32_t* planes, int64_t ldp, const void* g, int
       break;
     }
   switch (phases) {
-    case 1: return launch_nib_rows<TX, TS, TY, KP, 1>(rw, planes, ldp, g, N, K, x, y, s);
-    case 2: return launch_nib_rows<TX, TS, TY, KP, 2>(rw, planes, ldp, g, N, K, x, y, s);
-    case 3: return launch_nib_rows<TX, TS, TY, KP, 3>(rw, planes, ldp, g, N, K, x, y, s);
-    default: return launch_nib_rows<TX, TS, TY, KP, 4>(rw, planes, ldp, g, N, K, x, y, s);
+    case 1: return launch_nib_rows<TX, TS, TY, KP, 1, VAR>(rw, planes, ldp, g, N, K, x, y, mu, zero_one, s);
+    case 2: return launch_nib_rows<TX, TS, TY, KP, 2, VAR>(rw, planes, ldp, g, N, K, x, y, mu, zero_one, s);
+    case 3: return launch_nib_rows<TX, TS, TY, KP, 3, VAR>(rw, planes, ldp, g, N, K, x, y, mu, zero_one, s);
+    default: return launch_nib_rows<TX, TS, TY, KP, 4, VAR>(rw, planes, ldp, g, N, K, x, y, mu, zero_one, s);
   }
 }
 
@@ -325,11 +343,15 @@ bool gemv_nib_fits(int k, int64_t N, int64_t K, int64_t ldp, rb_dtype x_dtype, r
 
 hipError_t launch_gemv_nib(const uint32_t* planes, int64_t ldp, const void* g, rb_dtype scale_dtype, int k,
                            int64_t N, int64_t K, const void* x, rb_dtype x_dtype, void* y, rb_dtype y_dtype,
-                           hipStream_t s) {
+                           const void* mu, int zero_one, hipStream_t s) {
   if (x_dtype != RB_F16 || scale_dtype != RB_F16 || y_dtype != RB_F16) return hipErrorNotSupported;
   switch (k) {
-    case 1: return launch_nib_kp<__half, __half, __half, 1>(planes, ldp, g, N, K, x, y, s);
-    case 2: return launch_nib_kp<__half, __half, __half, 2>(planes, ldp, g, N, K, x, y, s);
+    case 1:
+      if (mu || zero_one) return launch_nib_kp<__half, __half, __half, 1, true>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
+      return launch_nib_kp<__half, __half, __half, 1, false>(planes, ldp, g, N, K, x, y, nullptr, 0, s);
+    case 2:
+      if (mu || zero_one) return launch_nib_kp<__half, __half, __half, 2, true>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
+      return launch_nib_kp<__half, __half, __half, 2, false>(planes, ldp, g, N, K, x, y, nullptr, 0, s);
     default: return hipErrorNotSupported;
   }
 }

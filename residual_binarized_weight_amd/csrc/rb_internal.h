@@ -27,7 +27,12 @@ bool gemv_nib_fits(int k, int64_t N, int64_t K, int64_t ldp, rb_dtype x_dtype, r
                    rb_dtype y_dtype);
 hipError_t launch_gemv_nib(const uint32_t* planes, int64_t ldp, const void* g, rb_dtype scale_dtype, int k,
                            int64_t N, int64_t K, const void* x, rb_dtype x_dtype, void* y, rb_dtype y_dtype,
-                           hipStream_t s);
+                           const void* mu, int zero_one, hipStream_t s);
+// the product with {0, 1} planes (zero_one) and/or a per-row offset mu (h must be NULL with mu)
+hipError_t launch_gemv_variant(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                               const void* mu, int zero_one, rb_dtype scale_dtype, int k, int64_t N, int64_t K,
+                               const void* x, rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,
+                               hipStream_t s);
 
 // small GEMM on the matrix cores
 size_t gemm_small_workspace_bytes(int k, int64_t N, int64_t K, int64_t M);
@@ -40,6 +45,15 @@ hipError_t launch_codebook_encode(const uint32_t* plane, int64_t ldp, int64_t N,
                                   const uint32_t* codebook, int c, int v, uint16_t* idx,
                                   hipStream_t s);
 size_t codebook_gemv_workspace_bytes(int64_t N, int64_t K, int64_t M);
+size_t codebook_learn_workspace_bytes(int c, int v);
+hipError_t launch_codebook_mstep(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
+                                 const uint16_t* idx, uint32_t* codebook, int c, uint32_t* counts, void* ws,
+                                 hipStream_t s);
+hipError_t launch_codebook_distinct(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
+                                    uint32_t* codebook, int c, int32_t* n_distinct, void* ws, hipStream_t s);
+hipError_t launch_codebook_learn(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
+                                 uint32_t* codebook, int c, int iters, uint16_t* idx, int32_t* n_distinct,
+                                 void* ws, hipStream_t s);
 hipError_t launch_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, int c, int v,
                                 const void* s, int group, int64_t N, int64_t K, const void* x,
                                 int64_t M, void* y, void* ws, hipStream_t st);

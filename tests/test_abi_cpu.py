@@ -361,3 +361,97 @@ def _qat_autotune(**kw):
 ])
 def test_qat_autotune_rejects(kw, status):
     assert _qat_autotune(**kw) == status
+
+
+def test_codebook_learn_workspace_bytes():
+    assert L.rb_codebook_learn_workspace_bytes(65536, 20) == 65536 * 21 * 4
+    assert L.rb_codebook_learn_workspace_bytes(16, 24) == 1 << 21          # the 2^24-bit bitmap
+    assert L.rb_codebook_learn_workspace_bytes(0, 20) == 0
+    assert L.rb_codebook_learn_workspace_bytes(16, 33) == 0
+
+
+def _cb_learn(fn, **kw):
+    a = dict(plane=P, ldp=32, N=16, K=1000, v=20, idx=P, C=P, c=256, counts=None, nd=P, iters=2, ws=P,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    if fn == "mstep":
+        return L.rb_codebook_mstep(a["plane"], a["ldp"], a["N"], a["K"], a["v"], a["idx"], a["C"], a["c"],
+                                   a["counts"], a["ws"], a["wsb"], a["stream"])
+    if fn == "distinct":
+        return L.rb_codebook_distinct(a["plane"], a["ldp"], a["N"], a["K"], a["v"], a["C"], a["c"], a["nd"],
+                                      a["ws"], a["wsb"], a["stream"])
+    return L.rb_codebook_learn(a["plane"], a["ldp"], a["N"], a["K"], a["v"], a["C"], a["c"], a["iters"], a["idx"],
+                               a["nd"], a["ws"], a["wsb"], a["stream"])
+
+
+_CB_COMMON = [
+    (dict(plane=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(C=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(N=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(K=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldp=31), _lib.RB_ERR_INVALID_ARG),
+    (dict(c=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(c=65537), _lib.RB_ERR_INVALID_ARG),
+    (dict(v=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(plane=P_MIS), _lib.RB_ERR_MISALIGNED),
+    (dict(C=P2), _lib.RB_ERR_MISALIGNED),
+    (dict(ws=None), _lib.RB_ERR_WORKSPACE),
+    (dict(wsb=256 * 21 * 4 - 1), _lib.RB_ERR_WORKSPACE),
+    (dict(ws=P2), _lib.RB_ERR_MISALIGNED),
+]
+
+
+@pytest.mark.parametrize("kw,status", _CB_COMMON + [
+    (dict(idx=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(v=33), _lib.RB_ERR_INVALID_ARG),
+    (dict(idx=P_ODD), _lib.RB_ERR_MISALIGNED),
+    (dict(counts=P2), _lib.RB_ERR_MISALIGNED),
+])
+def test_codebook_mstep_rejects(kw, status):
+    assert _cb_learn("mstep", **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", _CB_COMMON + [
+    (dict(nd=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(v=25), _lib.RB_ERR_INVALID_ARG),
+    (dict(nd=P2), _lib.RB_ERR_MISALIGNED),
+])
+def test_codebook_distinct_rejects(kw, status):
+    assert _cb_learn("distinct", **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", _CB_COMMON + [
+    (dict(idx=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(nd=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(iters=-1), _lib.RB_ERR_INVALID_ARG),
+    (dict(iters=1001), _lib.RB_ERR_INVALID_ARG),
+    (dict(v=25), _lib.RB_ERR_INVALID_ARG),
+    (dict(idx=P_ODD), _lib.RB_ERR_MISALIGNED),
+])
+def test_codebook_learn_rejects(kw, status):
+    assert _cb_learn("learn", **kw) == status
+
+
+def _gemv_variant(**kw):
+    a = dict(planes=P, ldp=2, g=P, h=None, mu=P, zo=0, sdt=_lib.RB_F16, k=2, N=16, K=64, x=P, xdt=_lib.RB_F16, M=1,
+             y=P, ydt=_lib.RB_F16, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.rb_gemv_variant(a["planes"], a["ldp"], a["g"], a["h"], a["mu"], a["zo"], a["sdt"], a["k"], a["N"],
+                             a["K"], a["x"], a["xdt"], a["M"], a["y"], a["ydt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(planes=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(g=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(zo=2), _lib.RB_ERR_INVALID_ARG),
+    (dict(zo=-1), _lib.RB_ERR_INVALID_ARG),
+    (dict(k=5), _lib.RB_ERR_INVALID_ARG),
+    (dict(M=17), _lib.RB_ERR_UNSUPPORTED),
+    (dict(h=P), _lib.RB_ERR_UNSUPPORTED),                  # an offset needs h = 1
+    (dict(mu=P_ODD), _lib.RB_ERR_MISALIGNED),
+    (dict(mu=P2, sdt=_lib.RB_F32), _lib.RB_ERR_MISALIGNED),
+    (dict(h=P_ODD, mu=None), _lib.RB_ERR_MISALIGNED),
+    (dict(x=P_MIS), _lib.RB_ERR_MISALIGNED),
+])
+def test_gemv_variant_rejects(kw, status):
+    assert _gemv_variant(**kw) == status

@@ -197,10 +197,13 @@ rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N,
  * Blocks are cut as in rb_codebook_encode (columns >= K count as +1). Everything is integer:
  * results are exact and deterministic.
  *
- * rb_codebook_learn_workspace_bytes -- workspace of the three calls below for c codewords of
- *   v bits (the member counters, c (v + 1) uint32, or the 2^v-bit pattern bitmap).
+ * rb_codebook_learn_workspace_bytes -- workspace of the three calls below for an N x K plane
+ *   and c codewords of v bits: the M-step's per-codeword counters and cursors (3 c uint32) and
+ *   one uint32 per block (the blocks sorted by codeword), or the 2^v-bit pattern bitmap of
+ *   rb_codebook_distinct, whichever is larger (0 for invalid sizes). N ceil(K/v) must be below
+ *   2^32 (else RB_ERR_UNSUPPORTED).
  */
-size_t rb_codebook_learn_workspace_bytes(int32_t c, int32_t v);
+size_t rb_codebook_learn_workspace_bytes(int64_t N, int64_t K, int32_t c, int32_t v);
 
 /* rb_codebook_mstep -- one M-step: codeword j = majority vote, bit by bit, of the blocks with
  *   idx == j (a tie gives 1, i.e. +1); a codeword no block chose keeps its value.
@@ -208,7 +211,7 @@ size_t rb_codebook_learn_workspace_bytes(int32_t c, int32_t v);
  *   idx        [N][ceil(K/v)] uint16, each < c (an entry >= c is skipped)
  *   codebook   [c] uint32, read and updated in place (low v bits)
  *   counts     optional output [c] uint32: blocks per codeword (NULL: not written)
- *   ws         rb_codebook_learn_workspace_bytes(c, v) bytes, 4-byte aligned */
+ *   ws         rb_codebook_learn_workspace_bytes(N, K, c, v) bytes, 4-byte aligned */
 rb_status rb_codebook_mstep(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K, int32_t v,
                             const uint16_t* idx, uint32_t* codebook, int32_t c, uint32_t* counts, void* ws,
                             size_t ws_bytes, void* stream);

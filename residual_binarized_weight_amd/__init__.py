@@ -171,9 +171,9 @@ def codebook_gemv(idx, codebook, v: int, s, group: int, x, K: int, ws=None, y=No
     return y
 
 
-def _learn_ws(c: int, v: int, device, ws):
+def _learn_ws(N: int, K: int, c: int, v: int, device, ws):
     if ws is None:
-        ws = torch.empty(max(4, lib.rb_codebook_learn_workspace_bytes(c, v)), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(4, lib.rb_codebook_learn_workspace_bytes(N, K, c, v)), dtype=torch.uint8, device=device)
     return ws
 
 
@@ -184,7 +184,7 @@ def codebook_mstep(sign_plane: torch.Tensor, K: int, idx: torch.Tensor, codebook
     N, ldp = sign_plane.shape
     c = codebook.numel()
     cnt = torch.empty(c, dtype=torch.int32, device=codebook.device) if counts else None
-    ws = _learn_ws(c, v, codebook.device, ws)
+    ws = _learn_ws(N, K, c, v, codebook.device, ws)
     check("rb_codebook_mstep", lib.rb_codebook_mstep(_ptr(sign_plane), ldp, N, K, v, _ptr(idx), _ptr(codebook), c,
                                                      _ptr(cnt), _ptr(ws), ws.numel(), _stream()))
     return cnt
@@ -197,7 +197,7 @@ def codebook_distinct(sign_plane: torch.Tensor, K: int, codebook: torch.Tensor, 
     N, ldp = sign_plane.shape
     c = codebook.numel()
     nd = torch.empty(1, dtype=torch.int32, device=codebook.device)
-    ws = _learn_ws(c, v, codebook.device, ws)
+    ws = _learn_ws(N, K, c, v, codebook.device, ws)
     check("rb_codebook_distinct", lib.rb_codebook_distinct(_ptr(sign_plane), ldp, N, K, v, _ptr(codebook), c,
                                                            _ptr(nd), _ptr(ws), ws.numel(), _stream()))
     return nd
@@ -212,7 +212,7 @@ def codebook_learn(sign_plane: torch.Tensor, K: int, codebook: torch.Tensor, v: 
     nb = (K + v - 1) // v
     idx = torch.empty((N, nb), dtype=torch.int16, device=codebook.device) if idx is None else idx
     nd = torch.empty(1, dtype=torch.int32, device=codebook.device)
-    ws = _learn_ws(c, v, codebook.device, ws)
+    ws = _learn_ws(N, K, c, v, codebook.device, ws)
     check("rb_codebook_learn", lib.rb_codebook_learn(_ptr(sign_plane), ldp, N, K, v, _ptr(codebook), c, iters,
                                                      _ptr(idx), _ptr(nd), _ptr(ws), ws.numel(), _stream()))
     return codebook, idx, nd

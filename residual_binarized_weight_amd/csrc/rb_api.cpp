@@ -189,9 +189,9 @@ rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N,
                                              static_cast<hipStream_t>(stream)));
 }
 
-size_t rb_codebook_learn_workspace_bytes(int32_t c, int32_t v) {
-  if (c < 1 || c > 65536 || v < 1 || v > 32) return 0;
-  return rb::codebook_learn_workspace_bytes(c, v);
+size_t rb_codebook_learn_workspace_bytes(int64_t N, int64_t K, int32_t c, int32_t v) {
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim || c < 1 || c > 65536 || v < 1 || v > 32) return 0;
+  return rb::codebook_learn_workspace_bytes(N, K, c, v);
 }
 
 namespace {
@@ -202,7 +202,8 @@ rb_status check_learn_args(const uint32_t* plane, int64_t ldp, int64_t N, int64_
   if (ldp < (K + 31) / 32) return RB_ERR_INVALID_ARG;
   if (c < 1 || c > 65536 || v < 1 || v > max_v) return RB_ERR_INVALID_ARG;
   if (!aligned(plane, 16) || !aligned(codebook, 4)) return RB_ERR_MISALIGNED;
-  if (!ws || ws_bytes < rb::codebook_learn_workspace_bytes(c, v)) return RB_ERR_WORKSPACE;
+  if (N * ((K + v - 1) / v) > 0xffffffffll) return RB_ERR_UNSUPPORTED;  // 32-bit bucket positions
+  if (!ws || ws_bytes < rb::codebook_learn_workspace_bytes(N, K, c, v)) return RB_ERR_WORKSPACE;
   if (!aligned(ws, 4)) return RB_ERR_MISALIGNED;
   return RB_OK;
 }

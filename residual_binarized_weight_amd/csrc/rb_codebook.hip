@@ -32,11 +32,14 @@ constexpr int kPatternsPerThread = 4;
 // Each thread keeps kPatternsPerThread patterns; the block streams the codebook through
 // LDS and every thread scores all staged codewords against its patterns. The running
 // best is the packed key (distance << 16 | index), whose unsigned minimum is the nearest
-// codeword with ties to the lowest index.
+// codeword with ties to the lowest index. With cnt (the E-step of the learning loop), each
+// block is also counted for the M-step: cnt[j][v] += 1 and cnt[j][t] += bit t for its
+// codeword j (integer atomics, spread over this long, ALU-bound kernel).
 __global__ __launch_bounds__(256) void encode_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
                                                      int64_t N, int64_t K,
                                                      const uint32_t* __restrict__ codebook, int c,
-                                                     int v, uint16_t* __restrict__ idx) {
+                                                     int v, uint16_t* __restrict__ idx,
+                                                     uint32_t* __restrict__ cnt) {
   __shared__ uint32_t cb[kEncodeTile];
   const int64_t nb = (K + v - 1) / v;
   const int64_t total = N * nb;
@@ -73,6 +76,16 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint32_t* __restrict_
   for (int p = 0; p < kPatternsPerThread; ++p) {
     const int64_t e = base + p;
     if (e < total) idx[e] = (uint16_t)(best[p] & 0xffffu);
+  }
+  if (cnt) {
+#pragma unroll
+    for (int p = 0; p < kPatternsPerThread; ++p) {
+      if (base + p < total) {
+        uint32_t* __restrict__ row = cnt + (int64_t)(best[p] & 0xffffu) * (v + 1);
+        atomicAdd(row + v, 1u);
+        for (uint32_t b = pat[p]; b; b &= b - 1u) atomicAdd(row + __builtin_ctz(b), 1u);
+      }
+    }
   }
 }
 
@@ -324,38 +337,108 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = val;
 }
 
-// cnt[c][v + 1]: entry t < v counts the members of codeword c whose bit t is 1, entry v counts
-// the members. One thread per pattern; integer atomics, so the totals do not depend on order.
-__global__ __launch_bounds__(256) void mstep_count_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
-                                                          int64_t N, int64_t K, int v,
-                                                          const uint16_t* __restrict__ idx, int c,
-                                                          uint32_t* __restrict__ cnt) {
+// M-step as a counting sort of the blocks by codeword, then a vote per codeword:
+//   hist     members[c] = number of blocks with idx == c              (one atomic per block)
+//   offsets  start[c] = exclusive prefix sum of members (one block)
+//   scatter  each block's pattern goes to bucket[start[c] + cursor[c]++] (one atomic per block)
+//   vote     thread c counts each bit over its bucket and sets the bits with 2 ones >= members
+//            (sum of +-1 >= 0: ties go to +1); a codeword without members keeps its value.
+// The order inside a bucket depends on the scheduling, the counts do not: the result is exact.
+__global__ __launch_bounds__(256) void mstep_hist_kernel(const uint16_t* __restrict__ idx, int64_t total, int c,
+                                                         uint32_t* __restrict__ members) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const uint32_t id = idx[e];
+    if (id < (uint32_t)c) atomicAdd(members + id, 1u);  // indices must be < c; others are skipped
+  }
+}
+
+constexpr int kScanThreads = 1024;
+
+// start[c] = sum of members[0..c), in two passes: each block of 1024 codewords scans its own
+// range (exclusive, in LDS) and writes its total; then each block adds the totals of the
+// blocks before it.
+__global__ __launch_bounds__(kScanThreads) void mstep_scan_local_kernel(const uint32_t* __restrict__ members, int c,
+                                                                        uint32_t* __restrict__ start,
+                                                                        uint32_t* __restrict__ totals) {
+  __shared__ uint32_t scan[2][kScanThreads];
+  const int t = threadIdx.x;
+  const int i = blockIdx.x * kScanThreads + t;
+  const uint32_t mine = i < c ? members[i] : 0u;
+  scan[0][t] = mine;
+  __syncthreads();
+  int src = 0;
+  for (int off = 1; off < kScanThreads; off <<= 1) {  // inclusive scan, double-buffered
+    scan[src ^ 1][t] = scan[src][t] + (t >= off ? scan[src][t - off] : 0u);
+    src ^= 1;
+    __syncthreads();
+  }
+  if (i < c) start[i] = scan[src][t] - mine;
+  if (t == kScanThreads - 1) totals[blockIdx.x] = scan[src][t];
+}
+
+__global__ __launch_bounds__(kScanThreads) void mstep_scan_add_kernel(const uint32_t* __restrict__ totals, int c,
+                                                                      uint32_t* __restrict__ start) {
+  uint32_t pre = 0u;
+  for (unsigned b = 0; b < blockIdx.x; ++b) pre += totals[b];  // at most 63 totals
+  const int i = blockIdx.x * kScanThreads + threadIdx.x;
+  if (i < c) start[i] += pre;
+}
+
+__global__ __launch_bounds__(256) void mstep_scatter_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
+                                                            int64_t N, int64_t K, int v,
+                                                            const uint16_t* __restrict__ idx, int c,
+                                                            const uint32_t* __restrict__ start,
+                                                            uint32_t* __restrict__ cursor,
+                                                            uint32_t* __restrict__ bucket) {
   const int64_t nb = (K + v - 1) / v;
   const int64_t total = N * nb;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const uint32_t id = idx[e];
-    if (id >= (uint32_t)c) continue;  // indices must be < c; any other entry is skipped
+    if (id >= (uint32_t)c) continue;
     const int64_t n = e / nb;
-    uint32_t b = extract_block(plane + n * ldp, K, (e - n * nb) * v, v);
-    uint32_t* __restrict__ row = cnt + (int64_t)id * (v + 1);
-    atomicAdd(row + v, 1u);
-    while (b) {
-      atomicAdd(row + __builtin_ctz(b), 1u);
-      b &= b - 1u;
-    }
+    const uint32_t b = extract_block(plane + n * ldp, K, (e - n * nb) * v, v);
+    bucket[start[id] + atomicAdd(cursor + id, 1u)] = b;
   }
 }
 
-// codeword c = the bits t with 2 ones >= members (sum of +-1 >= 0: ties go to +1); a codeword
-// with no member keeps its value. counts (optional) receives the member counts.
-__global__ __launch_bounds__(256) void mstep_vote_kernel(const uint32_t* __restrict__ cnt, int c, int v,
+// one wave per codeword: its bucket is read 64 blocks at a time and each bit's count is the
+// popcount of a ballot; bits with 2 ones >= members are set (ties go to +1)
+__global__ __launch_bounds__(256) void mstep_vote_kernel(const uint32_t* __restrict__ members,
+                                                         const uint32_t* __restrict__ start,
+                                                         const uint32_t* __restrict__ bucket, int c, int v,
                                                          uint32_t* __restrict__ codebook,
                                                          uint32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const int id = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (id >= c) return;  // uniform per wave
+  const uint32_t n = members[id];
+  if (counts && lane == 0) counts[id] = n;
+  if (n == 0) return;
+  const uint32_t* __restrict__ bk = bucket + start[id];
+  uint32_t ones[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) ones[t] = 0u;
+  for (uint32_t j0 = 0; j0 < n; j0 += 64) {
+    const bool ok = j0 + (uint32_t)lane < n;
+    const uint32_t b = ok ? bk[j0 + lane] : 0u;
+#pragma unroll
+    for (int t = 0; t < 32; ++t)
+      if (t < v) ones[t] += (uint32_t)__popcll(__ballot((b >> t) & 1u));
+  }
+  uint32_t w = 0u;
+#pragma unroll
+  for (int t = 0; t < 32; ++t)
+    if (t < v && 2ull * ones[t] >= n) w |= 1u << t;
+  if (lane == 0) codebook[id] = w;
+}
+
+// the vote from the counters cnt[c][v + 1] filled by the counting E-step
+__global__ __launch_bounds__(256) void mstep_vote_counts_kernel(const uint32_t* __restrict__ cnt, int c, int v,
+                                                                uint32_t* __restrict__ codebook) {
   const int id = blockIdx.x * 256 + threadIdx.x;
   if (id >= c) return;
   const uint32_t* __restrict__ row = cnt + (int64_t)id * (v + 1);
   const uint64_t n = row[v];
-  if (counts) counts[id] = (uint32_t)n;
   if (n == 0) return;
   uint32_t w = 0u;
   for (int t = 0; t < v; ++t) w |= (2ull * row[t] >= n ? 1u : 0u) << t;
@@ -435,7 +518,7 @@ hipError_t launch_codebook_encode(const uint32_t* plane, int64_t ldp, int64_t N,
   const int64_t total = N * nb;
   const int64_t per_block = 256 * kPatternsPerThread;
   const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
-  encode_kernel<<<grid, 256, 0, s>>>(plane, ldp, N, K, codebook, c, v, idx);
+  encode_kernel<<<grid, 256, 0, s>>>(plane, ldp, N, K, codebook, c, v, idx, nullptr);
   return hipGetLastError();
 }
 
@@ -478,21 +561,34 @@ hipError_t launch_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, i
   return hipGetLastError();
 }
 
-size_t codebook_learn_workspace_bytes(int c, int v) {
-  const size_t counters = (size_t)c * (size_t)(v + 1) * 4u;
+// workspace, used by one step at a time: the standalone M-step's members, start, cursor ([c]
+// each), block totals (64) and bucket (one word per block); the learning loop's counters
+// [c][v + 1]; the 2^v-bit bitmap of the distinct count
+size_t codebook_learn_workspace_bytes(int64_t N, int64_t K, int c, int v) {
+  const size_t blocks = (size_t)N * (size_t)((K + v - 1) / v);
+  const size_t mstep = 4u * (3u * (size_t)c + 64u + blocks);
+  const size_t counters = 4u * (size_t)c * (size_t)(v + 1);
   const size_t bitmap = v <= 24 ? ((size_t)1 << (v > 5 ? v - 3 : 2)) : 0u;
-  return counters > bitmap ? counters : bitmap;
+  size_t m = mstep > counters ? mstep : counters;
+  return m > bitmap ? m : bitmap;
 }
 
 hipError_t launch_codebook_mstep(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
                                  const uint16_t* idx, uint32_t* codebook, int c, uint32_t* counts, void* ws,
                                  hipStream_t s) {
-  uint32_t* cnt = static_cast<uint32_t*>(ws);
-  const int64_t ncnt = (int64_t)c * (v + 1);
-  fill_u32_kernel<<<stride_grid(ncnt), 256, 0, s>>>(cnt, ncnt, 0u);
+  uint32_t* members = static_cast<uint32_t*>(ws);
+  uint32_t* start = members + c;
+  uint32_t* cursor = start + c;
+  uint32_t* totals = cursor + c;
+  uint32_t* bucket = totals + 64;
   const int64_t total = N * ((K + v - 1) / v);
-  mstep_count_kernel<<<stride_grid(total), 256, 0, s>>>(plane, ldp, N, K, v, idx, c, cnt);
-  mstep_vote_kernel<<<(unsigned)((c + 255) / 256), 256, 0, s>>>(cnt, c, v, codebook, counts);
+  const unsigned nscan = (unsigned)((c + kScanThreads - 1) / kScanThreads);
+  fill_u32_kernel<<<stride_grid(3 * (int64_t)c), 256, 0, s>>>(members, 3 * (int64_t)c, 0u);
+  mstep_hist_kernel<<<stride_grid(total), 256, 0, s>>>(idx, total, c, members);
+  mstep_scan_local_kernel<<<nscan, kScanThreads, 0, s>>>(members, c, start, totals);
+  mstep_scan_add_kernel<<<nscan, kScanThreads, 0, s>>>(totals, c, start);
+  mstep_scatter_kernel<<<stride_grid(total), 256, 0, s>>>(plane, ldp, N, K, v, idx, c, start, cursor, bucket);
+  mstep_vote_kernel<<<(unsigned)((c + 3) / 4), 256, 0, s>>>(members, start, bucket, c, v, codebook, counts);
   return hipGetLastError();
 }
 
@@ -511,9 +607,17 @@ hipError_t launch_codebook_learn(const uint32_t* plane, int64_t ldp, int64_t N, 
                                  uint32_t* codebook, int c, int iters, uint16_t* idx, int32_t* n_distinct,
                                  void* ws, hipStream_t s) {
   hipError_t e = launch_codebook_distinct(plane, ldp, N, K, v, codebook, c, n_distinct, ws, s);
+  // each iteration: the E-step counts the members and their bits as it assigns them, then the
+  // vote replaces the codewords (a codeword without members keeps its value)
+  uint32_t* cnt = static_cast<uint32_t*>(ws);
+  const int64_t ncnt = (int64_t)c * (v + 1);
+  const int64_t total = N * ((K + v - 1) / v);
+  const unsigned egrid = (unsigned)((total + 256 * kPatternsPerThread - 1) / (256 * kPatternsPerThread));
   for (int it = 0; it < iters && e == hipSuccess; ++it) {
-    e = launch_codebook_encode(plane, ldp, N, K, codebook, c, v, idx, s);
-    if (e == hipSuccess) e = launch_codebook_mstep(plane, ldp, N, K, v, idx, codebook, c, nullptr, ws, s);
+    fill_u32_kernel<<<stride_grid(ncnt), 256, 0, s>>>(cnt, ncnt, 0u);
+    encode_kernel<<<egrid, 256, 0, s>>>(plane, ldp, N, K, codebook, c, v, idx, cnt);
+    mstep_vote_counts_kernel<<<(unsigned)((c + 255) / 256), 256, 0, s>>>(cnt, c, v, codebook);
+    e = hipGetLastError();
   }
   if (e == hipSuccess) e = launch_codebook_encode(plane, ldp, N, K, codebook, c, v, idx, s);
   return e;

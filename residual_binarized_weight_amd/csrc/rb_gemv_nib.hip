@@ -67,9 +67,9 @@ constexpr int kNibSH = 12;                      // entry row = 4 KB
 constexpr uint32_t kNibBuf = 65536u;
 
 // WV waves per block, RW rows per wave (row r of wave w of block b: (b * WV + w) * RW + r)
-// VAR: the product variants (a {0, 1} reading of the bits, a row offset); the plain product is
-// compiled without them.
-template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV, bool VAR>
+// VAR: the product variants, compiled separately so that none costs the others registers:
+// bit 0 reads the plane bits as {0, 1}, bit 1 adds a row offset; 0 is the plain product.
+template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV, int VAR>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, int64_t N, int64_t K,
     const TX* __restrict__ x, TY* __restrict__ y, const TS* __restrict__ mu, int zero_one) {
@@ -88,6 +88,23 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   const uint32_t Kw = (uint32_t)((K + 31) >> 5);
   const uint32_t Kc = (uint32_t)K;
   const uint32_t ldp_b = (uint32_t)ldp * 4u;
+
+  // the row offsets (if any): a wave's row is uniform, so each is one scalar-cache load of the
+  // aligned dword holding it, issued first; it does not wait behind the vector loads, and its
+  // raw bits stay in scalar registers until the epilogue. The aligned dword never reaches a page
+  // the offset array does not touch (its half-word neighbour is the array's or inside the same
+  // 4-byte unit), so the load cannot fault.
+  uint32_t mr[RW];
+  if constexpr ((VAR & 2) != 0) {
+    typedef __attribute__((address_space(4))) const uint32_t nib_const_u32;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int64_t row = n0 + r < N ? n0 + r : N - 1;
+      const uintptr_t a = reinterpret_cast<uintptr_t>(mu) + 2u * (uintptr_t)row;
+      const uint32_t w = *reinterpret_cast<nib_const_u32*>(a & ~(uintptr_t)3);
+      mr[r] = (a & 2u) ? (w >> 16) : (w & 0xffffu);
+    }
+  }
 
   // plane words and scales through 32-bit offsets (the host checks k N ldp * 4 < 2^31), x
   // through whole dwords (a column past K inside the last one is masked); past the end: 0
@@ -134,13 +151,6 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
     for (int i = 0; i < KP; ++i)
       gr[r][i] = NibScale<TS>::load(rg, (uint32_t)(n0 + r) * (uint32_t)sizeof(TS),
                                     (uint32_t)i * (uint32_t)N * (uint32_t)sizeof(TS));
-  // the row offsets (if any) are loaded with the scales, well before the epilogue needs them
-  uint32_t mr[RW];
-  if constexpr (VAR) {
-    const __amdgpu_buffer_rsrc_t rmu = buffer_rsrc(mu, mu ? (uint32_t)N * (uint32_t)sizeof(TS) : 0u);
-#pragma unroll
-    for (int r = 0; r < RW; ++r) mr[r] = NibScale<TS>::load(rmu, (uint32_t)(n0 + r) * (uint32_t)sizeof(TS), 0u);
-  }
   __builtin_amdgcn_sched_barrier(0);
 
   // Lookup addresses by byte splicing. Lane l's slot offset 32 l + 4 (i ^ a(l)) is
@@ -258,23 +268,21 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   float S = 0.0f;
 #pragma unroll
   for (int w = 0; w < WV; ++w) S += red[w];
-  const float ta = VAR && zero_one ? 1.0f : 2.0f;
-  const float ts = VAR && zero_one ? 0.0f : S;
+  constexpr float ta = (VAR & 1) != 0 ? 1.0f : 2.0f;
+  const float ts = (VAR & 1) != 0 ? 0.0f : S;
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     float v = 0.0f;
 #pragma unroll
     for (int i = 0; i < KP; ++i) v += NibScale<TS>::f32(gr[r][i]) * (ta * wave_sum_dpp(acc[r][i]) - ts);
     if (lane == 63 && n0 + r < N) {
-      if constexpr (VAR) {
-        if (mu) v += NibScale<TS>::f32(mr[r]) * S;
-      }
+      if constexpr ((VAR & 2) != 0) v += NibScale<TS>::f32(mr[r]) * S;
       nib_store<TY>(&y[n0 + r], v);
     }
   }
 }
 
-template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, bool VAR, int WV = kNibWaves>
+template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int VAR, int WV = kNibWaves>
 hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
                             const void* x, void* y, const void* mu, int zero_one, hipStream_t s) {
   // one phase needs one table buffer (two blocks fit on a compute unit), more need two
@@ -298,7 +306,7 @@ hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, 
 // 16 waves per block (larger counts spill)
 constexpr int nib_max_rows(int kp, int nph) { return kp == 1 ? (nph <= 3 ? 3 : 2) : (nph == 1 ? 3 : nph <= 3 ? 2 : 1); }
 
-template <typename TX, typename TS, typename TY, int KP, int NPH, bool VAR>
+template <typename TX, typename TS, typename TY, int KP, int NPH, int VAR>
 hipError_t launch_nib_rows(int rw, const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
                            const void* x, void* y, const void* mu, int zero_one, hipStream_t s) {
   constexpr int kMax = nib_max_rows(KP, NPH);
@@ -312,7 +320,7 @@ hipError_t launch_nib_rows(int rw, const uint32_t* planes, int64_t ldp, const vo
   return launch_nib_shape<TX, TS, TY, KP, NPH, 1, VAR>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
 }
 
-template <typename TX, typename TS, typename TY, int KP, bool VAR>
+template <typename TX, typename TS, typename TY, int KP, int VAR>
 hipError_t launch_nib_kp(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
                          const void* x, void* y, const void* mu, int zero_one, hipStream_t s) {
   const int64_t phases = ((K + 31) / 32 + kNibPhaseWords - 1) / kNibPhaseWords;
@@ -331,6 +339,18 @@ hipError_t launch_nib_kp(const uint32_t* planes, int64_t ldp, const void* g, int
   }
 }
 
+template <int KP>
+hipError_t launch_nib_var(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K, const void* x,
+                          void* y, const void* mu, int zero_one, hipStream_t s) {
+  const int var = (zero_one ? 1 : 0) | (mu ? 2 : 0);
+  switch (var) {
+    case 0: return launch_nib_kp<__half, __half, __half, KP, 0>(planes, ldp, g, N, K, x, y, nullptr, 0, s);
+    case 1: return launch_nib_kp<__half, __half, __half, KP, 1>(planes, ldp, g, N, K, x, y, nullptr, 1, s);
+    case 2: return launch_nib_kp<__half, __half, __half, KP, 2>(planes, ldp, g, N, K, x, y, mu, 0, s);
+    default: return launch_nib_kp<__half, __half, __half, KP, 3>(planes, ldp, g, N, K, x, y, mu, 1, s);
+  }
+}
+
 }  // namespace
 
 bool gemv_nib_fits(int k, int64_t N, int64_t K, int64_t ldp, rb_dtype x_dtype, rb_dtype scale_dtype,
@@ -346,12 +366,8 @@ hipError_t launch_gemv_nib(const uint32_t* planes, int64_t ldp, const void* g, r
                            const void* mu, int zero_one, hipStream_t s) {
   if (x_dtype != RB_F16 || scale_dtype != RB_F16 || y_dtype != RB_F16) return hipErrorNotSupported;
   switch (k) {
-    case 1:
-      if (mu || zero_one) return launch_nib_kp<__half, __half, __half, 1, true>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
-      return launch_nib_kp<__half, __half, __half, 1, false>(planes, ldp, g, N, K, x, y, nullptr, 0, s);
-    case 2:
-      if (mu || zero_one) return launch_nib_kp<__half, __half, __half, 2, true>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
-      return launch_nib_kp<__half, __half, __half, 2, false>(planes, ldp, g, N, K, x, y, nullptr, 0, s);
+    case 1: return launch_nib_var<1>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
+    case 2: return launch_nib_var<2>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
     default: return hipErrorNotSupported;
   }
 }

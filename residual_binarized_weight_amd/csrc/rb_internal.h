@@ -45,7 +45,7 @@ hipError_t launch_codebook_encode(const uint32_t* plane, int64_t ldp, int64_t N,
                                   const uint32_t* codebook, int c, int v, uint16_t* idx,
                                   hipStream_t s);
 size_t codebook_gemv_workspace_bytes(int64_t N, int64_t K, int64_t M);
-size_t codebook_learn_workspace_bytes(int c, int v);
+size_t codebook_learn_workspace_bytes(int64_t N, int64_t K, int c, int v);
 hipError_t launch_codebook_mstep(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
                                  const uint16_t* idx, uint32_t* codebook, int c, uint32_t* counts, void* ws,
                                  hipStream_t s);

@@ -364,10 +364,14 @@ def test_qat_autotune_rejects(kw, status):
 
 
 def test_codebook_learn_workspace_bytes():
-    assert L.rb_codebook_learn_workspace_bytes(65536, 20) == 65536 * 21 * 4
-    assert L.rb_codebook_learn_workspace_bytes(16, 24) == 1 << 21          # the 2^24-bit bitmap
-    assert L.rb_codebook_learn_workspace_bytes(0, 20) == 0
-    assert L.rb_codebook_learn_workspace_bytes(16, 33) == 0
+    # the largest of: 3 c counters + 64 block totals + one word per block (standalone M-step),
+    # c (v + 1) counters (learning loop), the 2^v-bit bitmap (distinct count)
+    assert L.rb_codebook_learn_workspace_bytes(4096, 11008, 65536, 20) == 4 * (3 * 65536 + 64 + 4096 * 551)
+    assert L.rb_codebook_learn_workspace_bytes(1, 40, 65536, 20) == 4 * 65536 * 21
+    assert L.rb_codebook_learn_workspace_bytes(16, 64, 16, 24) == 1 << 21
+    assert L.rb_codebook_learn_workspace_bytes(16, 64, 0, 20) == 0
+    assert L.rb_codebook_learn_workspace_bytes(16, 64, 16, 33) == 0
+    assert L.rb_codebook_learn_workspace_bytes(0, 64, 16, 20) == 0
 
 
 def _cb_learn(fn, **kw):
@@ -396,7 +400,7 @@ _CB_COMMON = [
     (dict(plane=P_MIS), _lib.RB_ERR_MISALIGNED),
     (dict(C=P2), _lib.RB_ERR_MISALIGNED),
     (dict(ws=None), _lib.RB_ERR_WORKSPACE),
-    (dict(wsb=256 * 21 * 4 - 1), _lib.RB_ERR_WORKSPACE),
+    (dict(wsb=4 * (3 * 256 + 64 + 16 * 50) - 1), _lib.RB_ERR_WORKSPACE),
     (dict(ws=P2), _lib.RB_ERR_MISALIGNED),
 ]
 

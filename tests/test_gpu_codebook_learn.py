@@ -114,3 +114,17 @@ def test_learn_mlp_down_layer_sampled():
     sub = P[rows]
     got = idx.cpu().numpy().view(np.uint16)[rows]
     assert np.array_equal(got, O.hamming_encode(sub, Cn))
+
+
+@pytest.mark.parametrize("N,K,v,c,iters", [(1, 1, 20, 1, 2), (1, 7, 3, 8, 2), (2, 45, 20, 3, 3), (1, 64, 24, 5, 1)])
+def test_learn_degenerate_shapes(N, K, v, c, iters):
+    # a single block, a codebook larger than the distinct blocks, one codeword, the widest v
+    words = sign_plane(760 + K, N, K)
+    P = O.sign_blocks(words, K, v)
+    C0 = init_codebook(K, c, v)
+    C_ref, idx_ref, M_ref, _ = O.codebook_learn(P, C0, v, iters)
+    C, idx, nd = rb.codebook_learn(to_dev(words), K, to_dev(C0), v, iters)
+    torch.cuda.synchronize()
+    assert int(nd.item()) == M_ref
+    assert np.array_equal(u32(C), C_ref)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint16), idx_ref.astype(np.uint16))

@@ -102,3 +102,18 @@ def test_mlp_down_layer_variants_sampled_rows():
             y_ref, sabs = O.gemv_variant(pl, gn, None, None if m is None else m.astype(np.float64)[rows],
                                          x.astype(np.float64), K, zero_one)
             assert_product_close(y.float().cpu().numpy()[:, rows], y_ref, sabs)
+
+
+@pytest.mark.parametrize("zero_one", [False, True])
+@pytest.mark.parametrize("N,K,M", [(1, 1, 1), (1, 64, 3), (5, 1, 16), (3, 33, 1)])
+def test_variant_degenerate_shapes(zero_one, N, K, M):
+    k = 2
+    planes = planes_of(850 + K, k, N, K)
+    rng = np.random.default_rng(851)
+    g = rng.uniform(0.005, 0.03, (k, N)).astype(np.float16)
+    mu = rng.normal(0, 0.002, N).astype(np.float16)
+    x = wl.activations(852, M, K)                                     # fp16
+    y = run(planes, g, None, mu, x, K, zero_one, torch.float16)
+    y_ref, sabs = O.gemv_variant(planes, g.astype(np.float64), None, mu.astype(np.float64), x.astype(np.float64),
+                                 K, zero_one)
+    assert_product_close(y, y_ref, sabs)

@@ -236,3 +236,19 @@ def test_mlp_down_layer_training_step_sampled():
     S = np.abs(Xv[toks]) @ np.abs(What_r).T
     assert_close(Y.float().cpu().numpy()[np.ix_(toks, rows)], Y_r, S, UNIT["bf16"] + 2e-5, UNIT["bf16"], "Y")
     check_backward(W, g, h, Xv, X, dYv, dY, "bf16", torch.bfloat16, rows=rows, cols=cols, y_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K,k", [(1, 1, 1, 1), (1, 1, 33, 4), (3, 5, 1, 2), (2, 7, 64, 3)])
+def test_degenerate_shapes(M, N, K, k):
+    # one row, one column, one token, and the largest k: every kernel's tail handling
+    W, g, h = layer(590 + K, N, K, k)
+    X, Xv = act(wl.activations(590, M, K, dtype=np.float32), "bf16")
+    dY, dYv = act(wl.output_grads(590, M, N), "bf16")
+    Wd, gd, hd = (torch.from_numpy(a).to(dev()) for a in (W, g, h))
+    Y, planes, What = rb.qat_forward(Wd, gd, hd, X, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Y_ref, What_ref, _, planes_ref = O.qat_forward(W, g, h, Xv)
+    assert np.array_equal(planes_np(planes, K), planes_ref)
+    assert_nearest(What, What_ref, "bf16")
+    assert_close(Y.cpu().numpy(), Y_ref, np.abs(Xv) @ np.abs(What_ref).T, UNIT["bf16"] + 2e-5, UNIT["f32"], "Y")
+    check_backward(W, g, h, Xv, X, dYv, dY, "bf16", torch.float32)

@@ -121,10 +121,13 @@ def cpu_baseline(planes_np, g_np, x_np, budget_s: float = 12.0):
 
 
 PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, vendor figure
-# VALU lane-operations per second: 256 CUs x 128 fp32 lanes x 2.4 GHz (157.3 TFLOP/s counts an
-# FMA as two flops); the codebook search spends 4 such operations per (pattern, codeword) pair
-PEAK_VALU_OPS = 157.3e12 / 2
-ENCODE_OPS_PER_PAIR = 4
+# VALU issue rate for plain 32-bit integer operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# = 39.3 T lane-operations/s. (The 157.3 TFLOP/s fp32 figure is this x 2 for an FMA's two flops
+# x 2 for packed fp32, which the integer operations of the search do not have.) One (pattern,
+# codeword) pair takes 3.5 of them: xor, popcount, the (distance, index) key, and half of a
+# three-way minimum.
+PEAK_VALU_OPS = 256 * 4 * 16 * 2.4e9
+ENCODE_OPS_PER_PAIR = 3.5
 
 
 def graph_us(torch, calls, rounds: int = 5) -> float:

@@ -350,6 +350,33 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
             f"the GPU's {2 * P_it + 1} passes per update")
         del Wso
 
+    # a3-a5 at M = 4 and 16 on the same layer (fp16, 40 rotated copies): the nibble kernel once
+    # per activation row, so the weight stream is read M times
+    Wb = torch.from_numpy(wl.weights_for("down")).to(dev)
+    planes_b, g_b = rb.pack(Wb, k, ldp=((K + 31) // 32 + 31) // 32 * 32)   # rows padded to 128 bytes
+    del Wb
+    copies_b = [planes_b.clone() for _ in range(COPIES)]
+    for Mb in (4, 16):
+        xb = torch.from_numpy(wl.activations_for("down", Mb)).to(dev)
+        yb = torch.empty((Mb, N), dtype=torch.float16, device=dev)
+        wsb = rb.workspace(rb.RB_OP_GEMV, k, N, K, Mb, device=dev)
+        us = graph_us(torch, [lambda c=c: rb.gemv(c, g_b, None, xb, K, ws=wsb, y=yb) for c in copies_b], 5)
+        byt = algorithmic_bytes(N, K, k, Mb)
+        row = rows[f"a3_a5_gemv_down_4096x11008_k2_m{Mb}"] = roof(
+            "hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us, algorithmic_bytes=byt,
+            weight_bytes_streamed=Mb * k * N * K // 8,
+            note="one nibble-table pass per activation row: the planes are streamed M times")
+        if with_oracle:
+            from oracle import rb_oracle as O
+            RS = 512
+            pl_s = np.ascontiguousarray(planes_b[:, :RS].cpu().numpy().view(np.uint32)[:, :, :(K + 31) // 32])
+            g_s = g_b[:, :RS].float().cpu().numpy().astype(np.float64).reshape(k, RS, 1)
+            xh = xb.cpu().numpy()
+            row["cpu_oracle"] = oracle_rate(lambda: O.gemv(pl_s, g_s, None, xh, K), algorithmic_bytes(RS, K, k, Mb),
+                                            1e9, "GB/s", f"first {RS} of the 4096 rows, M={Mb}, bytes scaled per row")
+    del copies_b, planes_b
+    torch.cuda.synchronize()
+
     # next row: one coupled-training step of the 4096x11008 layer, k = 2, 2048 tokens in bf16:
     # forward (derive planes + What from the fp32 weight, Y = X What^T) and backward (dW, dX,
     # dg, dh); the GEMM kernels are chosen for the shape first (untimed setup); two weight

@@ -568,6 +568,18 @@ hipError_t launch_gemv_variant(const uint32_t* planes, int64_t ldp, const void* 
         launch_gemv_nib(planes, ldp, g, scale_dtype, k, N, K, x, x_dtype, y, y_dtype, mu, zero_one, s);
     if (e != hipErrorNotSupported) return e;
   }
+  // a few activation rows (fp16, h = 1, rows of x that stay 16-byte aligned): the nibble kernel
+  // once per row. Each row re-reads the planes, but a row costs about what the M = 1 product
+  // does, against ~3 VALU operations per weight bit and batch row in the direct kernel.
+  if (M > 1 && M <= 16 && h == nullptr && K % 8 == 0 &&
+      gemv_nib_fits(k, N, K, ldp, x_dtype, scale_dtype, y_dtype)) {
+    for (int64_t m = 0; m < M; ++m) {
+      const hipError_t e = launch_gemv_nib(planes, ldp, g, scale_dtype, k, N, K, static_cast<const __half*>(x) + m * K,
+                                           x_dtype, static_cast<__half*>(y) + m * N, y_dtype, mu, zero_one, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (x_dtype == RB_F16)
     return launch_s<__half>(scale_dtype, y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, mu, zero_one, s);
   return launch_s<float>(scale_dtype, y_dtype, planes, ldp, g, h, k, N, K, x, M, y, ws, mu, zero_one, s);

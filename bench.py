@@ -374,7 +374,31 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
             xh = xb.cpu().numpy()
             row["cpu_oracle"] = oracle_rate(lambda: O.gemv(pl_s, g_s, None, xh, K), algorithmic_bytes(RS, K, k, Mb),
                                             1e9, "GB/s", f"first {RS} of the 4096 rows, M={Mb}, bytes scaled per row")
-    del copies_b, planes_b
+    # ... and with per-column scales h (fp16, the RaBiT dual-scale form) at M = 1: one nibble pass
+    # per plane with x (.) h_i in its tables, chained through the workspace
+    hb = torch.from_numpy(wl.random_scales(5, k, K, dtype=np.float16)).to(dev)
+    Wb = torch.from_numpy(wl.weights_for("down")).to(dev)
+    planes_h, g_h = rb.pack(Wb, k, h=hb, ldp=((K + 31) // 32 + 31) // 32 * 32)
+    del Wb
+    copies_h = [planes_h.clone() for _ in range(COPIES)]
+    x1 = torch.from_numpy(wl.activations_for("down", 1)).to(dev)
+    y1 = torch.empty((1, N), dtype=torch.float16, device=dev)
+    ws1 = rb.workspace(rb.RB_OP_GEMV, k, N, K, 1, device=dev)
+    us = graph_us(torch, [lambda c=c: rb.gemv(c, g_h, hb, x1, K, ws=ws1, y=y1) for c in copies_h], 5)
+    byt = algorithmic_bytes(N, K, k) + 2 * k * K
+    row = rows["a3_a5_gemv_down_4096x11008_k2_general_h_m1"] = roof(
+        "hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us, algorithmic_bytes=byt,
+        note="one single-plane nibble pass per plane (x times that plane's h in the tables)")
+    if with_oracle:
+        from oracle import rb_oracle as O
+        RS = 512
+        pl_s = np.ascontiguousarray(planes_h[:, :RS].cpu().numpy().view(np.uint32)[:, :, :(K + 31) // 32])
+        g_s = g_h[:, :RS].float().cpu().numpy().astype(np.float64).reshape(k, RS, 1)
+        h_s = hb.float().cpu().numpy().astype(np.float64)
+        xh = x1.cpu().numpy()
+        row["cpu_oracle"] = oracle_rate(lambda: O.gemv(pl_s, g_s, h_s, xh, K), algorithmic_bytes(RS, K, k) + 2 * k * K,
+                                        1e9, "GB/s", f"first {RS} of the 4096 rows, bytes scaled per row")
+    del copies_b, planes_b, copies_h, planes_h
     torch.cuda.synchronize()
 
     # next row: one coupled-training step of the 4096x11008 layer, k = 2, 2048 tokens in bf16:

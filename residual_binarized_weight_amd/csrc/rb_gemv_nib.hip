@@ -68,11 +68,16 @@ constexpr uint32_t kNibBuf = 65536u;
 
 // WV waves per block, RW rows per wave (row r of wave w of block b: (b * WV + w) * RW + r)
 // VAR: the product variants, compiled separately so that none costs the others registers:
-// bit 0 reads the plane bits as {0, 1}, bit 1 adds a row offset; 0 is the plain product.
+// bit 0 reads the plane bits as {0, 1}, bit 1 adds a row offset, bit 2 (one plane per pass)
+// multiplies the activations by that plane's column scales h before the tables are built and
+// chains the passes of k planes through an fp32 row sum: acc_mode bit 0 adds the sum of the
+// passes before (acc_io[n]), bit 1 writes the sum for the next pass instead of y (the last
+// pass zeroes acc_io[n] after reading it); 0 is the plain product.
 template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV, int VAR>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, int64_t N, int64_t K,
-    const TX* __restrict__ x, TY* __restrict__ y, const TS* __restrict__ mu, int zero_one) {
+    const TX* __restrict__ x, TY* __restrict__ y, const TS* __restrict__ mu, int zero_one,
+    const TX* __restrict__ hrow, float* __restrict__ acc_io, int acc_mode) {
   extern __shared__ __align__(16) uint8_t lds[];
   float* red = reinterpret_cast<float*>(lds + (NPH == 1 ? 1 : 2) * kNibBuf);  // after the table buffers
   const int tid = threadIdx.x;
@@ -123,6 +128,19 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   }
 #pragma unroll
   for (int p = 1; p < NPH; ++p) xr[p] = NibX<TX>::load(rx, (uint32_t)(p * kNibTables + tid) * NibX<TX>::bytes);
+  // h mode: this plane's column scales, in the same pattern as the activations
+  typename NibX<TX>::raw h0[kTB0];
+  typename NibX<TX>::raw hr[NPH];
+  if constexpr ((VAR & 4) != 0) {
+    const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(hrow, (uint32_t)((uint64_t)((K * sizeof(TX) + 3) & ~3ull)));
+    if (b0) {
+#pragma unroll
+      for (int b = 0; b < kTB0; ++b)
+        h0[b] = NibX<TX>::load(rh, (uint32_t)(b * kB0Threads + tid) * NibX<TX>::bytes);
+    }
+#pragma unroll
+    for (int p = 1; p < NPH; ++p) hr[p] = NibX<TX>::load(rh, (uint32_t)(p * kNibTables + tid) * NibX<TX>::bytes);
+  }
   // activations first, in every wave: requests return in order, and the table build must not
   // queue behind the weight stream
   __builtin_amdgcn_sched_barrier(0);
@@ -171,13 +189,14 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
 
   float xs = 0.0f;  // this thread's share of sum x
   // table q of phase p into buffer p % 2, from the 4 activations in `raw`
-  auto build_one = [&](int p, uint32_t q, typename NibX<TX>::raw raw) {
+  auto build_one = [&](int p, uint32_t q, typename NibX<TX>::raw raw, typename NibX<TX>::raw hraw) {
     typedef __attribute__((address_space(3))) float lds_f32p;
     const uint32_t Q = (uint32_t)(p * kNibTables) + q;
     float xv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float v = NibX<TX>::get(raw, j);
+      float v = NibX<TX>::get(raw, j);
+      if constexpr ((VAR & 4) != 0) v *= NibX<TX>::get(hraw, j);  // exact: fp16 x fp16 fits fp32
       xv[j] = 4u * Q + (uint32_t)j < Kc ? v : 0.0f;
     }
     xs += (xv[0] + xv[1]) + (xv[2] + xv[3]);
@@ -203,10 +222,10 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
     if (p == 0) {
       if (b0) {
 #pragma unroll
-        for (int b = 0; b < kTB0; ++b) build_one(0, (uint32_t)(b * kB0Threads + tid), x0[b]);
+        for (int b = 0; b < kTB0; ++b) build_one(0, (uint32_t)(b * kB0Threads + tid), x0[b], h0[b]);
       }
     } else {
-      build_one(p, (uint32_t)tid, xr[p]);
+      build_one(p, (uint32_t)tid, xr[p], hr[p]);
     }
     if (p == NPH - 1) {
       // every column has been seen: publish this wave's share of sum x (a barrier follows)
@@ -277,14 +296,33 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
     for (int i = 0; i < KP; ++i) v += NibScale<TS>::f32(gr[r][i]) * (ta * wave_sum_dpp(acc[r][i]) - ts);
     if (lane == 63 && n0 + r < N) {
       if constexpr ((VAR & 2) != 0) v += NibScale<TS>::f32(mr[r]) * S;
-      nib_store<TY>(&y[n0 + r], v);
+      if constexpr ((VAR & 4) != 0) {
+        if (acc_mode & 1) v += acc_io[n0 + r];
+        if (acc_mode & 2) {
+          acc_io[n0 + r] = v;
+        } else {
+          nib_store<TY>(&y[n0 + r], v);
+          if (acc_mode & 1) acc_io[n0 + r] = 0.0f;
+        }
+      } else {
+        nib_store<TY>(&y[n0 + r], v);
+      }
     }
   }
 }
 
+// the variant arguments, passed through the launchers unchanged
+struct NibExtra {
+  const void* mu = nullptr;
+  int zero_one = 0;
+  const void* h = nullptr;
+  float* acc = nullptr;
+  int acc_mode = 0;
+};
+
 template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int VAR, int WV = kNibWaves>
 hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
-                            const void* x, void* y, const void* mu, int zero_one, hipStream_t s) {
+                            const void* x, void* y, const NibExtra& ex, hipStream_t s) {
   // one phase needs one table buffer (two blocks fit on a compute unit), more need two
   constexpr size_t lds = (NPH == 1 ? 1 : 2) * (size_t)kNibBuf + 64;
   static bool attr_set = false;  // per instantiation
@@ -297,7 +335,7 @@ hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, 
   const unsigned grid = (unsigned)((N + WV * RW - 1) / (WV * RW));
   gemv_nib_kernel<TX, TS, TY, KP, NPH, RW, WV, VAR><<<grid, 64 * WV, lds, s>>>(
       planes, ldp, static_cast<const TS*>(g), N, K, static_cast<const TX*>(x), static_cast<TY*>(y),
-      static_cast<const TS*>(mu), zero_one);
+      static_cast<const TS*>(ex.mu), ex.zero_one, static_cast<const TX*>(ex.h), ex.acc, ex.acc_mode);
   return hipGetLastError();
 }
 
@@ -308,21 +346,21 @@ constexpr int nib_max_rows(int kp, int nph) { return kp == 1 ? (nph <= 3 ? 3 : 2
 
 template <typename TX, typename TS, typename TY, int KP, int NPH, int VAR>
 hipError_t launch_nib_rows(int rw, const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
-                           const void* x, void* y, const void* mu, int zero_one, hipStream_t s) {
+                           const void* x, void* y, const NibExtra& ex, hipStream_t s) {
   constexpr int kMax = nib_max_rows(KP, NPH);
   if (rw > kMax) rw = kMax;
   if constexpr (kMax >= 3) {
-    if (rw == 3) return launch_nib_shape<TX, TS, TY, KP, NPH, 3, VAR>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
+    if (rw == 3) return launch_nib_shape<TX, TS, TY, KP, NPH, 3, VAR>(planes, ldp, g, N, K, x, y, ex, s);
   }
   if constexpr (kMax >= 2) {
-    if (rw == 2) return launch_nib_shape<TX, TS, TY, KP, NPH, 2, VAR>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
+    if (rw == 2) return launch_nib_shape<TX, TS, TY, KP, NPH, 2, VAR>(planes, ldp, g, N, K, x, y, ex, s);
   }
-  return launch_nib_shape<TX, TS, TY, KP, NPH, 1, VAR>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
+  return launch_nib_shape<TX, TS, TY, KP, NPH, 1, VAR>(planes, ldp, g, N, K, x, y, ex, s);
 }
 
 template <typename TX, typename TS, typename TY, int KP, int VAR>
 hipError_t launch_nib_kp(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
-                         const void* x, void* y, const void* mu, int zero_one, hipStream_t s) {
+                         const void* x, void* y, const NibExtra& ex, hipStream_t s) {
   const int64_t phases = ((K + 31) / 32 + kNibPhaseWords - 1) / kNibPhaseWords;
   const int64_t cus = device_cu_count();
   int rw = 3;
@@ -332,22 +370,28 @@ hipError_t launch_nib_kp(const uint32_t* planes, int64_t ldp, const void* g, int
       break;
     }
   switch (phases) {
-    case 1: return launch_nib_rows<TX, TS, TY, KP, 1, VAR>(rw, planes, ldp, g, N, K, x, y, mu, zero_one, s);
-    case 2: return launch_nib_rows<TX, TS, TY, KP, 2, VAR>(rw, planes, ldp, g, N, K, x, y, mu, zero_one, s);
-    case 3: return launch_nib_rows<TX, TS, TY, KP, 3, VAR>(rw, planes, ldp, g, N, K, x, y, mu, zero_one, s);
-    default: return launch_nib_rows<TX, TS, TY, KP, 4, VAR>(rw, planes, ldp, g, N, K, x, y, mu, zero_one, s);
+    case 1: return launch_nib_rows<TX, TS, TY, KP, 1, VAR>(rw, planes, ldp, g, N, K, x, y, ex, s);
+    case 2: return launch_nib_rows<TX, TS, TY, KP, 2, VAR>(rw, planes, ldp, g, N, K, x, y, ex, s);
+    case 3: return launch_nib_rows<TX, TS, TY, KP, 3, VAR>(rw, planes, ldp, g, N, K, x, y, ex, s);
+    default: return launch_nib_rows<TX, TS, TY, KP, 4, VAR>(rw, planes, ldp, g, N, K, x, y, ex, s);
   }
 }
 
 template <int KP>
 hipError_t launch_nib_var(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K, const void* x,
-                          void* y, const void* mu, int zero_one, hipStream_t s) {
-  const int var = (zero_one ? 1 : 0) | (mu ? 2 : 0);
+                          void* y, const NibExtra& ex, hipStream_t s) {
+  const int var = (ex.zero_one ? 1 : 0) | (ex.mu ? 2 : 0) | (ex.h ? 4 : 0);
   switch (var) {
-    case 0: return launch_nib_kp<__half, __half, __half, KP, 0>(planes, ldp, g, N, K, x, y, nullptr, 0, s);
-    case 1: return launch_nib_kp<__half, __half, __half, KP, 1>(planes, ldp, g, N, K, x, y, nullptr, 1, s);
-    case 2: return launch_nib_kp<__half, __half, __half, KP, 2>(planes, ldp, g, N, K, x, y, mu, 0, s);
-    default: return launch_nib_kp<__half, __half, __half, KP, 3>(planes, ldp, g, N, K, x, y, mu, 1, s);
+    case 0: return launch_nib_kp<__half, __half, __half, KP, 0>(planes, ldp, g, N, K, x, y, ex, s);
+    case 1: return launch_nib_kp<__half, __half, __half, KP, 1>(planes, ldp, g, N, K, x, y, ex, s);
+    case 2: return launch_nib_kp<__half, __half, __half, KP, 2>(planes, ldp, g, N, K, x, y, ex, s);
+    case 3: return launch_nib_kp<__half, __half, __half, KP, 3>(planes, ldp, g, N, K, x, y, ex, s);
+    default:
+      if constexpr (KP == 1) {  // h mode: one plane per pass, no row offset
+        if (var == 4) return launch_nib_kp<__half, __half, __half, 1, 4>(planes, ldp, g, N, K, x, y, ex, s);
+        if (var == 5) return launch_nib_kp<__half, __half, __half, 1, 5>(planes, ldp, g, N, K, x, y, ex, s);
+      }
+      return hipErrorNotSupported;
   }
 }
 
@@ -366,10 +410,45 @@ hipError_t launch_gemv_nib(const uint32_t* planes, int64_t ldp, const void* g, r
                            const void* mu, int zero_one, hipStream_t s) {
   if (x_dtype != RB_F16 || scale_dtype != RB_F16 || y_dtype != RB_F16) return hipErrorNotSupported;
   switch (k) {
-    case 1: return launch_nib_var<1>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
-    case 2: return launch_nib_var<2>(planes, ldp, g, N, K, x, y, mu, zero_one, s);
+    case 1: {
+      NibExtra ex;
+      ex.mu = mu;
+      ex.zero_one = zero_one;
+      return launch_nib_var<1>(planes, ldp, g, N, K, x, y, ex, s);
+    }
+    case 2: {
+      NibExtra ex;
+      ex.mu = mu;
+      ex.zero_one = zero_one;
+      return launch_nib_var<2>(planes, ldp, g, N, K, x, y, ex, s);
+    }
     default: return hipErrorNotSupported;
   }
+}
+
+// general h, one activation row: one single-plane pass per plane with x (.) h_i in the tables;
+// the passes add up in acc (one fp32 per row, zero on entry and on return) and the last one
+// writes y. K must be a multiple of 4 and h 8-byte aligned (each pass reads h_i in 8-byte units).
+bool gemv_nib_h_fits(int k, int64_t N, int64_t K, int64_t ldp, const void* h, rb_dtype x_dtype,
+                     rb_dtype scale_dtype, rb_dtype y_dtype) {
+  return k >= 1 && k <= 4 && K % 4 == 0 && (reinterpret_cast<uintptr_t>(h) & 7u) == 0 &&
+         gemv_nib_fits(1, N, K, ldp, x_dtype, scale_dtype, y_dtype) &&
+         (uint64_t)k * N * ldp * 4 < 0x7fffffffull;
+}
+
+hipError_t launch_gemv_nib_h(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
+                             int64_t K, const void* x, void* y, int zero_one, float* acc, hipStream_t s) {
+  for (int i = 0; i < k; ++i) {
+    NibExtra ex;
+    ex.zero_one = zero_one;
+    ex.h = static_cast<const __half*>(h) + (int64_t)i * K;
+    ex.acc = acc;
+    ex.acc_mode = (i > 0 ? 1 : 0) | (i + 1 < k ? 2 : 0);
+    const hipError_t e = launch_nib_var<1>(planes + (int64_t)i * N * ldp, ldp,
+                                           static_cast<const __half*>(g) + (int64_t)i * N, N, K, x, y, ex, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace rb

@@ -28,6 +28,12 @@ bool gemv_nib_fits(int k, int64_t N, int64_t K, int64_t ldp, rb_dtype x_dtype, r
 hipError_t launch_gemv_nib(const uint32_t* planes, int64_t ldp, const void* g, rb_dtype scale_dtype, int k,
                            int64_t N, int64_t K, const void* x, rb_dtype x_dtype, void* y, rb_dtype y_dtype,
                            const void* mu, int zero_one, hipStream_t s);
+// general h at M = 1 (fp16): one single-plane nibble pass per plane, chained through acc
+// (N floats, zero on entry and on return)
+bool gemv_nib_h_fits(int k, int64_t N, int64_t K, int64_t ldp, const void* h, rb_dtype x_dtype,
+                     rb_dtype scale_dtype, rb_dtype y_dtype);
+hipError_t launch_gemv_nib_h(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
+                             int64_t K, const void* x, void* y, int zero_one, float* acc, hipStream_t s);
 // the product with {0, 1} planes (zero_one) and/or a per-row offset mu (h must be NULL with mu)
 hipError_t launch_gemv_variant(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                                const void* mu, int zero_one, rb_dtype scale_dtype, int k, int64_t N, int64_t K,

@@ -144,3 +144,39 @@ def test_gemv_m1_writes_nothing_past_y_and_is_deterministic(N, K, k):
     assert torch.equal(y1, y)
     y_ref, sabs = O.gemv(planes_np(pd, K), scales_np(gd, k, N), None, x, K)
     assert_product_close(y.float().cpu().numpy(), y_ref, sabs)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+@pytest.mark.parametrize("K", [300, 301, 4096, 11008, 16384])
+def test_gemv_general_h_fp16_m1(k, K):
+    # per-column scales h (fp16, some negative), one activation row: the single-plane nibble
+    # pass per plane (K a multiple of 4) or the direct kernel (K = 301)
+    N = 96
+    W = wl.heavy_tailed_weights(74 + k, N, K)
+    h = wl.random_scales(12 + k, k, K, negative_frac=0.2, dtype=np.float16)
+    x = wl.activations(75, 1, K)
+    planes, g = oracle_case(W, k, h=h)
+    y = gpu_gemv(planes, g, h, x, K)
+    y_ref, sabs = O.gemv(planes, g, h, x, K)
+    assert_product_close(y, y_ref, sabs)
+
+
+def test_gemv_general_h_leaves_the_workspace_zero():
+    # the h passes chain their sums through the workspace and must leave it zero for the
+    # byte-table kernel, which shares it (k = 3, h = 1 at M = 1 runs that kernel)
+    N, K = 200, 4096
+    W = wl.heavy_tailed_weights(76, N, K)
+    h = wl.random_scales(13, 2, K, dtype=np.float16)
+    x = wl.activations(77, 1, K)
+    p2, g2 = oracle_case(W, 2, h=h)
+    p3, g3 = oracle_case(W, 3)
+    ws = rb.workspace(rb.RB_OP_GEMV, 3, N, K, 1, device=dev())
+    for _ in range(2):
+        y2 = rb.gemv(to_dev(p2), to_dev(g2.reshape(2, N).astype(np.float16)), to_dev(h), to_dev(x), K, ws=ws)
+        y3 = rb.gemv(to_dev(p3), to_dev(g3.reshape(3, N).astype(np.float16)), None, to_dev(x), K, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws) == 0
+        r2, s2 = O.gemv(p2, g2, h, x, K)
+        r3, s3 = O.gemv(p3, g3, None, x, K)
+        assert_product_close(y2.float().cpu().numpy(), r2, s2)
+        assert_product_close(y3.float().cpu().numpy(), r3, s3)

@@ -117,3 +117,18 @@ def test_variant_degenerate_shapes(zero_one, N, K, M):
     y_ref, sabs = O.gemv_variant(planes, g.astype(np.float64), None, mu.astype(np.float64), x.astype(np.float64),
                                  K, zero_one)
     assert_product_close(y, y_ref, sabs)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_zero_one_with_general_h_fp16_m1(k):
+    # {0, 1} bits with per-column scales at M = 1 (fp16): the chained single-plane passes
+    N, K = 130, 4096
+    planes = planes_of(860 + k, k, N, K)
+    rng = np.random.default_rng(861)
+    g = rng.uniform(0.005, 0.03, (k, N)).astype(np.float16)
+    h = wl.random_scales(862, k, K, negative_frac=0.2, dtype=np.float16)
+    x = wl.activations(863, 1, K)
+    y = run(planes, g, h, None, x, K, True, torch.float16)
+    y_ref, sabs = O.gemv_variant(planes, g.astype(np.float64), h.astype(np.float64), None, x.astype(np.float64), K,
+                                 True)
+    assert_product_close(y, y_ref, sabs)

@@ -398,6 +398,17 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
         xh = x1.cpu().numpy()
         row["cpu_oracle"] = oracle_rate(lambda: O.gemv(pl_s, g_s, h_s, xh, K), algorithmic_bytes(RS, K, k) + 2 * k * K,
                                         1e9, "GB/s", f"first {RS} of the 4096 rows, bytes scaled per row")
+    # a6 on the 4096x11008 layer at M = 64 and 256 (prefill): 32 row tiles, so K is split
+    # across blocks and the chunks meet in the workspace
+    for Mb in (64, 256):
+        xb = torch.from_numpy(wl.activations_for("down", Mb)).to(dev)
+        yb = torch.empty((Mb, N), dtype=torch.float16, device=dev)
+        wsg = rb.workspace(rb.RB_OP_GEMM_SMALL, k, N, K, Mb, device=dev)
+        us = graph_us(torch, [lambda c=c: rb.gemm_small(c, g_b, None, xb, K, ws=wsg, y=yb) for c in copies_b], 3)
+        flops = 2.0 * Mb * N * K * k
+        rows[f"a6_gemm_small_down_4096x11008_k2_m{Mb}"] = roof(
+            "mfma", flops / (us * 1e-6) / 1e12, PEAK_FP16_MFMA_TFLOPS, "TFLOP/s", us, flops=flops,
+            k_chunks=(wsg.numel() // (4 * Mb * N)) if wsg is not None else 1)
     del copies_b, planes_b, copies_h, planes_h
     torch.cuda.synchronize()
 

@@ -162,7 +162,11 @@ rb_status rb_gemv_variant(const uint32_t* planes, int64_t ldp, const void* g, co
  *   Arguments as rb_gemv, except: x_dtype must be RB_F16; 1 <= M <= 4096; K must be a
  *   multiple of 64 and at most 2^22, ldp even and at most 2^20; a non-NULL h must be RB_F16 (scale_dtype
  *   RB_F16, else RB_ERR_UNSUPPORTED) and 16-byte aligned. Rows of y past M and columns
- *   past N are not written. No workspace (rb_workspace_bytes returns 0).
+ *   past N are not written. When the row and batch tiles are too few to fill the GPU (e.g.
+ *   N = 4096), K is split across blocks and the partial sums meet in the workspace:
+ *   rb_workspace_bytes(RB_OP_GEMM_SMALL, k, N, K, M) bytes (fp32 [chunks][M][N]; 0 when no
+ *   split is used), 4-byte aligned; its contents are scratch. The chunks are added in a fixed
+ *   order, so the result is deterministic.
  *   With fp16 g and h = NULL, +-g_i itself is the expanded operand and all planes share
  *   one accumulator; otherwise each plane's sum is scaled by g_i in fp32.
  */

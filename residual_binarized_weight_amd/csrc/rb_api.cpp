@@ -171,6 +171,7 @@ rb_status rb_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, cons
   if (h && !aligned(h, 16)) return RB_ERR_MISALIGNED;
   const size_t need = rb::gemm_small_workspace_bytes(k, N, K, M);
   if (need > 0 && (!ws || ws_bytes < need)) return RB_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 4)) return RB_ERR_MISALIGNED;
   log_call("rb_gemm_small", N, K, M, k);
   return from_hip(rb::launch_gemm_small(planes, ldp, g, h, scale_dtype, k, N, K, x, M, y, y_dtype, ws,
                                         static_cast<hipStream_t>(stream)));

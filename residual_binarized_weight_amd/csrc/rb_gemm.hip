@@ -159,11 +159,14 @@ __device__ __forceinline__ h8 expand_b(uint32_t nw, int t, int hh, u32x4g base) 
 // and they meet activations that read as 0, so they add +-0 (a non-finite g, which no
 // finite W packs to, would turn that row's +-0 into NaN).
 // NG wave groups per block (1 or 2). With two, MSPLIT: they take two halves of the batch,
-// else two halves of K.
+// else two halves of K. blockIdx.z splits K further into chunks of kz columns (a multiple of
+// the stage width) when the row and batch tiles alone would leave compute units idle; each
+// chunk's partial sums then go to part[z][M][N] (fp32) for gemm_reduce_kernel, else to y.
 template <typename TS, typename TY, int MT, int MODE, int KP, int NG, bool MSPLIT>
 __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, const __half* __restrict__ h,
-    int k, int64_t N, int64_t K, const __half* __restrict__ x, int64_t M, TY* __restrict__ y) {
+    int k, int64_t N, int64_t K, const __half* __restrict__ x, int64_t M, TY* __restrict__ y, int64_t kz,
+    float* __restrict__ part) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid_all = threadIdx.x;
   const int lane = tid_all & 63;
@@ -189,10 +192,14 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
   const int64_t m_base = MSPLIT ? ((int64_t)blockIdx.y * NG + grp) * MT * 32 : (int64_t)blockIdx.y * MT * 32;
   const int64_t m_left = M - m_base;
   const int64_t m_rows = m_left < 0 ? 0 : (m_left < MT * 32 ? m_left : MT * 32);
-  const int64_t kh_raw = (((K + 1) / 2 + kStageCols - 1) / kStageCols) * kStageCols;
-  const int64_t kh = (MSPLIT || NG == 1) ? K : (kh_raw < K ? kh_raw : K);
-  const int64_t kbeg = MSPLIT || grp == 0 ? 0 : kh;
-  const int64_t kend = MSPLIT || grp == 0 ? kh : K;
+  // this block's K chunk [kz0, kz1); the group split below works inside it
+  const int64_t kz0 = (int64_t)blockIdx.z * kz;
+  const int64_t kz1 = kz0 + kz < K ? kz0 + kz : K;
+  const int64_t kl = kz1 - kz0;
+  const int64_t kh_raw = (((kl + 1) / 2 + kStageCols - 1) / kStageCols) * kStageCols;
+  const int64_t kh = (MSPLIT || NG == 1) ? kl : (kh_raw < kl ? kh_raw : kl);
+  const int64_t kbeg = kz0 + (MSPLIT || grp == 0 ? 0 : kh);
+  const int64_t kend = kz0 + (MSPLIT || grp == 0 ? kh : kl);
   const int nch = (int)((kh + kStageCols - 1) / kStageCols);
   const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(x + (m_rows > 0 ? m_base : 0) * K, m_rows * K * 2);
   const uint32_t lane_off = (uint32_t)((nc - rb) * ldp * 4 + kbeg / 8);  // 4 bytes per 32 columns
@@ -338,10 +345,55 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int64_t m = m_base + mt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-        if (m < M) gemm_store<TY>(&y[m * N + n], yacc[mt][j]);
+        if (m < M) {
+          if (part)
+            part[((int64_t)blockIdx.z * M + m) * N + n] = yacc[mt][j];
+          else
+            gemm_store<TY>(&y[m * N + n], yacc[mt][j]);
+        }
       }
     }
   }
+}
+
+// y[m][n] = sum over the z chunks of part[z][m][n], in chunk order
+template <typename TY>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int64_t MN, int nz,
+                                                          TY* __restrict__ y) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += (int64_t)gridDim.x * 256) {
+    float s = 0.0f;
+    for (int z = 0; z < nz; ++z) s += part[(int64_t)z * MN + e];
+    gemm_store<TY>(&y[e], s);
+  }
+}
+
+// batch rows per block for M (as launch_mt picks the tiles)
+int64_t gemm_m_per_block(int64_t M, int mode_h) {
+  if (M <= 32) return 32;
+  if (M <= 64) return 64;
+  if (M <= 128 || mode_h) return 128;
+  return 256;
+}
+
+// K chunks per (row tile, batch tile): enough blocks for about one per compute unit (256),
+// each chunk at least 8 stages (1024 columns) long; 1 when the tiles alone fill the part.
+// (Measured on 4096 x 11008: two blocks per unit with 512-column chunks, or at most 4 chunks
+// from M = 128 on, were both slower at every M.)
+int gemm_k_split(int64_t N, int64_t K, int64_t M, int mode_h) {
+  const int64_t tiles = ((N + kGemmTileN - 1) / kGemmTileN) * ((M + gemm_m_per_block(M, mode_h) - 1) /
+                                                              gemm_m_per_block(M, mode_h));
+  if (tiles >= 192) return 1;
+  int64_t z = (256 + tiles - 1) / tiles;
+  const int64_t zmax = K / (8 * kStageCols);
+  if (z > zmax) z = zmax;
+  if (z > 16) z = 16;
+  return z < 1 ? 1 : (int)z;
+}
+
+// chunk width for z chunks: a whole number of stages
+int64_t gemm_k_chunk(int64_t K, int z) {
+  const int64_t stages = (K + kStageCols - 1) / kStageCols;
+  return ((stages + z - 1) / z) * kStageCols;
 }
 
 template <int MT, int NG>
@@ -351,7 +403,7 @@ constexpr size_t gemm_lds_bytes() {
 
 template <typename TS, typename TY, int MT, int MODE, int KP, int NG, bool MSPLIT>
 hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
-                      int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
+                      int64_t K, const void* x, int64_t M, void* y, float* ws, hipStream_t s) {
   constexpr size_t lds = gemm_lds_bytes<MT, NG>();
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
@@ -363,9 +415,17 @@ hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const 
   const int64_t m_per_block = (int64_t)32 * MT * (MSPLIT ? NG : 1);
   const unsigned gx = (unsigned)((N + kGemmTileN - 1) / kGemmTileN);
   const unsigned gy = (unsigned)((M + m_per_block - 1) / m_per_block);
-  gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT><<<dim3(gx, gy), kGemmGroupThreads * NG, lds, s>>>(
+  const int nz = gemm_k_split(N, K, M, MODE == kModeH);
+  const int64_t kz = nz > 1 ? gemm_k_chunk(K, nz) : K;
+  float* part = nz > 1 ? ws : nullptr;
+  gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT><<<dim3(gx, gy, (unsigned)nz), kGemmGroupThreads * NG, lds, s>>>(
       planes, ldp, static_cast<const TS*>(g), static_cast<const __half*>(h), k, N, K,
-      static_cast<const __half*>(x), M, static_cast<TY*>(y));
+      static_cast<const __half*>(x), M, static_cast<TY*>(y), kz, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nz == 1) return e;
+  const int64_t MN = M * N;
+  const int64_t rb = (MN + 255) / 256;
+  gemm_reduce_kernel<TY><<<(unsigned)(rb < 4096 ? rb : 4096), 256, 0, s>>>(part, MN, nz, static_cast<TY*>(y));
   return hipGetLastError();
 }
 
@@ -376,37 +436,43 @@ hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const 
 // slower at M = 256: one wave per SIMD hides less than the halved expansion work saves.)
 template <typename TS, typename TY, int MODE, int KP>
 hipError_t launch_mt(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
-                     int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
-  if (M <= 32) return launch_one<TS, TY, 1, MODE, KP, 2, false>(planes, ldp, g, h, k, N, K, x, M, y, s);
-  if (M <= 64) return launch_one<TS, TY, 2, MODE, KP, 2, false>(planes, ldp, g, h, k, N, K, x, M, y, s);
+                     int64_t K, const void* x, int64_t M, void* y, float* ws, hipStream_t s) {
+  if (M <= 32) return launch_one<TS, TY, 1, MODE, KP, 2, false>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+  if (M <= 64) return launch_one<TS, TY, 2, MODE, KP, 2, false>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   // h mode stages h as well and keeps at most two batch tiles (four would spill registers)
-  if (M <= 128 || MODE == kModeH) return launch_one<TS, TY, 2, MODE, KP, 2, true>(planes, ldp, g, h, k, N, K, x, M, y, s);
-  if constexpr (MODE != kModeH) return launch_one<TS, TY, 4, MODE, KP, 2, true>(planes, ldp, g, h, k, N, K, x, M, y, s);
+  if (M <= 128 || MODE == kModeH) return launch_one<TS, TY, 2, MODE, KP, 2, true>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+  if constexpr (MODE != kModeH) return launch_one<TS, TY, 4, MODE, KP, 2, true>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   return hipErrorNotSupported;
 }
 
 template <typename TY>
 hipError_t launch_y(rb_dtype scale_dtype, const uint32_t* planes, int64_t ldp, const void* g, const void* h,
-                    int k, int64_t N, int64_t K, const void* x, int64_t M, void* y, hipStream_t s) {
-  if (h != nullptr) return launch_mt<__half, TY, kModeH, 1>(planes, ldp, g, h, k, N, K, x, M, y, s);
-  if (scale_dtype == RB_F32) return launch_mt<float, TY, kModeOnes, 1>(planes, ldp, g, h, k, N, K, x, M, y, s);
+                    int k, int64_t N, int64_t K, const void* x, int64_t M, void* y, float* ws, hipStream_t s) {
+  if (h != nullptr) return launch_mt<__half, TY, kModeH, 1>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+  if (scale_dtype == RB_F32) return launch_mt<float, TY, kModeOnes, 1>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   switch (k) {
-    case 1: return launch_mt<__half, TY, kModeFold, 1>(planes, ldp, g, h, k, N, K, x, M, y, s);
-    case 2: return launch_mt<__half, TY, kModeFold, 2>(planes, ldp, g, h, k, N, K, x, M, y, s);
-    case 3: return launch_mt<__half, TY, kModeFold, 3>(planes, ldp, g, h, k, N, K, x, M, y, s);
-    default: return launch_mt<__half, TY, kModeFold, 4>(planes, ldp, g, h, k, N, K, x, M, y, s);
+    case 1: return launch_mt<__half, TY, kModeFold, 1>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+    case 2: return launch_mt<__half, TY, kModeFold, 2>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+    case 3: return launch_mt<__half, TY, kModeFold, 3>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+    default: return launch_mt<__half, TY, kModeFold, 4>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   }
 }
 
 }  // namespace
 
-size_t gemm_small_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
+// the K-split partial sums (fp32 [z][M][N]) when the tiles alone would leave compute units idle
+size_t gemm_small_workspace_bytes(int, int64_t N, int64_t K, int64_t M) {
+  const int nz = gemm_k_split(N, K, M, 0) > gemm_k_split(N, K, M, 1) ? gemm_k_split(N, K, M, 0)
+                                                                       : gemm_k_split(N, K, M, 1);
+  return nz > 1 ? (size_t)nz * (size_t)M * (size_t)N * sizeof(float) : 0u;
+}
 
 hipError_t launch_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                              rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x, int64_t M,
-                             void* y, rb_dtype y_dtype, void*, hipStream_t s) {
-  if (y_dtype == RB_F16) return launch_y<__half>(scale_dtype, planes, ldp, g, h, k, N, K, x, M, y, s);
-  return launch_y<float>(scale_dtype, planes, ldp, g, h, k, N, K, x, M, y, s);
+                             void* y, rb_dtype y_dtype, void* ws, hipStream_t s) {
+  float* wsf = static_cast<float*>(ws);
+  if (y_dtype == RB_F16) return launch_y<__half>(scale_dtype, planes, ldp, g, h, k, N, K, x, M, y, wsf, s);
+  return launch_y<float>(scale_dtype, planes, ldp, g, h, k, N, K, x, M, y, wsf, s);
 }
 
 }  // namespace rb

@@ -570,9 +570,16 @@ hipError_t launch_gemv_variant(const uint32_t* planes, int64_t ldp, const void* 
   }
   // one activation row with column scales h (fp16): the nibble kernel once per plane, x (.) h_i
   // in its tables, the planes' sums chained in fp32 through the workspace (left zero)
-  if (M == 1 && h != nullptr && mu == nullptr && ws != nullptr &&
-      gemv_nib_h_fits(k, N, K, ldp, h, x_dtype, scale_dtype, y_dtype))
-    return launch_gemv_nib_h(planes, ldp, g, h, k, N, K, x, y, zero_one, static_cast<float*>(ws), s);
+  // (and per activation row for a few rows whose starts stay 16-byte aligned)
+  if (M <= 16 && (M == 1 || K % 8 == 0) && h != nullptr && mu == nullptr && ws != nullptr &&
+      gemv_nib_h_fits(k, N, K, ldp, h, x_dtype, scale_dtype, y_dtype)) {
+    for (int64_t m = 0; m < M; ++m) {
+      const hipError_t e = launch_gemv_nib_h(planes, ldp, g, h, k, N, K, static_cast<const __half*>(x) + m * K,
+                                             static_cast<__half*>(y) + m * N, zero_one, static_cast<float*>(ws), s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   // a few activation rows (fp16, h = 1, rows of x that stay 16-byte aligned): the nibble kernel
   // once per row. Each row re-reads the planes, but a row costs about what the M = 1 product
   // does, against ~3 VALU operations per weight bit and batch row in the direct kernel.

@@ -459,3 +459,13 @@ def _gemv_variant(**kw):
 ])
 def test_gemv_variant_rejects(kw, status):
     assert _gemv_variant(**kw) == status
+
+
+def test_gemm_small_split_workspace():
+    # 32 row tiles of the 4096-row layer: K is split in 8 chunks of partial sums (fp32 [8][M][N]);
+    # the 28672-row layer fills the GPU with its tiles alone and needs none
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 11008, 64) == 8 * 64 * 4096 * 4
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 28672, 8192, 256) == 0
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 1024, 64) == 0   # chunks < 1024 columns
+    need = L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 11008, 64)
+    assert _prod("rb_gemm_small", k=2, N=4096, K=11008, M=64, ldp=344, ws=P2, wsb=need) == _lib.RB_ERR_MISALIGNED

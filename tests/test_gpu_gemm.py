@@ -143,3 +143,53 @@ def test_gemm_padded_ldp_no_writes_past_y_deterministic():
     assert torch.equal(y1, y)
     y_ref, sabs = O.gemv(res["planes"], res["g"], None, x, K)
     assert_product_close(y.float().cpu().numpy(), y_ref, sabs)
+
+
+@pytest.mark.parametrize("N,K", [(37, 2048), (300, 4160), (130, 11008)])
+@pytest.mark.parametrize("M", [1, 33, 64, 100, 256])
+@pytest.mark.parametrize("k", [1, 2])
+def test_gemm_k_split_fold(N, K, M, k):
+    # few row tiles: the K chunks of a tile run in separate blocks and meet in the workspace
+    W = wl.heavy_tailed_weights(92 + k, N, K)
+    x = wl.activations(93, M, K)
+    res = O.binarize(W, k)
+    y = gpu_gemm(res["planes"], res["g"], None, x, K, y_dtype=torch.float32)
+    y_ref, sabs = O.gemv(res["planes"], res["g"], None, x, K)
+    assert_product_close(y, y_ref, sabs, fp16_out=False)
+
+
+@pytest.mark.parametrize("mode", ["fp32_scales", "general_h"])
+@pytest.mark.parametrize("M", [20, 130])
+def test_gemm_k_split_other_modes(mode, M):
+    N, K, k = 90, 5120, 2
+    W = wl.heavy_tailed_weights(94, N, K)
+    x = wl.activations(95, M, K)
+    if mode == "fp32_scales":
+        res = O.binarize(W, k, scale_fmt="f32")
+        y = gpu_gemm(res["planes"], res["g"], None, x, K, y_dtype=torch.float16, sdt=np.float32)
+        y_ref, sabs = O.gemv(res["planes"], res["g"], None, x, K)
+    else:
+        h = wl.random_scales(15, k, K, negative_frac=0.3, dtype=np.float16)
+        res = O.binarize(W, k, h=h)
+        y = gpu_gemm(res["planes"], res["g"], h, x, K, y_dtype=torch.float16)
+        y_ref, sabs = O.gemv(res["planes"], res["g"], h, x, K)
+    assert_product_close(y, y_ref, sabs)
+
+
+@pytest.mark.parametrize("M", [64, 256])
+def test_gemm_mlp_down_layer_k_split_sampled_rows(M):
+    # the 4096 x 11008 layer (32 row tiles): K split across blocks, deterministic
+    W = wl.weights_for("down")
+    N, K = W.shape
+    planes, g = rb.pack(torch.from_numpy(W).to(dev()), 2)
+    x = wl.activations_for("down", M)
+    xd = to_dev(x)
+    y = rb.gemm_small(planes, g, None, xd, K, y_dtype=torch.float32)
+    y2 = rb.gemm_small(planes, g, None, xd, K, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    rows = np.sort(np.random.default_rng(96).choice(N, 96, replace=False))
+    pl = planes.cpu().numpy().view(np.uint32)[:, rows]
+    gn = g.float().cpu().numpy().astype(np.float64)[:, rows].reshape(2, len(rows), 1)
+    y_ref, sabs = O.gemv(pl, gn, None, x, K)
+    assert_product_close(y.cpu().numpy()[:, rows], y_ref, sabs, fp16_out=False)

@@ -180,3 +180,15 @@ def test_gemv_general_h_leaves_the_workspace_zero():
         r3, s3 = O.gemv(p3, g3, None, x, K)
         assert_product_close(y2.float().cpu().numpy(), r2, s2)
         assert_product_close(y3.float().cpu().numpy(), r3, s3)
+
+
+@pytest.mark.parametrize("M", [2, 5, 16])
+def test_gemv_general_h_fp16_small_batch(M):
+    N, K, k = 70, 1024, 2
+    W = wl.heavy_tailed_weights(78, N, K)
+    h = wl.random_scales(14, k, K, negative_frac=0.2, dtype=np.float16)
+    x = wl.activations(79, M, K)
+    planes, g = oracle_case(W, k, h=h)
+    y = gpu_gemv(planes, g, h, x, K)
+    y_ref, sabs = O.gemv(planes, g, h, x, K)
+    assert_product_close(y, y_ref, sabs)

@@ -364,8 +364,9 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
         byt = algorithmic_bytes(N, K, k, Mb)
         row = rows[f"a3_a5_gemv_down_4096x11008_k2_m{Mb}"] = roof(
             "hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us, algorithmic_bytes=byt,
-            weight_bytes_streamed=Mb * k * N * K // 8,
-            note="one nibble-table pass per activation row: the planes are streamed M times")
+            weight_bytes_streamed=k * N * K // 8,
+            note="a batch of 4 or more rows runs on the matrix cores: one pass over the planes, K split into "
+                 "chunks whose fp32 sums meet in the workspace")
         if with_oracle:
             from oracle import rb_oracle as O
             RS = 512
@@ -389,6 +390,13 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
     row = rows["a3_a5_gemv_down_4096x11008_k2_general_h_m1"] = roof(
         "hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us, algorithmic_bytes=byt,
         note="one single-plane nibble pass per plane (x times that plane's h in the tables)")
+    x16 = torch.from_numpy(wl.activations_for("down", 16)).to(dev)
+    y16 = torch.empty((16, N), dtype=torch.float16, device=dev)
+    us16 = graph_us(torch, [lambda c=c: rb.gemv(c, g_h, hb, x16, K, ws=ws1, y=y16) for c in copies_h], 5)
+    byt16 = algorithmic_bytes(N, K, k, 16) + 2 * k * K
+    rows["a3_a5_gemv_down_4096x11008_k2_general_h_m16"] = roof(
+        "hbm", byt16 / (us16 * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us16, algorithmic_bytes=byt16,
+        note="on the matrix cores, h_i entering the fp16 operand")
     if with_oracle:
         from oracle import rb_oracle as O
         RS = 512

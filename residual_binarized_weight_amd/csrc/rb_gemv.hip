@@ -553,14 +553,37 @@ int device_cu_count() {
   return cached[dev];
 }
 
-// The LUT path (M = 1) needs one 64-bit accumulator per row; the workspace is sized
-// for it whatever M is, so one workspace serves every batch size of a layer.
-size_t gemv_workspace_bytes(int, int64_t N, int64_t K, int64_t) { return lut_workspace_bytes(N, K); }
+// Batches of a few rows on the matrix cores: the MFMA kernel's time is nearly flat in M up to
+// 16 (4096x11008, k = 2: 17.3 us at M = 2 and 18.7 us at M = 16), while the nibble kernel
+// streams the planes once per activation row (6.3 us per row). Measured crossovers on
+// 4096x4096, 11008x4096, 4096x11008 (k = 1, 2) fall at M = 3..4, and at M = 2 on 28672x8192
+// (2^27 bits and more); with column scales h likewise. The kernel takes fp16 x, K a multiple
+// of 64, an even ldp, and h only as fp16 (16-byte aligned).
+static bool gemv_on_matrix_cores(int k, int64_t N, int64_t K, int64_t ldp, int64_t M, const void* h, rb_dtype x_dtype,
+                                 rb_dtype scale_dtype) {
+  if (M < 2 || x_dtype != RB_F16 || K % 64 != 0 || ldp % 2 != 0) return false;
+  if (K > (int64_t(1) << 22) || ldp > (int64_t(1) << 20)) return false;
+  if (h != nullptr && (scale_dtype != RB_F16 || (reinterpret_cast<uintptr_t>(h) & 15u) != 0)) return false;
+  return M >= 4 || (double)k * (double)N * (double)K >= 134217728.0;
+}
+
+// Workspace: first the LUT path's region (M = 1: one 64-bit accumulator per row; the general-h
+// chain's fp32 row sums), zero between calls; after it, for K a multiple of 64, the K-chunk
+// partial sums of the matrix-core kernel at M = 16 (written before they are read, so their
+// contents do not matter). Sized for M = 16 whatever M is asked for, so one workspace serves
+// every batch size of a layer.
+size_t gemv_workspace_bytes(int k, int64_t N, int64_t K, int64_t) {
+  return lut_workspace_bytes(N, K) + (K % 64 == 0 ? gemm_small_workspace_bytes(k, N, K, 16) : 0u);
+}
 
 hipError_t launch_gemv_variant(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                                const void* mu, int zero_one, rb_dtype scale_dtype, int k, int64_t N, int64_t K,
                                const void* x, rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,
                                hipStream_t s) {
+  if (mu == nullptr && !zero_one && ws != nullptr &&
+      gemv_on_matrix_cores(k, N, K, ldp, M, h, x_dtype, scale_dtype))
+    return launch_gemm_small(planes, ldp, g, h, scale_dtype, k, N, K, x, M, y, y_dtype,
+                             static_cast<char*>(ws) + lut_workspace_bytes(N, K), s);
   // one activation row, h = 1: the whole-row nibble-table kernel where it applies (fp16
   // data, k <= 2), else the byte-table kernel (plain product only) or the direct kernel
   if (M == 1 && h == nullptr && gemv_nib_fits(k, N, K, ldp, x_dtype, scale_dtype, y_dtype)) {

@@ -131,6 +131,20 @@ def test_workspace_too_small_is_reported():
             assert _prod(fn, k=k, N=N, K=K, M=M, ldp=ldp, ws=P, wsb=need - 1) == _lib.RB_ERR_WORKSPACE
 
 
+def test_gemv_workspace_holds_the_matrix_core_partials():
+    # K a multiple of 64: the LUT region (8 bytes per row, 256-byte multiple) and then the
+    # matrix-core kernel's K-chunk partials at M = 16, the same size for every M
+    for (k, N, K) in ((2, 4096, 11008), (1, 512, 4096), (2, 11008, 4096), (2, 28672, 8192)):
+        lut = (N * 8 + 255) // 256 * 256
+        gemm16 = L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, k, N, K, 16)
+        for M in (1, 2, 16):
+            assert L.rb_workspace_bytes(_lib.RB_OP_GEMV, k, N, K, M) == lut + gemm16
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 1, 512, 4096, 16) == 4 * 16 * 512 * 4
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 28672, 8192, 16) == 0   # no K split
+    # other K: the LUT region alone
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMV, 2, 300, 1000, 16) == (300 * 8 + 255) // 256 * 256
+
+
 def test_workspace_bytes_invalid_sizes():
     assert L.rb_workspace_bytes(_lib.RB_OP_GEMV, 0, 16, 16, 1) == 0
     assert L.rb_workspace_bytes(_lib.RB_OP_PACK, 2, 16, 16, 1) == 0

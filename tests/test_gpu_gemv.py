@@ -192,3 +192,63 @@ def test_gemv_general_h_fp16_small_batch(M):
     y = gpu_gemv(planes, g, h, x, K)
     y_ref, sabs = O.gemv(planes, g, h, x, K)
     assert_product_close(y, y_ref, sabs)
+
+
+@pytest.mark.parametrize("general_h", [False, True])
+@pytest.mark.parametrize("M", [2, 3, 4, 7, 16])
+def test_gemv_batches_on_both_sides_of_the_matrix_core_switch(M, general_h):
+    # fp16, K a multiple of 64, small planes: M = 2, 3 run as nibble passes per row, M >= 4 on
+    # the matrix cores (K split into chunks that meet in the workspace)
+    N, K, k = 300, 2048, 2
+    W = wl.heavy_tailed_weights(90 + M, N, K)
+    h = wl.random_scales(91, k, K, negative_frac=0.2, dtype=np.float16) if general_h else None
+    x = wl.activations(92 + M, M, K)
+    planes, g = oracle_case(W, k, h=h)
+    y = gpu_gemv(planes, g, h, x, K)
+    y_ref, sabs = O.gemv(planes, g, h, x, K)
+    assert_product_close(y, y_ref, sabs)
+
+
+def test_gemv_two_rows_on_large_planes_sampled():
+    # 28672 x 8192, k = 1 (2^27 bits and more): M = 2 already runs on the matrix cores; random
+    # planes and scales, the oracle on 256 sampled rows
+    N, K, k = 28672, 8192, 1
+    rng = np.random.default_rng(95)
+    planes = rng.integers(0, 2**32, size=(k, N, K // 32), dtype=np.uint32)
+    g = rng.uniform(0.005, 0.03, (k, N)).astype(np.float16)
+    x = wl.activations(96, 2, K)
+    y = rb.gemv(to_dev(planes), to_dev(g), None, to_dev(x), K).float().cpu().numpy()
+    rows = np.sort(rng.choice(N, 256, replace=False))
+    y_ref, sabs = O.gemv(planes[:, rows], g[:, rows].astype(np.float64), None, x, K)
+    assert_product_close(y[:, rows], y_ref, sabs)
+
+
+def test_gemv_matrix_core_batches_keep_the_lut_region_zero():
+    # a batch on the matrix cores writes its K-chunk partials after the region that the M = 1
+    # byte-table kernel (k = 3) and the general-h chain need zero; all three share one workspace
+    N, K = 512, 4096
+    W = wl.heavy_tailed_weights(97, N, K)
+    h = wl.random_scales(98, 2, K, dtype=np.float16)
+    x1 = wl.activations(99, 1, K)
+    x16 = wl.activations(100, 16, K)
+    p2, g2 = oracle_case(W, 2, h=h)
+    p3, g3 = oracle_case(W, 3)
+    g2d = to_dev(g2.reshape(2, N).astype(np.float16))
+    g3d = to_dev(g3.reshape(3, N).astype(np.float16))
+    ws = rb.workspace(rb.RB_OP_GEMV, 3, N, K, 1, device=dev())
+    lut = (N * 8 + 255) // 256 * 256
+    assert ws.numel() > lut                                  # the partials' region is there
+    for _ in range(2):
+        y16 = rb.gemv(to_dev(p3), g3d, None, to_dev(x16), K, ws=ws)
+        y16h = rb.gemv(to_dev(p2), g2d, to_dev(h), to_dev(x16), K, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws[:lut]) == 0
+        assert torch.count_nonzero(ws[lut:]) > 0            # the K chunks went through it
+        y3 = rb.gemv(to_dev(p3), g3d, None, to_dev(x1), K, ws=ws)
+        y2 = rb.gemv(to_dev(p2), g2d, to_dev(h), to_dev(x1), K, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws[:lut]) == 0
+        for y, p, g, hh, x in ((y16, p3, g3, None, x16), (y16h, p2, g2, h, x16), (y3, p3, g3, None, x1),
+                               (y2, p2, g2, h, x1)):
+            r, s = O.gemv(p, g, hh, x, K)
+            assert_product_close(y.float().cpu().numpy(), r, s)

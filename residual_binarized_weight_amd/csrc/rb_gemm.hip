@@ -154,10 +154,11 @@ __device__ __forceinline__ h8 expand_b(uint32_t nw, int t, int hh, u32x4g base) 
 }
 
 // KP = planes multiplied per pass (fold mode: all k; otherwise 1).
-// Stages run in groups of kDepth with no branch inside a group: the plane words of a
-// stage past the end (or past K in a 64-column tail) are whatever the row holds there,
-// and they meet activations that read as 0, so they add +-0 (a non-finite g, which no
-// finite W packs to, would turn that row's +-0 into NaN).
+// A group runs nch stages (group 0's count). The plane words of a stage past its half (or
+// past K in a 64-column tail) are whatever the row holds there, and they meet activations
+// that read as 0, so they add +-0 (a non-finite g, which no finite W packs to, would turn
+// that row's +-0 into NaN). Activations are fetched XD stages ahead: kDepth for one 32-row
+// batch tile, whose MFMAs per stage are too few to cover a load's latency, else 1.
 // NG wave groups per block (1 or 2). With two, MSPLIT: they take two halves of the batch,
 // else two halves of K. blockIdx.z splits K further into chunks of kz columns (a multiple of
 // the stage width) when the row and batch tiles alone would leave compute units idle; each
@@ -208,6 +209,7 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) yacc[mt] = (f32x16){};
 
+  constexpr int XD = MT == 1 ? kDepth : 1;  // activation stages in flight (divides kDepth)
   const int passes = MODE == kModeFold ? 1 : k;
   for (int pass = 0; pass < passes; ++pass) {
     const int i0 = MODE == kModeFold ? 0 : pass;
@@ -242,28 +244,30 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
     for (int d = 0; d < kDepth; ++d)
 #pragma unroll
       for (int p = 0; p < KP; ++p) wr[d][p] = buf_load16(rw[p], lane_off + 16u * d);
-    {
-      XStage<MT> xs0;
-      HStage hs0;
-      load_x_stage<MT>(xs0, rx, K, kend, kbeg, tid);
-      if (MODE == kModeH) load_h_stage(hs0, rh, kend, kbeg, tid);
-      __syncthreads();  // the previous pass may still read buffer 0
-      store_x_stage<MT>(xs0, xbuf0, tid);
-      if (MODE == kModeH) store_h_stage(hs0, hbuf0, tid);
-      __syncthreads();
+    // activation (and h) stages ride a ring of XD register slots: stage c sits in slot
+    // c % XD from its load, XD stages ahead, until it is written to LDS at the end of stage c-1
+    XStage<MT> xq[XD];
+    HStage hq[XD];
+#pragma unroll
+    for (int j = 0; j < XD; ++j) {
+      load_x_stage<MT>(xq[j], rx, K, kend, kbeg + (int64_t)j * kStageCols, tid);
+      if (MODE == kModeH) load_h_stage(hq[j], rh, kend, kbeg + (int64_t)j * kStageCols, tid);
     }
+    __syncthreads();  // the previous pass may still read buffer 0
+    store_x_stage<MT>(xq[0], xbuf0, tid);
+    if (MODE == kModeH) store_h_stage(hq[0], hbuf0, tid);
+    __syncthreads();
 
     for (int cb = 0; cb < nch; cb += kDepth) {
 #pragma unroll
       for (int d = 0; d < kDepth; ++d) {
         const int c = cb + d;
+        if (c >= nch) break;  // uniform: every wave of the block runs nch stages
         u32x4g cur[KP];
 #pragma unroll
         for (int p = 0; p < KP; ++p) cur[p] = wr[d][p];
-        XStage<MT> xn;
-        HStage hn;
-        load_x_stage<MT>(xn, rx, K, kend, kbeg + (int64_t)(c + 1) * kStageCols, tid);
-        if (MODE == kModeH) load_h_stage(hn, rh, kend, kbeg + (int64_t)(c + 1) * kStageCols, tid);
+        load_x_stage<MT>(xq[d % XD], rx, K, kend, kbeg + (int64_t)(c + XD) * kStageCols, tid);
+        if (MODE == kModeH) load_h_stage(hq[d % XD], rh, kend, kbeg + (int64_t)(c + XD) * kStageCols, tid);
 #pragma unroll
         for (int p = 0; p < KP; ++p) wr[d][p] = buf_load16(rw[p], lane_off + 16u * (uint32_t)(c + kDepth));
         // keep the loads at the top of the stage: they must be in flight during its MFMAs
@@ -303,8 +307,8 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        store_x_stage<MT>(xn, (d & 1) ? xbuf0 : xbuf1, tid);
-        if (MODE == kModeH) store_h_stage(hn, (d & 1) ? hbuf0 : hbuf1, tid);
+        store_x_stage<MT>(xq[(d + 1) % XD], (d & 1) ? xbuf0 : xbuf1, tid);
+        if (MODE == kModeH) store_h_stage(hq[(d + 1) % XD], (d & 1) ? hbuf0 : hbuf1, tid);
         __syncthreads();
       }
     }
@@ -396,6 +400,22 @@ int64_t gemm_k_chunk(int64_t K, int z) {
   return ((stages + z - 1) / z) * kStageCols;
 }
 
+// Fewer chunks when the grid would not fit the blocks resident at once: tiles * z0 blocks
+// beyond `slots` (compute units times the blocks one unit holds) run in a second round, so
+// the count with the smallest rounds / z wins (86 row tiles at one block per unit: 3 chunks
+// make 258 blocks and two rounds, 2 chunks 172 blocks and one). Never more than z0, which
+// sizes the workspace.
+int gemm_fit_split(int z0, int64_t tiles, int64_t slots) {
+  if (slots < 1) slots = 1;
+  int best = z0;
+  double best_cost = (double)((tiles * z0 + slots - 1) / slots) / z0;
+  for (int z = z0 - 1; z >= 1; --z) {
+    const double c = (double)((tiles * z + slots - 1) / slots) / z;
+    if (c < best_cost) { best = z; best_cost = c; }
+  }
+  return best;
+}
+
 template <int MT, int NG>
 constexpr size_t gemm_lds_bytes() {
   return (size_t)NG * (2 * MT * 32 * kRowBytes + 512);
@@ -406,16 +426,21 @@ hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const 
                       int64_t K, const void* x, int64_t M, void* y, float* ws, hipStream_t s) {
   constexpr size_t lds = gemm_lds_bytes<MT, NG>();
   static bool attr_set = false;  // per instantiation
+  static int per_cu = 1;          // blocks of this instantiation one compute unit holds at once
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const void* fn = (const void*)gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT>;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kGemmGroupThreads * NG, lds) == hipSuccess && nb > 0)
+      per_cu = nb;
     attr_set = true;
   }
   const int64_t m_per_block = (int64_t)32 * MT * (MSPLIT ? NG : 1);
   const unsigned gx = (unsigned)((N + kGemmTileN - 1) / kGemmTileN);
   const unsigned gy = (unsigned)((M + m_per_block - 1) / m_per_block);
-  const int nz = gemm_k_split(N, K, M, MODE == kModeH);
+  int nz = gemm_k_split(N, K, M, MODE == kModeH);
+  if (nz > 1) nz = gemm_fit_split(nz, (int64_t)gx * gy, (int64_t)device_cu_count() * per_cu);
   const int64_t kz = nz > 1 ? gemm_k_chunk(K, nz) : K;
   float* part = nz > 1 ? ws : nullptr;
   gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT><<<dim3(gx, gy, (unsigned)nz), kGemmGroupThreads * NG, lds, s>>>(

@@ -360,13 +360,20 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
   }
 }
 
-// y[m][n] = sum over the z chunks of part[z][m][n], in chunk order
+// y[m][n] = sum over the z chunks of part[z][m][n], in chunk order. All nz (<= kMaxChunks)
+// loads are issued before the first add, so their latencies overlap.
+constexpr int kMaxChunks = 16;
 template <typename TY>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int64_t MN, int nz,
                                                           TY* __restrict__ y) {
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += (int64_t)gridDim.x * 256) {
+    float v[kMaxChunks];
+#pragma unroll
+    for (int z = 0; z < kMaxChunks; ++z) v[z] = z < nz ? part[(int64_t)z * MN + e] : 0.0f;
     float s = 0.0f;
-    for (int z = 0; z < nz; ++z) s += part[(int64_t)z * MN + e];
+#pragma unroll
+    for (int z = 0; z < kMaxChunks; ++z)
+      if (z < nz) s += v[z];
     gemm_store<TY>(&y[e], s);
   }
 }
@@ -390,7 +397,7 @@ int gemm_k_split(int64_t N, int64_t K, int64_t M, int mode_h) {
   int64_t z = (256 + tiles - 1) / tiles;
   const int64_t zmax = K / (8 * kStageCols);
   if (z > zmax) z = zmax;
-  if (z > 16) z = 16;
+  if (z > kMaxChunks) z = kMaxChunks;
   return z < 1 ? 1 : (int)z;
 }
 

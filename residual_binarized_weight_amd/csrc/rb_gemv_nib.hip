@@ -72,14 +72,19 @@ constexpr uint32_t kNibBuf = 65536u;
 // multiplies the activations by that plane's column scales h before the tables are built and
 // chains the passes of k planes through an fp32 row sum: acc_mode bit 0 adds the sum of the
 // passes before (acc_io[n]), bit 1 writes the sum for the next pass instead of y (the last
-// pass zeroes acc_io[n] after reading it); 0 is the plain product.
+// pass zeroes acc_io[n] after reading it); bit 3 (with bit 2 and KP = 2) runs both planes in
+// one pass instead, plane 0's phases and then plane 1's, each phase's tables built from x times
+// the column scales of its plane (two sums S, no chaining); 0 is the plain product.
 template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int WV, int VAR>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, int64_t N, int64_t K,
     const TX* __restrict__ x, TY* __restrict__ y, const TS* __restrict__ mu, int zero_one,
     const TX* __restrict__ hrow, float* __restrict__ acc_io, int acc_mode) {
   extern __shared__ __align__(16) uint8_t lds[];
-  float* red = reinterpret_cast<float*>(lds + (NPH == 1 ? 1 : 2) * kNibBuf);  // after the table buffers
+  constexpr bool kSeq = (VAR & 8) != 0;
+  static_assert(!kSeq || (KP == 2 && (VAR & 4) != 0), "planes in sequence: two planes with column scales");
+  constexpr int NV = kSeq ? 2 * NPH : NPH;  // phases run (plane 1's after plane 0's)
+  float* red = reinterpret_cast<float*>(lds + (NV == 1 ? 1 : 2) * kNibBuf);  // after the table buffers
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -131,6 +136,8 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   // h mode: this plane's column scales, in the same pattern as the activations
   typename NibX<TX>::raw h0[kTB0];
   typename NibX<TX>::raw hr[NPH];
+  typename NibX<TX>::raw h10[kTB0];  // planes in sequence: plane 1's column scales (else unused)
+  typename NibX<TX>::raw h1r[NPH];
   if constexpr ((VAR & 4) != 0) {
     const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(hrow, (uint32_t)((uint64_t)((K * sizeof(TX) + 3) & ~3ull)));
     if (b0) {
@@ -140,6 +147,18 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
     }
 #pragma unroll
     for (int p = 1; p < NPH; ++p) hr[p] = NibX<TX>::load(rh, (uint32_t)(p * kNibTables + tid) * NibX<TX>::bytes);
+    if constexpr (kSeq) {
+      const __amdgpu_buffer_rsrc_t rh1 =
+          buffer_rsrc(hrow + K, (uint32_t)((uint64_t)((K * sizeof(TX) + 3) & ~3ull)));
+      if (b0) {
+#pragma unroll
+        for (int b = 0; b < kTB0; ++b)
+          h10[b] = NibX<TX>::load(rh1, (uint32_t)(b * kB0Threads + tid) * NibX<TX>::bytes);
+      }
+#pragma unroll
+      for (int p = 1; p < NPH; ++p)
+        h1r[p] = NibX<TX>::load(rh1, (uint32_t)(p * kNibTables + tid) * NibX<TX>::bytes);
+    }
   }
   // activations first, in every wave: requests return in order, and the table build must not
   // queue behind the weight stream
@@ -187,9 +206,9 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   }
   const uint32_t lh4 = (uint32_t)(lane >> 3) * 0x01010101u;
 
-  float xs = 0.0f;  // this thread's share of sum x
-  // table q of phase p into buffer p % 2, from the 4 activations in `raw`
-  auto build_one = [&](int p, uint32_t q, typename NibX<TX>::raw raw, typename NibX<TX>::raw hraw) {
+  float xs = 0.0f;  // this thread's share of sum x (of the current plane's x h in sequence)
+  // table q of phase p (run as phase vp) into buffer vp % 2, from the 4 activations in `raw`
+  auto build_one = [&](int vp, int p, uint32_t q, typename NibX<TX>::raw raw, typename NibX<TX>::raw hraw) {
     typedef __attribute__((address_space(3))) float lds_f32p;
     const uint32_t Q = (uint32_t)(p * kNibTables) + q;
     float xv[4];
@@ -202,12 +221,12 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
     xs += (xv[0] + xv[1]) + (xv[2] + xv[3]);
     const uint32_t w = q >> 3, i = q & 7;
     const uint32_t slot = 8u * w + (i ^ (((w >> 2) ^ ((w >> 5) & 1u)) & 7u));
-    const uint32_t base = (uint32_t)(p & 1) * kNibBuf + slot * 4u;
+    const uint32_t base = (uint32_t)(vp & 1) * kNibBuf + slot * 4u;
     const float lo[4] = {0.0f, xv[0], xv[1], xv[0] + xv[1]};
     const float hi[4] = {0.0f, xv[2], xv[3], xv[2] + xv[3]};
     // entry 0 is 0 for every table: written by each buffer's first build only. Tables wholly
     // past K are read only at entry 0 (their words are 0), so they need no other entry.
-    if (p < 2) *(lds_f32p*)(size_t)base = 0.0f;
+    if (vp < 2) *(lds_f32p*)(size_t)base = 0.0f;
     if (4u * Q < Kc) {
 #pragma unroll
       for (int e = 1; e < 16; ++e) {
@@ -218,19 +237,28 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   };
   // phase p's tables: phase 0 by the first waves (their activations arrive first: the
   // memory returns to a block's waves in launch order), later phases one per thread
-  auto build = [&](int p) {
+  auto build = [&](int vp) {
+    const int p = kSeq ? vp % NPH : vp;
+    const bool second = kSeq && vp >= NPH;  // plane 1's phase
     if (p == 0) {
       if (b0) {
 #pragma unroll
-        for (int b = 0; b < kTB0; ++b) build_one(0, (uint32_t)(b * kB0Threads + tid), x0[b], h0[b]);
+        for (int b = 0; b < kTB0; ++b) {
+          typename NibX<TX>::raw hb = h0[b];
+          if constexpr (kSeq) hb = second ? h10[b] : hb;
+          build_one(vp, 0, (uint32_t)(b * kB0Threads + tid), x0[b], hb);
+        }
       }
     } else {
-      build_one(p, (uint32_t)tid, xr[p], hr[p]);
+      typename NibX<TX>::raw hp = hr[p];
+      if constexpr (kSeq) hp = second ? h1r[p] : hp;
+      build_one(vp, p, (uint32_t)tid, xr[p], hp);
     }
     if (p == NPH - 1) {
       // every column has been seen: publish this wave's share of sum x (a barrier follows)
       const float xw = wave_sum_dpp(xs);
-      if (lane == 63) red[wave] = xw;
+      if (lane == 63) red[(second ? WV : 0) + wave] = xw;
+      if constexpr (kSeq) xs = 0.0f;
     }
   };
 
@@ -245,9 +273,10 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int p = 0; p < NPH; ++p) {
+  for (int vp = 0; vp < NV; ++vp) {
+    const int p = kSeq ? vp % NPH : vp;
     // 3. the next phase's tables (activations only: no wait on the weight stream)
-    if (p + 1 < NPH) build(p + 1);
+    if (vp + 1 < NV) build(vp + 1);
     __builtin_amdgcn_sched_barrier(0);
     // 4. lookups in this phase's buffer: one LDS read per 4 weight bits. A lane past the row's
     // last word holds 0 (its load was out of range) and reads entry 0, which is 0 in every
@@ -260,9 +289,10 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
         if (p == NPH - 1 && (uint32_t)(kNibPhaseWords * p + 64 * j) >= Kw) continue;
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
+          if (kSeq && i != vp / NPH) continue;  // in sequence: this phase's plane only
           const uint32_t w = wd[r][p][j][i];
           const uint32_t o = 2048u * (uint32_t)j;
-          const uint32_t* c = cb[p & 1];
+          const uint32_t* c = cb[vp & 1];
           const uint32_t ev = ((w << 4) & 0xf0f0f0f0u) | lh4;  // byte m: nibble 2 m
           const uint32_t od = (w & 0xf0f0f0f0u) | lh4;         // byte m: nibble 2 m + 1
           // selector: byte 0 <- c byte 0, byte 1 <- word byte m, byte 2 <- c byte 2, byte 3 <- 0
@@ -275,7 +305,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
         }
       }
     // the next phase's tables are complete, and this phase's buffer is free for phase p + 2
-    if (p + 1 < NPH) {
+    if (vp + 1 < NV) {
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
@@ -287,13 +317,20 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(1, 4)))
   float S = 0.0f;
 #pragma unroll
   for (int w = 0; w < WV; ++w) S += red[w];
+  float S1 = 0.0f;  // in sequence: plane 1's sum of x h
+  if constexpr (kSeq) {
+#pragma unroll
+    for (int w = 0; w < WV; ++w) S1 += red[WV + w];
+  }
   constexpr float ta = (VAR & 1) != 0 ? 1.0f : 2.0f;
   const float ts = (VAR & 1) != 0 ? 0.0f : S;
+  const float ts1 = (VAR & 1) != 0 ? 0.0f : S1;
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     float v = 0.0f;
 #pragma unroll
-    for (int i = 0; i < KP; ++i) v += NibScale<TS>::f32(gr[r][i]) * (ta * wave_sum_dpp(acc[r][i]) - ts);
+    for (int i = 0; i < KP; ++i)
+      v += NibScale<TS>::f32(gr[r][i]) * (ta * wave_sum_dpp(acc[r][i]) - (kSeq && i == 1 ? ts1 : ts));
     if (lane == 63 && n0 + r < N) {
       if constexpr ((VAR & 2) != 0) v += NibScale<TS>::f32(mr[r]) * S;
       if constexpr ((VAR & 4) != 0) {
@@ -323,8 +360,10 @@ struct NibExtra {
 template <typename TX, typename TS, typename TY, int KP, int NPH, int RW, int VAR, int WV = kNibWaves>
 hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
                             const void* x, void* y, const NibExtra& ex, hipStream_t s) {
-  // one phase needs one table buffer (two blocks fit on a compute unit), more need two
-  constexpr size_t lds = (NPH == 1 ? 1 : 2) * (size_t)kNibBuf + 64;
+  // one phase needs one table buffer (two blocks fit on a compute unit), more need two; the
+  // block's sums of x (one per plane in sequence) follow the buffers
+  constexpr int NV = (VAR & 8) != 0 ? 2 * NPH : NPH;
+  constexpr size_t lds = (NV == 1 ? 1 : 2) * (size_t)kNibBuf + ((VAR & 8) != 0 ? 128 : 64);
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib_kernel<TX, TS, TY, KP, NPH, RW, WV, VAR>,
@@ -341,13 +380,15 @@ hipError_t launch_nib_shape(const uint32_t* planes, int64_t ldp, const void* g, 
 
 // rows per wave: the smallest count that puts at most one block on each compute unit, up
 // to the most whose plane words still fit in registers next to the lookups' temporaries at
-// 16 waves per block (larger counts spill)
-constexpr int nib_max_rows(int kp, int nph) { return kp == 1 ? (nph <= 3 ? 3 : 2) : (nph == 1 ? 3 : nph <= 3 ? 2 : 1); }
+// 16 waves per block (larger counts spill; planes in sequence hold both planes' scales too)
+constexpr int nib_max_rows(int kp, int nph, bool seq) {
+  return seq ? (nph == 1 ? 3 : nph == 2 ? 2 : 1) : kp == 1 ? (nph <= 3 ? 3 : 2) : (nph == 1 ? 3 : nph <= 3 ? 2 : 1);
+}
 
 template <typename TX, typename TS, typename TY, int KP, int NPH, int VAR>
 hipError_t launch_nib_rows(int rw, const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
                            const void* x, void* y, const NibExtra& ex, hipStream_t s) {
-  constexpr int kMax = nib_max_rows(KP, NPH);
+  constexpr int kMax = nib_max_rows(KP, NPH, (VAR & 8) != 0);
   if (rw > kMax) rw = kMax;
   if constexpr (kMax >= 3) {
     if (rw == 3) return launch_nib_shape<TX, TS, TY, KP, NPH, 3, VAR>(planes, ldp, g, N, K, x, y, ex, s);
@@ -390,6 +431,9 @@ hipError_t launch_nib_var(const uint32_t* planes, int64_t ldp, const void* g, in
       if constexpr (KP == 1) {  // h mode: one plane per pass, no row offset
         if (var == 4) return launch_nib_kp<__half, __half, __half, 1, 4>(planes, ldp, g, N, K, x, y, ex, s);
         if (var == 5) return launch_nib_kp<__half, __half, __half, 1, 5>(planes, ldp, g, N, K, x, y, ex, s);
+      } else {  // two planes with h: in sequence in one pass
+        if (var == 4) return launch_nib_kp<__half, __half, __half, 2, 12>(planes, ldp, g, N, K, x, y, ex, s);
+        if (var == 5) return launch_nib_kp<__half, __half, __half, 2, 13>(planes, ldp, g, N, K, x, y, ex, s);
       }
       return hipErrorNotSupported;
   }
@@ -438,6 +482,12 @@ bool gemv_nib_h_fits(int k, int64_t N, int64_t K, int64_t ldp, const void* h, rb
 
 hipError_t launch_gemv_nib_h(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
                              int64_t K, const void* x, void* y, int zero_one, float* acc, hipStream_t s) {
+  if (k == 2) {  // both planes in one pass (h_1 follows h_0 at h + K); acc is not used
+    NibExtra ex;
+    ex.zero_one = zero_one;
+    ex.h = h;
+    return launch_nib_var<2>(planes, ldp, g, N, K, x, y, ex, s);
+  }
   for (int i = 0; i < k; ++i) {
     NibExtra ex;
     ex.zero_one = zero_one;

@@ -252,3 +252,25 @@ def test_gemv_matrix_core_batches_keep_the_lut_region_zero():
                                (y2, p2, g2, h, x1)):
             r, s = O.gemv(p, g, hh, x, K)
             assert_product_close(y.float().cpu().numpy(), r, s)
+
+
+@pytest.mark.parametrize("zero_one", [False, True])
+@pytest.mark.parametrize("N,K", [(11008, 4096), (5000, 8200), (777, 4100), (33, 12000), (4096, 11008)])
+def test_gemv_two_planes_with_h_in_one_pass(N, K, zero_one):
+    # k = 2 with fp16 column scales at M = 1: both planes in one nibble pass, plane 1's phases
+    # after plane 0's (3, 2 and 1 rows per wave; 1 to 3 phases, ragged N, a short last phase);
+    # random planes and scales, the oracle on up to 300 sampled rows
+    k = 2
+    rng = np.random.default_rng(N + K)
+    planes = rng.integers(0, 2**32, size=(k, N, (K + 31) // 32), dtype=np.uint32)
+    if K % 32:
+        planes[:, :, -1] &= np.uint32((1 << (K % 32)) - 1)
+    g = rng.uniform(0.005, 0.03, (k, N)).astype(np.float16)
+    h = wl.random_scales(N, k, K, negative_frac=0.2, dtype=np.float16)
+    x = wl.activations(K, 1, K)
+    y = rb.gemv_variant(to_dev(planes), to_dev(g), to_dev(h), to_dev(x), K, zero_one=zero_one)
+    torch.cuda.synchronize()
+    rows = np.arange(N) if N <= 300 else np.sort(rng.choice(N, 300, replace=False))
+    y_ref, sabs = O.gemv_variant(planes[:, rows], g[:, rows].astype(np.float64), h.astype(np.float64), None,
+                                 x.astype(np.float64), K, zero_one)
+    assert_product_close(y.float().cpu().numpy()[:, rows], y_ref, sabs)

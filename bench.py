@@ -647,8 +647,8 @@ def main() -> int:
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs the decode product on one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not run)"}))
+        print(json.dumps({"error": "the product runs on one GPU here; --gpus must be 1 "
+                                   "(a row-sharded multi-GPU layout is not implemented)"}))
         return 2
 
     import numpy as np

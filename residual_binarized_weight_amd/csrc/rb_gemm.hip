@@ -175,11 +175,12 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
   const int grp = NG == 1 ? 0 : wave_all / kGemmWaves;  // group of this wave
   const int wave = wave_all % kGemmWaves;   // wave within its group
   const int tid = tid_all % kGemmGroupThreads;
-  uint8_t* const gbase = smem + grp * (2 * MT * 32 * kRowBytes + 512);
+  constexpr int NH = MODE == kModeH ? KP : 1;  // h mode: one h stage and one accumulator per plane
+  uint8_t* const gbase = smem + grp * (2 * MT * 32 * kRowBytes + 512 * NH);
   uint8_t* const xbuf0 = gbase;
   uint8_t* const xbuf1 = gbase + MT * 32 * kRowBytes;
-  uint8_t* const hbuf0 = gbase + 2 * MT * 32 * kRowBytes;
-  uint8_t* const hbuf1 = hbuf0 + 256;
+  uint8_t* const hbuf0 = gbase + 2 * MT * 32 * kRowBytes;  // plane q's h stage at + 256 q
+  uint8_t* const hbuf1 = hbuf0 + 256 * NH;
 
   const int nl = lane & 31;
   const int hh = lane >> 5;
@@ -210,9 +211,9 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
   for (int mt = 0; mt < MT; ++mt) yacc[mt] = (f32x16){};
 
   constexpr int XD = MT == 1 ? kDepth : 1;  // activation stages in flight (divides kDepth)
-  const int passes = MODE == kModeFold ? 1 : k;
+  const int passes = MODE == kModeFold ? 1 : k / KP;
   for (int pass = 0; pass < passes; ++pass) {
-    const int i0 = MODE == kModeFold ? 0 : pass;
+    const int i0 = MODE == kModeFold ? 0 : pass * KP;
     __amdgpu_buffer_rsrc_t rw[KP];
     u32x4g base[KP];
     uint32_t gsgn[KP];
@@ -232,11 +233,15 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
         gsgn[p] = 0u;
       }
     }
-    const __amdgpu_buffer_rsrc_t rh = gemm_rsrc(MODE == kModeH ? h + (int64_t)i0 * K : x, K * 2);
-
-    f32x16 acc[MT];
+    __amdgpu_buffer_rsrc_t rh[NH];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x16){};
+    for (int q = 0; q < NH; ++q) rh[q] = gemm_rsrc(MODE == kModeH ? h + (int64_t)(i0 + q) * K : x, K * 2);
+
+    f32x16 acc[NH][MT];
+#pragma unroll
+    for (int q = 0; q < NH; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[q][mt] = (f32x16){};
 
     // prologue: plane words of stages 0 .. kDepth-1, activation stage 0
     u32x4g wr[kDepth][KP];
@@ -247,15 +252,21 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
     // activation (and h) stages ride a ring of XD register slots: stage c sits in slot
     // c % XD from its load, XD stages ahead, until it is written to LDS at the end of stage c-1
     XStage<MT> xq[XD];
-    HStage hq[XD];
+    HStage hq[XD][NH];
 #pragma unroll
     for (int j = 0; j < XD; ++j) {
       load_x_stage<MT>(xq[j], rx, K, kend, kbeg + (int64_t)j * kStageCols, tid);
-      if (MODE == kModeH) load_h_stage(hq[j], rh, kend, kbeg + (int64_t)j * kStageCols, tid);
+      if (MODE == kModeH) {
+#pragma unroll
+        for (int q = 0; q < NH; ++q) load_h_stage(hq[j][q], rh[q], kend, kbeg + (int64_t)j * kStageCols, tid);
+      }
     }
     __syncthreads();  // the previous pass may still read buffer 0
     store_x_stage<MT>(xq[0], xbuf0, tid);
-    if (MODE == kModeH) store_h_stage(hq[0], hbuf0, tid);
+    if (MODE == kModeH) {
+#pragma unroll
+      for (int q = 0; q < NH; ++q) store_h_stage(hq[0][q], hbuf0 + 256 * q, tid);
+    }
     __syncthreads();
 
     for (int cb = 0; cb < nch; cb += kDepth) {
@@ -267,7 +278,11 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
 #pragma unroll
         for (int p = 0; p < KP; ++p) cur[p] = wr[d][p];
         load_x_stage<MT>(xq[d % XD], rx, K, kend, kbeg + (int64_t)(c + XD) * kStageCols, tid);
-        if (MODE == kModeH) load_h_stage(hq[d % XD], rh, kend, kbeg + (int64_t)(c + XD) * kStageCols, tid);
+        if (MODE == kModeH) {
+#pragma unroll
+          for (int q = 0; q < NH; ++q)
+            load_h_stage(hq[d % XD][q], rh[q], kend, kbeg + (int64_t)(c + XD) * kStageCols, tid);
+        }
 #pragma unroll
         for (int p = 0; p < KP; ++p) wr[d][p] = buf_load16(rw[p], lane_off + 16u * (uint32_t)(c + kDepth));
         // keep the loads at the top of the stage: they must be in flight during its MFMAs
@@ -294,32 +309,39 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
               for (int mt = 0; mt < MT; ++mt)
                 anext[mt] = *reinterpret_cast<const h8*>(xb + (mt * 32 + nl) * kRowBytes + rn * 16);
             }
-            u32x4g hbase = base[0];
-            if (MODE == kModeH) hbase = *reinterpret_cast<const u32x4g*>(hb + r * 16);
 #pragma unroll
             for (int p = 0; p < KP; ++p) {
+              u32x4g bp = base[p];
+              if (MODE == kModeH) bp = *reinterpret_cast<const u32x4g*>(hb + 256 * p + r * 16);
               const uint32_t nwd = ~cur[p][w] ^ gsgn[p];
-              const h8 b = expand_b<MODE>(nwd, t, hh, MODE == kModeH ? hbase : base[p]);
+              const h8 b = expand_b<MODE>(nwd, t, hh, bp);
+              const int q = MODE == kModeH ? p : 0;  // fold and ones modes: one sum
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt], b, acc[mt], 0, 0, 0);
+                acc[q][mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt], b, acc[q][mt], 0, 0, 0);
             }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
         store_x_stage<MT>(xq[(d + 1) % XD], (d & 1) ? xbuf0 : xbuf1, tid);
-        if (MODE == kModeH) store_h_stage(hq[(d + 1) % XD], (d & 1) ? hbuf0 : hbuf1, tid);
+        if (MODE == kModeH) {
+#pragma unroll
+          for (int q = 0; q < NH; ++q) store_h_stage(hq[(d + 1) % XD][q], ((d & 1) ? hbuf0 : hbuf1) + 256 * q, tid);
+        }
         __syncthreads();
       }
     }
 
     if (MODE == kModeFold) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) yacc[mt] = acc[mt];
+      for (int mt = 0; mt < MT; ++mt) yacc[mt] = acc[0][mt];
     } else {
-      const float gi = scale_f32<TS>(g + (int64_t)i0 * N + nc);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) yacc[mt] += gi * acc[mt];
+      for (int q = 0; q < NH; ++q) {  // planes in order, as one pass per plane would add them
+        const float gi = scale_f32<TS>(g + (int64_t)(i0 + q) * N + nc);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) yacc[mt] += gi * acc[q][mt];
+      }
     }
   }
 
@@ -423,15 +445,15 @@ int gemm_fit_split(int z0, int64_t tiles, int64_t slots) {
   return best;
 }
 
-template <int MT, int NG>
+template <int MT, int NG, int NH>
 constexpr size_t gemm_lds_bytes() {
-  return (size_t)NG * (2 * MT * 32 * kRowBytes + 512);
+  return (size_t)NG * (2 * MT * 32 * kRowBytes + 512 * NH);
 }
 
 template <typename TS, typename TY, int MT, int MODE, int KP, int NG, bool MSPLIT>
 hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
                       int64_t K, const void* x, int64_t M, void* y, float* ws, hipStream_t s) {
-  constexpr size_t lds = gemm_lds_bytes<MT, NG>();
+  constexpr size_t lds = gemm_lds_bytes<MT, NG, MODE == kModeH ? KP : 1>();
   static bool attr_set = false;  // per instantiation
   static int per_cu = 1;          // blocks of this instantiation one compute unit holds at once
   if (!attr_set) {
@@ -480,6 +502,10 @@ hipError_t launch_mt(const uint32_t* planes, int64_t ldp, const void* g, const v
 template <typename TY>
 hipError_t launch_y(rb_dtype scale_dtype, const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                     int k, int64_t N, int64_t K, const void* x, int64_t M, void* y, float* ws, hipStream_t s) {
+  // h mode, one 32-row batch tile, even k: two planes per sweep of K (the activation stages and
+  // the start-up shared), each with its own accumulator
+  if (h != nullptr && M <= 32 && k % 2 == 0)
+    return launch_one<__half, TY, 1, kModeH, 2, 2, false>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   if (h != nullptr) return launch_mt<__half, TY, kModeH, 1>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   if (scale_dtype == RB_F32) return launch_mt<float, TY, kModeOnes, 1>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   switch (k) {

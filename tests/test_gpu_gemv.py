@@ -274,3 +274,18 @@ def test_gemv_two_planes_with_h_in_one_pass(N, K, zero_one):
     y_ref, sabs = O.gemv_variant(planes[:, rows], g[:, rows].astype(np.float64), h.astype(np.float64), None,
                                  x.astype(np.float64), K, zero_one)
     assert_product_close(y.float().cpu().numpy()[:, rows], y_ref, sabs)
+
+
+@pytest.mark.parametrize("fmt,general_h,y_dtype", [("f32", False, torch.float32), ("f32", False, torch.float16),
+                                                    ("f16", True, torch.float32), ("f16", False, torch.float32)])
+def test_gemv_matrix_core_batches_other_dtypes(fmt, general_h, y_dtype):
+    # batches on the matrix cores with fp32 row scales (one accumulator per plane, g applied in
+    # fp32), fp16 h, and fp32 outputs
+    N, K, k, M = 200, 3072, 2, 8
+    W = wl.heavy_tailed_weights(110, N, K)
+    h = wl.random_scales(111, k, K, negative_frac=0.2, dtype=np.float16) if general_h else None
+    x = wl.activations(112, M, K)
+    planes, g = oracle_case(W, k, h=h, fmt=fmt)
+    y = gpu_gemv(planes, g, h, x, K, y_dtype=y_dtype, fmt=fmt)
+    y_ref, sabs = O.gemv(planes, g, h, x, K)
+    assert_product_close(y, y_ref, sabs, fp16_out=y_dtype == torch.float16)

@@ -40,7 +40,7 @@ constexpr int kGemmTileN = 32 * kGemmWaves;     // weight rows per block
 constexpr int kStageCols = 128;                 // columns per stage: 4 words per plane row
 constexpr int kStageWords = kStageCols / 32;
 constexpr int kRowBytes = kStageCols * 2 + 16;  // 16 groups of 16 B + pad
-constexpr int kDepth = 4;                       // plane-word prefetch distance in stages
+constexpr int kDepth = 2;                       // plane-word prefetch distance in stages
 
 enum { kModeFold = 0, kModeOnes = 1, kModeH = 2 };
 

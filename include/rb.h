@@ -134,7 +134,7 @@ rb_status rb_pack(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, int64_t
  *   ws, ws_bytes  device workspace of at least rb_workspace_bytes(RB_OP_GEMV, k, N, K, M)
  *                 bytes (the same for every M), zero-filled once after allocation; its first
  *                 part is left zero by every call, the rest holds per-call partial sums
- *   A batch of M >= 4 rows (M >= 2 when k*N*K >= 2^27) with fp16 x, K a multiple of 64, an
+ *   A batch of M >= 4 rows (M = 3 when K >= 2N; M >= 2 when k*N*K >= 2^27) with fp16 x, K a multiple of 64, an
  *   even ldp and h NULL or fp16 and 16-byte aligned is computed as rb_gemm_small computes it
  *   (on the matrix cores, fp32 accumulation); other calls on the vector units. Either way
  *   the result meets the same bound against the exact product.

@@ -197,8 +197,8 @@ def test_gemv_general_h_fp16_small_batch(M):
 @pytest.mark.parametrize("general_h", [False, True])
 @pytest.mark.parametrize("M", [2, 3, 4, 7, 16])
 def test_gemv_batches_on_both_sides_of_the_matrix_core_switch(M, general_h):
-    # fp16, K a multiple of 64, small planes: M = 2, 3 run as nibble passes per row, M >= 4 on
-    # the matrix cores (K split into chunks that meet in the workspace)
+    # fp16, K a multiple of 64, small planes: M = 2 runs as nibble passes per row, M >= 3 (K >= 2 N)
+    # on the matrix cores (K split into chunks that meet in the workspace)
     N, K, k = 300, 2048, 2
     W = wl.heavy_tailed_weights(90 + M, N, K)
     h = wl.random_scales(91, k, K, negative_frac=0.2, dtype=np.float16) if general_h else None
@@ -289,3 +289,16 @@ def test_gemv_matrix_core_batches_other_dtypes(fmt, general_h, y_dtype):
     y = gpu_gemv(planes, g, h, x, K, y_dtype=y_dtype, fmt=fmt)
     y_ref, sabs = O.gemv(planes, g, h, x, K)
     assert_product_close(y, y_ref, sabs, fp16_out=y_dtype == torch.float16)
+
+
+@pytest.mark.parametrize("general_h", [False, True])
+def test_gemv_three_rows_when_n_exceeds_k_half(general_h):
+    # M = 3 with K < 2 N stays on the nibble passes (one per row)
+    N, K, k, M = 700, 1024, 2, 3
+    W = wl.heavy_tailed_weights(120, N, K)
+    h = wl.random_scales(121, k, K, negative_frac=0.2, dtype=np.float16) if general_h else None
+    x = wl.activations(122, M, K)
+    planes, g = oracle_case(W, k, h=h)
+    y = gpu_gemv(planes, g, h, x, K)
+    y_ref, sabs = O.gemv(planes, g, h, x, K)
+    assert_product_close(y, y_ref, sabs)

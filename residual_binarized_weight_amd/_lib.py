@@ -53,7 +53,6 @@ SIGNATURES = {
                                        ctypes.c_int, _i64, _vp, _i64, _vp, ctypes.c_int, _i64, _vp]),
     # streaming-read probe used by the bench (not part of the method)
     "rb_bench_stream_read": (ctypes.c_int, [_vp, _i64, _vp, _i32, _vp]),
-    "rb_bench_spin": (ctypes.c_int, [ctypes.c_double, _vp]),
     "rb_bench_gather": (ctypes.c_int, [_vp, ctypes.c_uint32, _i32, _vp, _i32, _vp]),
 }
 

@@ -201,8 +201,9 @@ def binarize(W: np.ndarray, k: int, h: np.ndarray | None = None, scale_fmt: str 
     rounding of a tie-ambiguous scale.
 
     Returns a dict with planes (k, N, ceil(K/32)) uint32, g (k, N, G) float64 holding
-    values of ``scale_fmt``, ambiguous (k, N, G) bool, and the residual row norms
-    ||R_i||_2 for i = 0..k as ``res_norm`` (k+1, N).
+    values of ``scale_fmt``, ambiguous (k, N, G) bool, the unrounded quotients as
+    float64 (k, N, G) ``quot`` (which side of the stored scale the exact value lies on),
+    and the residual row norms ||R_i||_2 for i = 0..k as ``res_norm`` (k+1, N).
     """
     if not np.all(np.isfinite(W)):
         raise ValueError("W holds NaN or Inf")
@@ -215,6 +216,7 @@ def binarize(W: np.ndarray, k: int, h: np.ndarray | None = None, scale_fmt: str 
     planes = np.zeros((k, N, Kw), dtype=np.uint32)
     g = np.zeros((k, N, G), dtype=np.float64)
     amb = np.zeros((k, N, G), dtype=bool)
+    quot64 = np.zeros((k, N, G), dtype=np.float64)
     res_norm = np.zeros((k + 1, N), dtype=np.float64)
     res_norm[0] = np.sqrt(np.sum(R * R, axis=1))
     for i in range(k):
@@ -238,11 +240,12 @@ def binarize(W: np.ndarray, k: int, h: np.ndarray | None = None, scale_fmt: str 
                 else:
                     amb[i, n, q] = quot != 0 and midpoint_distance(quot, scale_fmt) <= tie_tolerance(c1 - c0)
                 g[i, n, q] = gv
+                quot64[i, n, q] = float(quot)
                 g_col[n, c0:c1] = gv
         # W_i = g (.) B (.) h ; g*h is exact in float64 (<= 48 significant bits), *B exact.
         R = R - (g_col * hi[None, :]) * B
         res_norm[i + 1] = np.sqrt(np.sum(R * R, axis=1))
-    return {"planes": planes, "g": g, "ambiguous": amb, "res_norm": res_norm}
+    return {"planes": planes, "g": g, "ambiguous": amb, "quot": quot64, "res_norm": res_norm}
 
 
 def dequantize(planes: np.ndarray, g: np.ndarray, h: np.ndarray | None, K: int,

@@ -10,7 +10,7 @@ import torch
 import residual_binarized_weight_amd as rb
 import workloads as wl
 from oracle import rb_oracle as O
-from tests.gpu_util import assert_product_close, dev, planes_np, scales_np, to_dev
+from tests.gpu_util import assert_pack_matches, assert_product_close, dev, planes_np, scales_np, to_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs the GPU")]
@@ -36,6 +36,17 @@ def wide_layer():
     del Wd
     torch.cuda.synchronize()
     return planes_d, g_d
+
+
+def test_pack_wide_layer_sampled_rows(wide_layer):
+    """The packing these products use, bit-exact against the oracle on 384 sampled rows of
+    the 28672x8192 layer (the first and last row included)."""
+    planes_d, g_d = wide_layer
+    W = wl.weights_for("wide")
+    N, K = W.shape
+    rows = np.sort(np.random.default_rng(7).choice(np.arange(1, N - 1), 382, replace=False))
+    rows = np.concatenate([[0], rows, [N - 1]])
+    assert_pack_matches(W, 2, None, "f16", 0, planes_np(planes_d, K), scales_np(g_d, 2, N), rows=rows)
 
 
 @pytest.mark.parametrize("k", [1, 2])

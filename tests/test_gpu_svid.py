@@ -116,3 +116,10 @@ def test_svid_mlp_down_layer_two_sweeps():
     # the 4096 x 11008 layer at k = 2: two sweeps against the oracle (fp64 ARPACK SVD)
     W = wl.weights_for("down")
     check_against_oracle(W, 2, T=2, P=4)
+
+
+def test_svid_down_layer_width_twenty_sweeps():
+    # the benched setting, T = 20 sweeps of P = 4 power steps, at the 11008-wide rows of the
+    # 4096 x 11008 layer (512 of its rows, so the fp64 oracle finishes in seconds)
+    W = wl.weights_for("down", N=512)
+    check_against_oracle(W, 2, T=20, P=4)

@@ -75,8 +75,13 @@ int rb_version(void);
 const char* rb_status_string(rb_status s);
 
 /* Device workspace (bytes) an operation needs for the given sizes; 0 when it needs
- * none. A workspace must be zero-filled once after allocation; every call returns it
- * to all-zero before its last kernel ends, so it can be reused without clearing. */
+ * none. Every workspace begins with a zero region of ceil(8N / 256) * 256 bytes (one
+ * 64-bit accumulator per output row), which rb_gemv and rb_gemv_variant need all-zero on
+ * entry and return to all-zero before their last kernel ends; the bytes after it are
+ * scratch. rb_gemm_small, rb_svid_init and rb_qat_backward use only bytes after the zero
+ * region and never write it. So: zero-fill a workspace once after allocation, and one
+ * buffer of the largest size its calls need can serve all of them (calls on one stream;
+ * calls that overlap in time need separate workspaces). */
 size_t rb_workspace_bytes(rb_op op, int32_t k, int64_t N, int64_t K, int64_t M);
 
 /* Storage cost in bits per weight of k planes plus per-row g_i and (if has_h)
@@ -169,8 +174,8 @@ rb_status rb_gemv_variant(const uint32_t* planes, int64_t ldp, const void* g, co
  *   RB_F16, else RB_ERR_UNSUPPORTED) and 16-byte aligned. Rows of y past M and columns
  *   past N are not written. When the row and batch tiles are too few to fill the GPU (e.g.
  *   N = 4096), K is split across blocks and the partial sums meet in the workspace:
- *   rb_workspace_bytes(RB_OP_GEMM_SMALL, k, N, K, M) bytes (fp32 [chunks][M][N]; 0 when no
- *   split is used), 4-byte aligned; its contents are scratch. The chunks are added in a fixed
+ *   rb_workspace_bytes(RB_OP_GEMM_SMALL, k, N, K, M) bytes (the zero region, then fp32
+ *   [chunks][M][N]; 0 when no split is used), 4-byte aligned; the partials are scratch. The chunks are added in a fixed
  *   order, so the result is deterministic.
  *   With fp16 g and h = NULL, +-g_i itself is the expanded operand and all planes share
  *   one accumulator; otherwise each plane's sum is scaled by g_i in fp32.
@@ -282,7 +287,7 @@ rb_status rb_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, int32_
  *            aligned, ldp >= ceil(K/32); words past ceil(K/32) are not written
  *   g        output [k][N] fp32 row scales;  h  output [k][K] fp32 column scales (both >= 0)
  *   ws       rb_workspace_bytes(RB_OP_SVID_INIT, k, N, K, 1) bytes, 16-byte aligned; no
- *            zero-filling needed (every call writes what it reads); it holds scratch afterwards
+ *            zero-filling needed (every call writes the scratch it reads, after the zero region)
  *   The caller owns every buffer; the call only enqueues on `stream`.
  */
 rb_status rb_svid_init(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, int64_t ldw, int32_t k,

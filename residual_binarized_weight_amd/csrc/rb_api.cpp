@@ -86,14 +86,21 @@ const char* rb_status_string(rb_status s) {
   return "RB_ERR_UNKNOWN";
 }
 
+// rb_gemm_small's K-chunk partials: scratch, after the zero region (none when K is not split)
+static size_t gemm_small_ws(int k, int64_t N, int64_t K, int64_t M) {
+  const size_t p = rb::gemm_small_workspace_bytes(k, N, K, M);
+  return p > 0 ? rb::zero_region_bytes(N) + p : 0u;
+}
+
 size_t rb_workspace_bytes(rb_op op, int32_t k, int64_t N, int64_t K, int64_t M) {
   if (k < 1 || k > 4 || N < 1 || K < 1 || M < 1) return 0;
   switch (op) {
     case RB_OP_GEMV: return rb::gemv_workspace_bytes(k, N, K, M);
-    case RB_OP_GEMM_SMALL: return rb::gemm_small_workspace_bytes(k, N, K, M);
+    case RB_OP_GEMM_SMALL: return gemm_small_ws(k, N, K, M);
     case RB_OP_CODEBOOK_GEMV: return rb::codebook_gemv_workspace_bytes(N, K, M);
-    case RB_OP_SVID_INIT: return (N > kMaxDim || K > kMaxDim) ? 0 : rb::svid_workspace_bytes(k, N, K);
-    case RB_OP_QAT_BACKWARD: return (N > kQatMaxDim || K > kQatMaxDim) ? 0 : rb::qat_backward_workspace_bytes(k, N, K);
+    case RB_OP_SVID_INIT: return (N > kMaxDim || K > kMaxDim) ? 0 : rb::zero_region_bytes(N) + rb::svid_workspace_bytes(k, N, K);
+    case RB_OP_QAT_BACKWARD:
+      return (N > kQatMaxDim || K > kQatMaxDim) ? 0 : rb::zero_region_bytes(N) + rb::qat_backward_workspace_bytes(k, N, K);
     default: return 0;
   }
 }
@@ -169,11 +176,12 @@ rb_status rb_gemm_small(const uint32_t* planes, int64_t ldp, const void* g, cons
   if (K > (int64_t(1) << 22) || ldp > (int64_t(1) << 20)) return RB_ERR_UNSUPPORTED;  // 32-bit offsets
   if (h && scale_dtype != RB_F16) return RB_ERR_UNSUPPORTED;  // h enters the fp16 operand
   if (h && !aligned(h, 16)) return RB_ERR_MISALIGNED;
-  const size_t need = rb::gemm_small_workspace_bytes(k, N, K, M);
+  const size_t need = gemm_small_ws(k, N, K, M);
   if (need > 0 && (!ws || ws_bytes < need)) return RB_ERR_WORKSPACE;
   if (need > 0 && !aligned(ws, 4)) return RB_ERR_MISALIGNED;
   log_call("rb_gemm_small", N, K, M, k);
-  return from_hip(rb::launch_gemm_small(planes, ldp, g, h, scale_dtype, k, N, K, x, M, y, y_dtype, ws,
+  void* scratch_ws = need > 0 ? static_cast<char*>(ws) + rb::zero_region_bytes(N) : nullptr;
+  return from_hip(rb::launch_gemm_small(planes, ldp, g, h, scale_dtype, k, N, K, x, M, y, y_dtype, scratch_ws,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -280,12 +288,13 @@ rb_status rb_svid_init(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, in
   if (!aligned(W, 16) || !aligned(planes, 16) || !aligned(g, 4) || !aligned(h, 4) ||
       !aligned(s_in, 4) || !aligned(s_out, 4))
     return RB_ERR_MISALIGNED;
-  const size_t need = rb::svid_workspace_bytes(k, N, K);
+  const size_t need = rb::zero_region_bytes(N) + rb::svid_workspace_bytes(k, N, K);
   if (!ws || ws_bytes < need) return RB_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return RB_ERR_MISALIGNED;
   log_call("rb_svid_init", N, K, 1, k);
   return from_hip(rb::launch_svid_init(static_cast<const float*>(W), N, K, ldw, k, T, P, s_in, s_out, a_in,
-                                       a_out, planes, ldp, g, h, ws, static_cast<hipStream_t>(stream)));
+                                       a_out, planes, ldp, g, h, static_cast<char*>(ws) + rb::zero_region_bytes(N),
+                                       static_cast<hipStream_t>(stream)));
 }
 
 rb_status rb_qat_derive(const float* W, int64_t N, int64_t K, int64_t ldw, int32_t k, const float* g,
@@ -336,12 +345,14 @@ rb_status rb_qat_backward(const void* dY, rb_dtype a_dtype, int64_t M, int64_t l
   if (!elem_aligned(dY, a_dtype) || !elem_aligned(X, a_dtype) || !aligned(dW, 4) || !elem_aligned(dX, dx_dtype) ||
       !aligned(dg, 4) || !aligned(dh, 4))
     return RB_ERR_MISALIGNED;
-  const size_t need = rb::qat_backward_workspace_bytes(k, N, K);
+  const size_t need = rb::zero_region_bytes(N) + rb::qat_backward_workspace_bytes(k, N, K);
   if (!ws || ws_bytes < need) return RB_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return RB_ERR_MISALIGNED;
   log_call("rb_qat_backward", N, K, M, k);
   return from_hip(rb::launch_qat_backward(dY, a_dtype, M, lddy, X, ldx, What, ldwh, planes, ldp, g, h, k, N, K, dW,
-                                          lddw, dX, dx_dtype, lddx, dg, dh, ws, static_cast<hipStream_t>(stream)));
+                                          lddw, dX, dx_dtype, lddx, dg, dh,
+                                          static_cast<char*>(ws) + rb::zero_region_bytes(N),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 rb_status rb_qat_autotune(const void* X, const void* dY, rb_dtype a_dtype, int64_t M, int64_t ldx, int64_t lddy,

@@ -453,9 +453,7 @@ LutPlan lut_plan(int64_t N, int64_t K, int cus) {
   return p;
 }
 
-size_t lut_workspace_bytes(int64_t N, int64_t) {
-  return (size_t)(((N * 8 + 255) / 256) * 256);  // one 64-bit accumulator per row
-}
+size_t lut_workspace_bytes(int64_t N, int64_t) { return zero_region_bytes(N); }
 
 template <typename TX, typename TS, typename TY, int KP, int PAIRS>
 hipError_t launch_lut_kp(const LutPlan& p, const uint32_t* planes, int64_t ldp, const void* g, int64_t N,
@@ -539,6 +537,10 @@ hipError_t launch_s(rb_dtype scale_dtype, rb_dtype y_dtype, const uint32_t* plan
 }
 
 }  // namespace
+
+size_t zero_region_bytes(int64_t N) {
+  return (size_t)(((N * 8 + 255) / 256) * 256);  // one 64-bit accumulator per row
+}
 
 // compute units of the current device (cached per device)
 int device_cu_count() {

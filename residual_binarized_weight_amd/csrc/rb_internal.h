@@ -17,6 +17,10 @@ hipError_t launch_pack(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, in
 
 // GEMV (M <= 16)
 size_t gemv_workspace_bytes(int k, int64_t N, int64_t K, int64_t M);
+// The first bytes of every workspace (256-byte multiple): the per-row accumulators that the
+// GEMV calls need zero on entry and leave zero. Calls with scratch-only workspaces place
+// their scratch after it and never write it, so one buffer can serve every call.
+size_t zero_region_bytes(int64_t N);
 hipError_t launch_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                        rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x,
                        rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,

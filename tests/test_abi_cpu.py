@@ -131,18 +131,30 @@ def test_workspace_too_small_is_reported():
             assert _prod(fn, k=k, N=N, K=K, M=M, ldp=ldp, ws=P, wsb=need - 1) == _lib.RB_ERR_WORKSPACE
 
 
+def zero_region(N):
+    return (N * 8 + 255) // 256 * 256
+
+
 def test_gemv_workspace_holds_the_matrix_core_partials():
-    # K a multiple of 64: the LUT region (8 bytes per row, 256-byte multiple) and then the
-    # matrix-core kernel's K-chunk partials at M = 16, the same size for every M
+    # K a multiple of 64: the zero region (8 bytes per row, 256-byte multiple) and then the
+    # matrix-core kernel's K-chunk partials at M = 16, the same size for every M; it is the
+    # rb_gemm_small workspace at M = 16 whenever that one splits K
     for (k, N, K) in ((2, 4096, 11008), (1, 512, 4096), (2, 11008, 4096), (2, 28672, 8192)):
-        lut = (N * 8 + 255) // 256 * 256
         gemm16 = L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, k, N, K, 16)
         for M in (1, 2, 16):
-            assert L.rb_workspace_bytes(_lib.RB_OP_GEMV, k, N, K, M) == lut + gemm16
-    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 1, 512, 4096, 16) == 4 * 16 * 512 * 4
+            assert L.rb_workspace_bytes(_lib.RB_OP_GEMV, k, N, K, M) == max(gemm16, zero_region(N))
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 1, 512, 4096, 16) == zero_region(512) + 4 * 16 * 512 * 4
     assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 28672, 8192, 16) == 0   # no K split
-    # other K: the LUT region alone
-    assert L.rb_workspace_bytes(_lib.RB_OP_GEMV, 2, 300, 1000, 16) == (300 * 8 + 255) // 256 * 256
+    # other K: the zero region alone
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMV, 2, 300, 1000, 16) == zero_region(300)
+
+
+def test_scratch_workspaces_start_after_the_zero_region():
+    # calls whose workspace is scratch keep clear of the GEMV's zero region, so one buffer
+    # serves all calls: each needs the zero region plus its own scratch
+    assert L.rb_workspace_bytes(_lib.RB_OP_SVID_INIT, 2, 4096, 11008, 1) > zero_region(4096)
+    assert L.rb_workspace_bytes(_lib.RB_OP_QAT_BACKWARD, 2, 4096, 11008, 2048) > zero_region(4096)
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 11008, 64) > zero_region(4096)
 
 
 def test_workspace_bytes_invalid_sizes():
@@ -335,7 +347,7 @@ def test_qat_backward_rejects(kw, status):
 
 def test_qat_workspace_covers_the_partial_sums():
     # strips of 256 columns x k x N row partials + tiles of 256 rows x k x K column partials
-    ws = L.rb_workspace_bytes(_lib.RB_OP_QAT_BACKWARD, 2, 4096, 11008, 2048)
+    ws = L.rb_workspace_bytes(_lib.RB_OP_QAT_BACKWARD, 2, 4096, 11008, 2048) - zero_region(4096)
     assert ws >= 4 * (43 * 2 * 4096 + 16 * 2 * 11008)
     assert ws < 4 * (43 * 2 * 4096 + 16 * 2 * 11008) + 512
     assert L.rb_workspace_bytes(_lib.RB_OP_QAT_BACKWARD, 2, (1 << 28) + 1, 64, 1) == 0
@@ -478,7 +490,7 @@ def test_gemv_variant_rejects(kw, status):
 def test_gemm_small_split_workspace():
     # 32 row tiles of the 4096-row layer: K is split in 8 chunks of partial sums (fp32 [8][M][N]);
     # the 28672-row layer fills the GPU with its tiles alone and needs none
-    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 11008, 64) == 8 * 64 * 4096 * 4
+    assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 11008, 64) == zero_region(4096) + 8 * 64 * 4096 * 4
     assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 28672, 8192, 256) == 0
     assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 1024, 64) == 0   # chunks < 1024 columns
     need = L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 11008, 64)

@@ -254,6 +254,40 @@ def test_gemv_matrix_core_batches_keep_the_lut_region_zero():
             assert_product_close(y.float().cpu().numpy(), r, s)
 
 
+def test_one_workspace_serves_every_call():
+    # one buffer of the largest size the calls need, shared by rb_gemm_small (K-chunk
+    # partials), rb_svid_init (scratch) and the M = 1 byte-table and general-h products
+    # (which need the zero region zero): the scratch users keep out of the zero region
+    N, K = 512, 4096
+    W = wl.heavy_tailed_weights(101, N, K)
+    h = wl.random_scales(102, 2, K, dtype=np.float16)
+    x1 = wl.activations(103, 1, K)
+    x64 = wl.activations(104, 64, K)
+    p2, g2 = oracle_case(W, 2, h=h)
+    p3, g3 = oracle_case(W, 3)
+    g2d = to_dev(g2.reshape(2, N).astype(np.float16))
+    g3d = to_dev(g3.reshape(3, N).astype(np.float16))
+    sizes = [rb.workspace_bytes(rb.RB_OP_GEMV, 3, N, K, 1), rb.workspace_bytes(rb.RB_OP_GEMM_SMALL, 3, N, K, 64),
+             rb.workspace_bytes(rb.RB_OP_SVID_INIT, 2, N, K, 1)]
+    zr = (N * 8 + 255) // 256 * 256
+    assert min(sizes) > zr
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device=dev())
+    Wd = torch.from_numpy(W).to(dev())
+    for _ in range(2):
+        y64 = rb.gemm_small(to_dev(p3), g3d, None, to_dev(x64), K, ws=ws)
+        rb.svid_init(Wd, 2, T=1, P=2, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws[:zr]) == 0
+        assert torch.count_nonzero(ws[zr:]) > 0
+        y3 = rb.gemv(to_dev(p3), g3d, None, to_dev(x1), K, ws=ws)
+        y2 = rb.gemv(to_dev(p2), g2d, to_dev(h), to_dev(x1), K, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws[:zr]) == 0
+        for y, p, g, hh, x in ((y64, p3, g3, None, x64), (y3, p3, g3, None, x1), (y2, p2, g2, h, x1)):
+            r, sa = O.gemv(p, g, hh, x, K)
+            assert_product_close(y.float().cpu().numpy(), r, sa)
+
+
 @pytest.mark.parametrize("zero_one", [False, True])
 @pytest.mark.parametrize("N,K", [(11008, 4096), (5000, 8200), (777, 4100), (33, 12000), (4096, 11008)])
 def test_gemv_two_planes_with_h_in_one_pass(N, K, zero_one):

@@ -37,7 +37,8 @@ def objective(W, B, g, h, fo, fi):
     return float(np.linalg.norm(Wp - rec))
 
 
-def check_against_oracle(W, k, T, s_in=None, s_out=None, a_in=0.0, a_out=0.0, P=8):
+def check_against_oracle(W, k, T, s_in=None, s_out=None, a_in=0.0, a_out=0.0, P=8, gh_tol=1e-4, flip_tol=1e-4,
+                         obj_tol=1e-4):
     N, K = W.shape
     ref = O.svid_init(W.astype(np.float64), k, T=T, s_in=s_in, s_out=s_out, a_in=a_in, a_out=a_out)
     _, pl, g, h = gpu_svid(W, k, T, P, s_in, s_out, a_in, a_out)
@@ -45,8 +46,8 @@ def check_against_oracle(W, k, T, s_in=None, s_out=None, a_in=0.0, a_out=0.0, P=
     fo = np.ones(N) if s_out is None else s_out.astype(np.float32).astype(np.float64) ** a_out
     fi = np.ones(K) if s_in is None else s_in.astype(np.float32).astype(np.float64) ** a_in
     for i in range(k):
-        assert np.max(np.abs(g[i] - ref["g"][i])) <= 1e-4 * np.max(np.abs(ref["g"][i])), f"g of path {i}"
-        assert np.max(np.abs(h[i] - ref["h"][i])) <= 1e-4 * np.max(np.abs(ref["h"][i])), f"h of path {i}"
+        assert np.max(np.abs(g[i] - ref["g"][i])) <= gh_tol * np.max(np.abs(ref["g"][i])), f"g of path {i}"
+        assert np.max(np.abs(h[i] - ref["h"][i])) <= gh_tol * np.max(np.abs(ref["h"][i])), f"h of path {i}"
     flips = B != ref["B"]
     assert flips.sum() <= max(2, 1e-4 * B.size), f"{flips.sum()} of {B.size} bits differ"
     if flips.any():
@@ -55,9 +56,9 @@ def check_against_oracle(W, k, T, s_in=None, s_out=None, a_in=0.0, a_out=0.0, P=
         What = ref["B"] * np.einsum("in,ik->ink", ref["gp"], ref["hp"])
         for (i, n, c) in zip(*np.nonzero(flips)):
             R = Wp[n, c] - (What[:, n, c].sum() - What[i, n, c])
-            assert abs(R) <= 1e-4 * ref["gp"][i, n] * np.max(ref["hp"][i]), f"flip at {(i, n, c)}, R = {R}"
+            assert abs(R) <= flip_tol * ref["gp"][i, n] * np.max(ref["hp"][i]), f"flip at {(i, n, c)}, R = {R}"
     obj = objective(W.astype(np.float64), B, g, h, fo, fi)
-    assert abs(obj - ref["history"][-1]) <= 1e-4 * ref["history"][-1]
+    assert abs(obj - ref["history"][-1]) <= obj_tol * ref["history"][-1]
     return pl, g, h
 
 
@@ -120,6 +121,12 @@ def test_svid_mlp_down_layer_two_sweeps():
 
 def test_svid_down_layer_width_twenty_sweeps():
     # the benched setting, T = 20 sweeps of P = 4 power steps, at the 11008-wide rows of the
-    # 4096 x 11008 layer (512 of its rows, so the fp64 oracle finishes in seconds)
+    # 4096 x 11008 layer (512 of its rows, so the fp64 oracle finishes in seconds).
+    # Twenty alternating sweeps amplify rounding: the same iteration run in fp32 with NumPy
+    # on this input departs from the fp64 oracle by up to 1.05e-3 (h) and 1.1e-4 (g) of the
+    # largest entry and flips 36 bits at residuals up to 6.3e-4 g max h, while its objective
+    # agrees to 9e-8 (in fp64, 4 power steps match the exact SVD to 1e-11). The bounds are
+    # those figures with about 3x headroom; the objective, which the fit minimises, keeps a
+    # tight bound.
     W = wl.weights_for("down", N=512)
-    check_against_oracle(W, 2, T=20, P=4)
+    check_against_oracle(W, 2, T=20, P=4, gh_tol=3e-3, flip_tol=2e-3, obj_tol=1e-5)

@@ -150,6 +150,24 @@ rb_status rb_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void
                   void* stream);
 
 /*
+ * rb_gemv_noalloc -- rb_gemv for callers that cannot allocate device memory: code under HIP
+ *   graph capture, tight serving loops, harnesses that forbid hipMalloc. Same product, same
+ *   arguments and errors as rb_gemv, except that there is no ws / ws_bytes: the workspace is a
+ *   fixed 4 MB array inside the library, one per GPU, held from the library's load until the
+ *   process ends (the call itself allocates nothing). Its device address is looked up once per
+ *   device. Each call first clears the array's zero region (one small fill kernel on `stream`,
+ *   no memset) and then runs rb_gemv's kernels on it.
+ *   Returns RB_ERR_WORKSPACE when rb_workspace_bytes(RB_OP_GEMV, k, N, K, M) exceeds 4 MB
+ *   (e.g. more than 524288 rows), before touching the device.
+ *   All calls on one GPU share its array: calls that overlap in time on one GPU (different
+ *   streams, threads or processes without ordering) race and give undefined results; order
+ *   them on one stream.
+ */
+rb_status rb_gemv_noalloc(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
+                          rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,
+                          rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* stream);
+
+/*
  * rb_gemv_variant -- rb_gemv for two cheap weight variants:
  *   zero_one = 1: the plane bits are {0, 1} instead of {-1, +1}, W_hat = sum_i g_i (.) B01_i (.) h_i
  *     [SigmoidBitLinear blog: a weight binarizes to {0, scale_row}: a set bit keeps the row's

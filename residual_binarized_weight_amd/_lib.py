@@ -29,6 +29,8 @@ SIGNATURES = {
                                _vp, _i64, _vp, _vp, _vp]),
     "rb_gemv": (ctypes.c_int, [_vp, _i64, _vp, _vp, ctypes.c_int, _i32, _i64, _i64, _vp, ctypes.c_int,
                                _i64, _vp, ctypes.c_int, _vp, _sz, _vp]),
+    "rb_gemv_noalloc": (ctypes.c_int, [_vp, _i64, _vp, _vp, ctypes.c_int, _i32, _i64, _i64, _vp, ctypes.c_int,
+                                       _i64, _vp, ctypes.c_int, _vp]),
     "rb_gemv_variant": (ctypes.c_int, [_vp, _i64, _vp, _vp, _vp, _i32, ctypes.c_int, _i32, _i64, _i64, _vp,
                                        ctypes.c_int, _i64, _vp, ctypes.c_int, _vp, _sz, _vp]),
     "rb_gemm_small": (ctypes.c_int, [_vp, _i64, _vp, _vp, ctypes.c_int, _i32, _i64, _i64, _vp,

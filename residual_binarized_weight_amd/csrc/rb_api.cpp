@@ -132,13 +132,27 @@ rb_status rb_pack(const void* W, rb_dtype w_dtype, int64_t N, int64_t K, int64_t
                                   d_status, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace rb {
+rb_status gemv_args_status(const uint32_t* planes, int64_t ldp, const void* g, const void* h, rb_dtype scale_dtype,
+                           int32_t k, int64_t N, int64_t K, const void* x, rb_dtype x_dtype, int64_t M, void* y,
+                           rb_dtype y_dtype) {
+  rb_status st = check_product_args(planes, ldp, g, scale_dtype, k, N, K, x, x_dtype, M, y, y_dtype, 16);
+  if (st != RB_OK) return st;
+  if (h && !aligned(h, scale_dtype == RB_F32 ? 4 : 2)) return RB_ERR_MISALIGNED;
+  return RB_OK;
+}
+}  // namespace rb
+
+extern "C" {
+
 rb_status rb_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                   rb_dtype scale_dtype, int32_t k, int64_t N, int64_t K, const void* x,
                   rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws, size_t ws_bytes,
                   void* stream) {
-  rb_status st = check_product_args(planes, ldp, g, scale_dtype, k, N, K, x, x_dtype, M, y, y_dtype, 16);
+  rb_status st = rb::gemv_args_status(planes, ldp, g, h, scale_dtype, k, N, K, x, x_dtype, M, y, y_dtype);
   if (st != RB_OK) return st;
-  if (h && !aligned(h, scale_dtype == RB_F32 ? 4 : 2)) return RB_ERR_MISALIGNED;
   const size_t need = rb::gemv_workspace_bytes(k, N, K, M);
   if (need > 0 && (!ws || ws_bytes < need)) return RB_ERR_WORKSPACE;
   if (ws && !aligned(ws, 16)) return RB_ERR_MISALIGNED;

@@ -21,6 +21,10 @@ size_t gemv_workspace_bytes(int k, int64_t N, int64_t K, int64_t M);
 // GEMV calls need zero on entry and leave zero. Calls with scratch-only workspaces place
 // their scratch after it and never write it, so one buffer can serve every call.
 size_t zero_region_bytes(int64_t N);
+// rb_gemv's host-side argument checks (everything but the workspace)
+rb_status gemv_args_status(const uint32_t* planes, int64_t ldp, const void* g, const void* h, rb_dtype scale_dtype,
+                           int32_t k, int64_t N, int64_t K, const void* x, rb_dtype x_dtype, int64_t M, void* y,
+                           rb_dtype y_dtype);
 hipError_t launch_gemv(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                        rb_dtype scale_dtype, int k, int64_t N, int64_t K, const void* x,
                        rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,

@@ -527,6 +527,24 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
         rows["a7_codebook_encode_4096x11008_v20_c65536"]["cpu_oracle"] = oracle_rate(
             lambda: O.hamming_encode(pat, Ch), RC * nb * C.numel() * ENCODE_OPS_PER_PAIR, 1e12, "Tops/s",
             f"first {RC} of the 4096 rows ({RC * nb} patterns x 65536 codewords), operations scaled per pair")
+    # the same encode through the nearest-codeword table (breadth-first search over the 2^20
+    # patterns, then one lookup per block; identical indices)
+    ws_t = torch.empty(rb.lib.rb_codebook_table_bytes(20), dtype=torch.uint8, device=dev)
+    idx_t = rb.codebook_encode(pl[0], Kc, C, 20, table=True, ws=ws_t)
+    torch.cuda.synchronize()
+    if not torch.equal(idx_t, idx):
+        raise RuntimeError("table encode differs from the brute-force encode")
+    e0.record()
+    for _ in range(10):
+        rb.codebook_encode(pl[0], Kc, C, 20, table=True, ws=ws_t)
+    e1.record()
+    torch.cuda.synchronize()
+    us_t = e0.elapsed_time(e1) * 1e3 / 10
+    rows["a7_codebook_encode_4096x11008_v20_c65536"]["table"] = {
+        "us": round(us_t, 2), "speedup_vs_search": round(us / us_t, 1),
+        "note": "rb_codebook_encode_table: table of the nearest codeword of all 2^20 patterns by a multi-source "
+                "breadth-first search over the hypercube (ties to the lowest index), then one lookup per block"}
+    del ws_t, idx_t
     s2 = sc[0].reshape(Nc, -1).contiguous()
     xc = torch.from_numpy(wl.activations_for("codebook", 1)).to(dev)
     yc = torch.empty((1, Nc), dtype=torch.float16, device=dev)
@@ -606,8 +624,9 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
         "iteration_us": round(lr_us - l0_us, 1),
         "e_step_alone_us": round(enc_us, 1),
         "loop_counting_atomics": loop_atomics,
-        "note": "learn with 0 iterations = distinct + the final E-step; each iteration adds an E-step that "
-                "also counts members and bits (atomics hidden under its ALU work) and a vote",
+        "note": "learn with 0 iterations = distinct + the final E-step; each iteration adds an E-step and an "
+                "M-step; at this size the E-steps go through the nearest-codeword table and the M-step is the "
+                "counting sort (e_step_alone_us is the brute-force search, for comparison)",
     }
     if with_oracle:
         pats = O.sign_blocks(words_np, Kc, 20)

@@ -222,6 +222,22 @@ rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N,
                              void* stream);
 
 /*
+ * rb_codebook_encode_table -- rb_codebook_encode through a table of the nearest codeword of
+ *   every one of the 2^v possible blocks, built first by a breadth-first search over the
+ *   hypercube from all codewords at once (layer d + 1 takes the lowest index among the
+ *   distance-d neighbours, which is the lowest index among the nearest codewords). The result is
+ *   identical to rb_codebook_encode's, bit for bit; the work is about 2^v x (a few layers) table
+ *   visits plus one lookup per block instead of N ceil(K/v) c distance evaluations.
+ *   v 1..24 (else RB_ERR_UNSUPPORTED); codewords must hold only their low v bits (the table is
+ *   indexed by them); ws rb_codebook_table_bytes(v) bytes (4 << v, plus 128), 4-byte aligned,
+ *   scratch (no zero-filling needed). Other arguments as rb_codebook_encode.
+ */
+size_t rb_codebook_table_bytes(int32_t v);
+rb_status rb_codebook_encode_table(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K,
+                                   const uint32_t* codebook, int32_t c, int32_t v, uint16_t* idx, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/*
  * Binary codebook learning (binary K-means over the v-column sign blocks of one plane).
  *   [BTC 2.1.1: E-step = nearest codeword in Hamming distance (rb_codebook_encode); M-step =
  *   each codeword becomes the sign of the sum of its members' +-1 vectors, zeros -> +1; when
@@ -231,9 +247,11 @@ rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N,
  *
  * rb_codebook_learn_workspace_bytes -- workspace of the three calls below for an N x K plane
  *   and c codewords of v bits: the M-step's per-codeword counters and cursors (3 c uint32) and
- *   one uint32 per block (the blocks sorted by codeword), or the 2^v-bit pattern bitmap of
- *   rb_codebook_distinct, whichever is larger (0 for invalid sizes). N ceil(K/v) must be below
- *   2^32 (else RB_ERR_UNSUPPORTED).
+ *   one uint32 per block (the blocks sorted by codeword), the 2^v-bit pattern bitmap of
+ *   rb_codebook_distinct, or, when rb_codebook_learn encodes through the nearest-codeword table
+ *   (v <= 24 and N ceil(K/v) c > 64 x 2^v, where the table is the cheaper search), that table,
+ *   whichever is largest (0 for invalid sizes). N ceil(K/v) must be below 2^32 (else
+ *   RB_ERR_UNSUPPORTED).
  */
 size_t rb_codebook_learn_workspace_bytes(int64_t N, int64_t K, int32_t c, int32_t v);
 

@@ -147,13 +147,22 @@ def gemm_small(planes, g, h, x, K: int, y_dtype=torch.float16, ws=None, y=None):
     return _product("rb_gemm_small", planes, g, h, x, K, y_dtype, ws, y, RB_OP_GEMM_SMALL)
 
 
-def codebook_encode(sign_plane: torch.Tensor, K: int, codebook: torch.Tensor, v: int):
-    """uint16 indices (int16 storage) [N][ceil(K/v)] of the nearest codewords."""
+def codebook_encode(sign_plane: torch.Tensor, K: int, codebook: torch.Tensor, v: int, table: bool = False,
+                    ws: torch.Tensor | None = None):
+    """uint16 indices (int16 storage) [N][ceil(K/v)] of the nearest codewords; with table=True
+    through the nearest-codeword table of all 2^v patterns (v <= 24; same result)."""
     N, ldp = sign_plane.shape
     nb = (K + v - 1) // v
     idx = torch.empty((N, nb), dtype=torch.int16, device=sign_plane.device)
-    check("rb_codebook_encode", lib.rb_codebook_encode(_ptr(sign_plane), ldp, N, K, _ptr(codebook),
-                                                       codebook.numel(), v, _ptr(idx), _stream()))
+    if not table:
+        check("rb_codebook_encode", lib.rb_codebook_encode(_ptr(sign_plane), ldp, N, K, _ptr(codebook),
+                                                           codebook.numel(), v, _ptr(idx), _stream()))
+        return idx
+    if ws is None:
+        ws = torch.empty(max(4, lib.rb_codebook_table_bytes(v)), dtype=torch.uint8, device=sign_plane.device)
+    check("rb_codebook_encode_table", lib.rb_codebook_encode_table(_ptr(sign_plane), ldp, N, K, _ptr(codebook),
+                                                                   codebook.numel(), v, _ptr(idx), _ptr(ws),
+                                                                   ws.numel(), _stream()))
     return idx
 
 

@@ -38,6 +38,8 @@ SIGNATURES = {
     "rb_codebook_encode": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _vp]),
     "rb_codebook_gemv": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _i32, _i64, _i64, _vp, _i64, _vp,
                                         _vp, _sz, _vp]),
+    "rb_codebook_table_bytes": (_sz, [_i32]),
+    "rb_codebook_encode_table": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
     "rb_codebook_learn_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "rb_codebook_mstep": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "rb_codebook_distinct": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),

@@ -212,6 +212,24 @@ rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N,
                                              static_cast<hipStream_t>(stream)));
 }
 
+size_t rb_codebook_table_bytes(int32_t v) { return rb::codebook_table_bytes(v); }
+
+rb_status rb_codebook_encode_table(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K,
+                                   const uint32_t* codebook, int32_t c, int32_t v, uint16_t* idx, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!sign_plane || !codebook || !idx) return RB_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (ldp < (K + 31) / 32) return RB_ERR_INVALID_ARG;
+  if (c < 1 || c > 65536 || v < 1 || v > 32) return RB_ERR_INVALID_ARG;
+  if (v > 24) return RB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < rb::codebook_table_bytes(v)) return RB_ERR_WORKSPACE;
+  if (!aligned(sign_plane, 16) || !aligned(codebook, 4) || !aligned(idx, 2) || !aligned(ws, 4))
+    return RB_ERR_MISALIGNED;
+  log_call("rb_codebook_encode_table", N, K, 0, 1);
+  return from_hip(rb::launch_codebook_encode_table(sign_plane, ldp, N, K, codebook, c, v, idx, ws,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 size_t rb_codebook_learn_workspace_bytes(int64_t N, int64_t K, int32_t c, int32_t v) {
   if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim || c < 1 || c > 65536 || v < 1 || v > 32) return 0;
   return rb::codebook_learn_workspace_bytes(N, K, c, v);

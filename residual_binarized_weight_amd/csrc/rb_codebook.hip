@@ -504,6 +504,68 @@ __global__ __launch_bounds__(kDistinctThreads) void distinct_compact_kernel(cons
   for (int64_t i = (int64_t)total + t; i < c; i += kDistinctThreads) codebook[i] = (uint32_t)top;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Nearest-codeword table (v <= 24): the encode result of every one of the 2^v patterns, found by
+// a breadth-first search over the hypercube from all codewords at once.
+//   layer 0      T[C[i]] = (0, the lowest i holding that codeword)
+//   layer d + 1  a pattern p not reached yet, with neighbours q = p ^ (1 << t) at distance d,
+//                gets (d + 1, the lowest index among those neighbours' entries)
+// Why that is the brute-force answer (nearest in Hamming distance, ties to the lowest index):
+// if p's nearest codewords lie at distance d + 1, each of them lies at distance d from some
+// neighbour q of p (one step along a shortest path), no neighbour is nearer than d to the
+// codebook, so those q sit exactly at distance d, and every nearest codeword of such a q is a
+// nearest codeword of p. The minimum of the neighbours' indices is therefore the lowest index
+// among p's nearest codewords. Entries are (distance << 24) | index, 0xffffffff = not reached; a
+// layer reads only entries of distance d and writes only distance d + 1, so no launch reads what
+// it writes. flag[d] is nonzero when some pattern has distance d: once a layer reaches nothing,
+// every pattern has been reached (the hypercube is connected) and the later layers return at once.
+// ---------------------------------------------------------------------------------------------
+constexpr uint32_t kTableUnreached = 0xffffffffu;
+constexpr int kTableMaxV = 24;
+
+__global__ __launch_bounds__(256) void table_seed_kernel(const uint32_t* __restrict__ codebook, int c, int v,
+                                                         uint32_t* __restrict__ table, uint32_t* __restrict__ flag) {
+  const uint32_t mask = (1u << v) - 1u;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < c; i += gridDim.x * 256)
+    atomicMin(&table[codebook[i] & mask], (uint32_t)i);  // distance 0; codewords hold v bits
+  if (blockIdx.x == 0 && threadIdx.x == 0) flag[0] = 1u;
+}
+
+__global__ __launch_bounds__(256) void table_layer_kernel(uint32_t* __restrict__ table, int v, int d,
+                                                          uint32_t* __restrict__ flag) {
+  if (flag[d] == 0u) return;  // nothing at distance d: everything is reached
+  __shared__ int any;
+  if (threadIdx.x == 0) any = 0;
+  __syncthreads();
+  const uint32_t p = blockIdx.x * 256u + threadIdx.x;  // the grid covers the 2^v patterns exactly
+  if (table[p] == kTableUnreached) {
+    uint32_t best = kTableUnreached;
+    for (int t = 0; t < v; ++t) {
+      const uint32_t e = table[p ^ (1u << t)];
+      if ((e >> 24) == (uint32_t)d) best = (e & 0xffffffu) < best ? (e & 0xffffffu) : best;
+    }
+    if (best != kTableUnreached) {
+      table[p] = ((uint32_t)(d + 1) << 24) | best;
+      any = 1;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && any) flag[d + 1] = 1u;
+}
+
+// encode by lookup: the same blocks as encode_kernel, the same answer
+__global__ __launch_bounds__(256) void encode_table_kernel(const uint32_t* __restrict__ plane, int64_t ldp, int64_t N,
+                                                           int64_t K, int v, const uint32_t* __restrict__ table,
+                                                           uint16_t* __restrict__ idx) {
+  const int64_t nb = (K + v - 1) / v;
+  const int64_t total = N * nb;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t n = e / nb;
+    const int64_t j = e - n * nb;
+    idx[e] = (uint16_t)(table[extract_block(plane + n * ldp, K, j * v, v)] & 0xffffu);
+  }
+}
+
 unsigned stride_grid(int64_t items) {
   const int64_t b = (items + 255) / 256;
   return (unsigned)(b < 1 ? 1 : b > (1 << 20) ? (1 << 20) : b);
@@ -569,7 +631,9 @@ size_t codebook_learn_workspace_bytes(int64_t N, int64_t K, int c, int v) {
   const size_t mstep = 4u * (3u * (size_t)c + 64u + blocks);
   const size_t counters = 4u * (size_t)c * (size_t)(v + 1);
   const size_t bitmap = v <= 24 ? ((size_t)1 << (v > 5 ? v - 3 : 2)) : 0u;
+  const size_t table = codebook_use_table(N, K, c, v) ? codebook_table_bytes(v) : 0u;
   size_t m = mstep > counters ? mstep : counters;
+  m = m > table ? m : table;
   return m > bitmap ? m : bitmap;
 }
 
@@ -603,10 +667,54 @@ hipError_t launch_codebook_distinct(const uint32_t* plane, int64_t ldp, int64_t 
   return hipGetLastError();
 }
 
+// the table and the layer flags (one word per possible distance 0..v, 32 of them)
+size_t codebook_table_bytes(int v) { return v >= 1 && v <= kTableMaxV ? ((size_t)4 << v) + 128u : 0u; }
+
+hipError_t launch_codebook_table(const uint32_t* codebook, int c, int v, void* ws, hipStream_t s) {
+  uint32_t* table = static_cast<uint32_t*>(ws);
+  const int64_t np = (int64_t)1 << v;
+  uint32_t* flag = table + np;
+  fill_u32_kernel<<<stride_grid(np), 256, 0, s>>>(table, np, kTableUnreached);
+  fill_u32_kernel<<<1, 256, 0, s>>>(flag, 32, 0u);
+  table_seed_kernel<<<(unsigned)((c + 255) / 256 < 1024 ? (c + 255) / 256 : 1024), 256, 0, s>>>(codebook, c, v, table,
+                                                                                                 flag);
+  const unsigned grid = (unsigned)((np + 255) / 256);
+  for (int d = 0; d < v; ++d) table_layer_kernel<<<grid, 256, 0, s>>>(table, v, d, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_codebook_encode_table(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K,
+                                        const uint32_t* codebook, int c, int v, uint16_t* idx, void* ws,
+                                        hipStream_t s) {
+  const hipError_t e = launch_codebook_table(codebook, c, v, ws, s);
+  if (e != hipSuccess) return e;
+  encode_table_kernel<<<stride_grid(N * ((K + v - 1) / v)), 256, 0, s>>>(plane, ldp, N, K, v,
+                                                                        static_cast<const uint32_t*>(ws), idx);
+  return hipGetLastError();
+}
+
+// The table pays when the brute-force search would score many more (pattern, codeword) pairs
+// than the table's search visits entries (about 2^v times the few layers that do work).
+bool codebook_use_table(int64_t N, int64_t K, int c, int v) {
+  if (v < 1 || v > kTableMaxV) return false;
+  const double pairs = (double)N * (double)((K + v - 1) / v) * (double)c;
+  return pairs > 64.0 * (double)((int64_t)1 << v);
+}
+
 hipError_t launch_codebook_learn(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
                                  uint32_t* codebook, int c, int iters, uint16_t* idx, int32_t* n_distinct,
                                  void* ws, hipStream_t s) {
   hipError_t e = launch_codebook_distinct(plane, ldp, N, K, v, codebook, c, n_distinct, ws, s);
+  if (codebook_use_table(N, K, c, v)) {
+    // each iteration: the table of the current codebook, the lookups, then the counting-sort
+    // M-step (the workspace holds one of them at a time)
+    for (int it = 0; it < iters && e == hipSuccess; ++it) {
+      e = launch_codebook_encode_table(plane, ldp, N, K, codebook, c, v, idx, ws, s);
+      if (e == hipSuccess) e = launch_codebook_mstep(plane, ldp, N, K, v, idx, codebook, c, nullptr, ws, s);
+    }
+    if (e == hipSuccess) e = launch_codebook_encode_table(plane, ldp, N, K, codebook, c, v, idx, ws, s);
+    return e;
+  }
   // each iteration: the E-step counts the members and their bits as it assigns them, then the
   // vote replaces the codewords (a codeword without members keeps its value)
   uint32_t* cnt = static_cast<uint32_t*>(ws);

@@ -495,3 +495,20 @@ def test_gemm_small_split_workspace():
     assert L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 1024, 64) == 0   # chunks < 1024 columns
     need = L.rb_workspace_bytes(_lib.RB_OP_GEMM_SMALL, 2, 4096, 11008, 64)
     assert _prod("rb_gemm_small", k=2, N=4096, K=11008, M=64, ldp=344, ws=P2, wsb=need) == _lib.RB_ERR_MISALIGNED
+
+
+def test_codebook_table_sizes_and_validation():
+    assert L.rb_codebook_table_bytes(20) == (4 << 20) + 128
+    assert L.rb_codebook_table_bytes(1) == 8 + 128
+    assert L.rb_codebook_table_bytes(25) == 0 and L.rb_codebook_table_bytes(0) == 0
+    need = L.rb_codebook_table_bytes(12)
+
+    def call(v=12, ws=P, wsb=None, plane=P, cb=P, idx=P, c=40):
+        return L.rb_codebook_encode_table(plane, 4, 3, 100, cb, c, v, idx, ws, need if wsb is None else wsb, None)
+    assert call(plane=None) == _lib.RB_ERR_INVALID_ARG
+    assert call(c=0) == _lib.RB_ERR_INVALID_ARG
+    assert call(v=33) == _lib.RB_ERR_INVALID_ARG
+    assert call(v=25) == _lib.RB_ERR_UNSUPPORTED
+    assert call(ws=None) == _lib.RB_ERR_WORKSPACE
+    assert call(wsb=need - 1) == _lib.RB_ERR_WORKSPACE
+    assert call(idx=ctypes.c_void_p(0x100001)) == _lib.RB_ERR_MISALIGNED

@@ -99,3 +99,62 @@ def test_codebook_pipeline_pack_encode_product():
     assert np.array_equal(idx.cpu().numpy().view(np.uint16), idx_ref)
     y_ref, sabs = O.codebook_gemv(idx_ref, C, 20, res["g"][0], 16, x, K)
     assert_product_close(y, y_ref, sabs)
+
+
+# ---- encoding through the nearest-codeword table (breadth-first search over all 2^v patterns)
+
+def _sign_words(seed, N, K):
+    return O.binarize(wl.heavy_tailed_weights(seed, N, K), 1)["planes"][0]
+
+
+@pytest.mark.parametrize("N,K,v,c,dups", [(37, 333, 8, 40, 0), (37, 333, 8, 40, 12), (13, 1000, 20, 3000, 50),
+                                          (5, 97, 1, 2, 0), (9, 450, 12, 4096, 0), (4, 100, 24, 300, 20),
+                                          (21, 700, 16, 1, 0)])
+def test_codebook_encode_table_matches_oracle(N, K, v, c, dups):
+    # distinct codewords plus repeats of some of them at later indices (a repeat must never win:
+    # ties go to the lowest index), ragged K (the last block padded with +1)
+    words = _sign_words(90 + v, N, K)
+    rng = np.random.default_rng([91, v, c])
+    C = rng.choice(1 << v, size=min(c, 1 << v), replace=False).astype(np.uint32)
+    if dups:
+        C = np.concatenate([C, C[rng.integers(0, len(C), dups)]])
+    rng.shuffle(C[len(C) // 2:])
+    P = O.sign_blocks(words, K, v)
+    ref = O.hamming_encode(P, C)
+    wd, Cd = to_dev(words), to_dev(C)
+    got = rb.codebook_encode(wd, K, Cd, v, table=True).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+    brute = rb.codebook_encode(wd, K, Cd, v).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, brute)
+
+
+def test_codebook_encode_table_equidistant_ties():
+    # two codewords 0000 and 1111 (v = 4): every block with two set bits is equidistant and
+    # goes to index 0; the same codewords in the other order send it to index 0 again (1111)
+    v, K = 4, 64
+    blocks = np.array([[0b0011, 0b0101, 0b1001, 0b0110, 0b1010, 0b1100, 0b0001, 0b0111,
+                        0b0000, 0b1111, 0b1011, 0b0010, 0b1101, 0b0100, 0b1000, 0b1110]])
+    bits = ((blocks[:, :, None] >> np.arange(v)) & 1).reshape(1, K)
+    words = O.pack_bits(np.where(bits > 0, 1.0, -1.0))
+    for C in (np.array([0b0000, 0b1111], np.uint32), np.array([0b1111, 0b0000], np.uint32),
+              np.array([0b0001, 0b0010, 0b0100, 0b1000], np.uint32)):
+        ref = O.hamming_encode(O.sign_blocks(words, K, v), C)
+        got = rb.codebook_encode(to_dev(words), K, to_dev(C), v, table=True).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, ref)
+
+
+def test_codebook_encode_table_full_layer():
+    # the 4096 x 11008 sign matrix against the full seeded codebook (v = 20, c = 65536): every
+    # index equals the brute-force kernel's, and 24 sampled rows equal the oracle's
+    W = wl.weights_for("codebook")
+    N, K = W.shape
+    words = O.pack_bits(O.sign_pm1(W))
+    C = wl.codebook()
+    wd, Cd = to_dev(words), to_dev(C)
+    got = rb.codebook_encode(wd, K, Cd, 20, table=True)
+    brute = rb.codebook_encode(wd, K, Cd, 20)
+    torch.cuda.synchronize()
+    assert torch.equal(got, brute)
+    rows = np.random.default_rng(92).choice(N, 24, replace=False)
+    P = O.sign_blocks(words[rows], K, 20)
+    assert np.array_equal(got.cpu().numpy().view(np.uint16)[rows], O.hamming_encode(P, C))

@@ -537,8 +537,8 @@ __global__ __launch_bounds__(256) void table_layer_kernel(uint32_t* __restrict__
   __shared__ int any;
   if (threadIdx.x == 0) any = 0;
   __syncthreads();
-  const uint32_t p = blockIdx.x * 256u + threadIdx.x;  // the grid covers the 2^v patterns exactly
-  if (table[p] == kTableUnreached) {
+  const uint32_t p = blockIdx.x * 256u + threadIdx.x;  // the grid covers the 2^v patterns (more when v < 8)
+  if (p < (1u << v) && table[p] == kTableUnreached) {
     uint32_t best = kTableUnreached;
     for (int t = 0; t < v; ++t) {
       const uint32_t e = table[p ^ (1u << t)];

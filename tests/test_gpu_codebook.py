@@ -158,3 +158,19 @@ def test_codebook_encode_table_full_layer():
     rows = np.random.default_rng(92).choice(N, 24, replace=False)
     P = O.sign_blocks(words[rows], K, 20)
     assert np.array_equal(got.cpu().numpy().view(np.uint16)[rows], O.hamming_encode(P, C))
+
+
+@pytest.mark.parametrize("v", [1, 3, 7, 8])
+def test_codebook_encode_table_stays_inside_its_workspace(v):
+    # for v < 8 the 2^v patterns fill less than one 256-thread block: nothing past the table
+    # and its flags may be read or written (a canary after rb_codebook_table_bytes(v))
+    N, K, c = 3, 90, min(3, 1 << v)
+    words = _sign_words(93, N, K)
+    C = np.arange(c, dtype=np.uint32)
+    need = rb.lib.rb_codebook_table_bytes(v)
+    ws = torch.full(((need + 4096) // 4,), -1, dtype=torch.int32, device=dev())
+    got = rb.codebook_encode(to_dev(words), K, to_dev(C), v, table=True, ws=ws.view(torch.uint8))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint16), O.hamming_encode(O.sign_blocks(words, K, v), C))
+    tail = ws.view(torch.uint8)[need:].cpu().numpy()
+    assert np.all(tail == 0xff)

@@ -128,3 +128,22 @@ def test_learn_degenerate_shapes(N, K, v, c, iters):
     assert int(nd.item()) == M_ref
     assert np.array_equal(u32(C), C_ref)
     assert np.array_equal(idx.cpu().numpy().view(np.uint16), idx_ref.astype(np.uint16))
+
+
+def test_mstep_mlp_down_layer_full():
+    # the M-step on the whole 4096 x 11008 sign matrix (2.26 M blocks, v = 20, c = 65536), with
+    # the indices of the nearest-codeword encode: codebook and member counts bit-exact
+    W = wl.weights_for("codebook")
+    N, K = W.shape
+    words = O.pack_bits(O.sign_pm1(W))
+    C0 = wl.codebook()
+    wd = to_dev(words)
+    idx = rb.codebook_encode(wd, K, to_dev(C0), 20, table=True)
+    P = O.sign_blocks(words, K, 20)
+    idx_np = idx.cpu().numpy().view(np.uint16)
+    C_ref, cnt_ref = O.codebook_mstep(P, idx_np, C0, 20)
+    C = to_dev(C0)
+    cnt = rb.codebook_mstep(wd, K, idx, C, 20)
+    torch.cuda.synchronize()
+    assert np.array_equal(u32(C), C_ref)
+    assert np.array_equal(u32(cnt), cnt_ref.astype(np.uint32))

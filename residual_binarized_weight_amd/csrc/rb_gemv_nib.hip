@@ -399,9 +399,294 @@ hipError_t launch_nib_rows(int rw, const uint32_t* planes, int64_t ldp, const vo
   return launch_nib_shape<TX, TS, TY, KP, NPH, 1, VAR>(planes, ldp, g, N, K, x, y, ex, s);
 }
 
+// ---------------------------------------------------------------------------
+// One build for the whole row: K from 4097 up to 10240 columns in LDS, plus a short tail
+// ---------------------------------------------------------------------------
+// The tables hold sums of +-x, T[e] = sum_j (bit j of e ? +x_j : -x_j), so a +-1 plane needs
+// no sum of x (Sum_c B x = sum over nibbles of T[bits]) and entry 0 is written like the others.
+// All of a row's tables are built once, with one block barrier, and then looked up with no
+// further barrier: 64-word groups of 32 KB (16 entry rows of 2 KB), group j at 32 KB j, nibble i
+// of word 64 j + l in slot 8 l + (i ^ a(l)) of every entry row (the swizzle of the phased
+// kernel above, the same 64 distinct banks per lookup). Five groups fill the 160 KB of LDS
+// (320 words). Words past that (at most 32 of them, whole words) are the tail: one lane per
+// half word forms the +-x products of its 16 columns in every plane with v_dot2_f32_f16, no table.
+// A lookup address is (j >> 1) << 16 | e << 11 | (l >> 3) << 8 | low byte, plus the immediate
+// 32 KB (j & 1): byte 1 holds the nibble and l >> 3, joined with the lane's constant bytes by
+// one byte permute as above.
+constexpr int kSbGroupWords = 64;
+constexpr int kSbMaxGroups = 5;
+constexpr uint32_t kSbGroupBytes = 32768u;
+constexpr int kSbSH = 11;  // entry row = 2 KB
+
+template <int KP, int NG, int NG1, bool TAIL, int RW>
+__global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib1_kernel(
+    const uint32_t* __restrict__ planes, int64_t ldp, const __half* __restrict__ g, int64_t N, int64_t K,
+    const __half* __restrict__ x, __half* __restrict__ y) {
+  typedef __attribute__((address_space(3))) float lds_f32p;
+  constexpr int WV = kNibWaves;
+  static_assert(NG1 >= 1 && NG1 <= NG, "groups of the first build");
+  constexpr int kTA = 8 * kSbGroupWords * NG1;                  // tables built before the first lookups
+  constexpr int kTables = 8 * kSbGroupWords * NG;               // tables of the row
+  constexpr int kTBA = (kTA + 64 * WV - 1) / (64 * WV);         // per thread (the last one partial)
+  constexpr int kTBB = (kTables - kTA + 64 * WV - 1) / (64 * WV);
+  constexpr int kTB = kTBA + kTBB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = ((int64_t)blockIdx.x * WV + wave) * RW;
+  const uint32_t Kw = (uint32_t)((K + 31) >> 5);
+  const uint32_t Kc = (uint32_t)K;
+  const uint32_t ldp_b = (uint32_t)ldp * 4u;
+  const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(planes, (uint32_t)((uint64_t)KP * N * ldp * 4));
+  const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g, (uint32_t)((uint64_t)KP * N * 2));
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)((uint64_t)((K * 2 + 3) & ~3ll)));
+
+  // 1. the activations of this thread's tables (nibbles tid + 1024 b of the first build, then
+  // kTA + tid + 1024 b of the second), then of its tail word
+  auto table_of = [&](int b) -> uint32_t {
+    return b < kTBA ? (uint32_t)(b * 64 * WV + tid) : (uint32_t)(kTA + (b - kTBA) * 64 * WV + tid);
+  };
+  auto table_live = [&](int b) -> bool {  // wave-uniform (the table counts are multiples of 512)
+    return b < kTBA ? table_of(b) < (uint32_t)kTA : table_of(b) < (uint32_t)kTables;
+  };
+  nib_u32x2 xq[kTB];
+#pragma unroll
+  for (int b = 0; b < kTB; ++b)
+    xq[b] = table_live(b)
+                ? __builtin_bit_cast(nib_u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (int)(8u * table_of(b)), 0, 0))
+                : nib_u32x2{0u, 0u};
+  // tail: lane l < 2 TW takes half l & 1 (16 columns) of word 320 + (l >> 1), every plane
+  constexpr uint32_t kTail0 = (uint32_t)(kSbGroupWords * NG);
+  const uint32_t TW = TAIL ? Kw - kTail0 : 1u;
+  const uint32_t tword = kTail0 + ((uint32_t)lane >> 1);
+  const uint32_t thalf = (uint32_t)lane & 1u;
+  const bool tlive = TAIL && (uint32_t)lane < 2u * TW;
+  uint32_t xt[8];
+  if constexpr (TAIL) {
+    const uint32_t xo = tlive ? 64u * tword + 32u * thalf : kNibOob;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo + 16u * v), 0, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xt[4 * v + c] = q4[c];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();  // every wave's activations are requested before any weights
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. the tail words (first: their steps run among the first lookups), plane words (lane l:
+  // word 64 j + l of each group), the scales
+  uint32_t wd[RW][NG][KP];
+  uint32_t wt[RW][KP];
+  if constexpr (TAIL) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int i = 0; i < KP; ++i)
+        wt[r][i] = buf_u32(rp, tlive ? (uint32_t)(n0 + r) * ldp_b + 4u * tword : kNibOob,
+                           (uint32_t)i * (uint32_t)N * ldp_b);
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const uint32_t row_off = (uint32_t)(n0 + r) * ldp_b;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const uint32_t w = (uint32_t)(kSbGroupWords * j + lane);
+      const uint32_t voff = w < Kw ? row_off + 4u * w : kNibOob;
+#pragma unroll
+      for (int i = 0; i < KP; ++i) wd[r][j][i] = buf_u32(rp, voff, (uint32_t)i * (uint32_t)N * ldp_b);
+    }
+  }
+  uint32_t gr[RW][KP];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int i = 0; i < KP; ++i)
+      gr[r][i] = buf_u16(rg, (uint32_t)(n0 + r) * 2u, (uint32_t)i * (uint32_t)N * 2u);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. the tables: entry e = lo[e & 3] + hi[e >> 2], lo = {-x0-x1, x0-x1, x1-x0, x0+x1}
+  auto build = [&](int b) {
+    if (!table_live(b)) return;
+    const uint32_t q = table_of(b);
+    float xv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float v = __half2float(__ushort_as_half((uint16_t)((xq[b][c >> 1] >> (16 * (c & 1))) & 0xffffu)));
+      xv[c] = 4u * q + (uint32_t)c < Kc ? v : 0.0f;
+    }
+    const float s01 = xv[0] + xv[1], d01 = xv[0] - xv[1];
+    const float s23 = xv[2] + xv[3], d23 = xv[2] - xv[3];
+    const float lo[4] = {-s01, d01, -d01, s01};
+    const float hi[4] = {-s23, d23, -d23, s23};
+    const uint32_t w = q >> 3, i = q & 7, wl = w & 63u;
+    const uint32_t slot = 8u * wl + (i ^ (((wl >> 2) ^ ((wl >> 5) & 1u)) & 7u));
+    const uint32_t base = (w >> 6) * kSbGroupBytes + slot * 4u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      *(lds_f32p*)(size_t)(((uint32_t)e << kSbSH) + base) = lo[e & 3] + hi[e >> 2];
+  };
+#pragma unroll
+  for (int b = 0; b < kTBA; ++b) build(b);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  // the other groups' tables, while the first groups are looked up (one more barrier below)
+#pragma unroll
+  for (int b = kTBA; b < kTB; ++b) build(b);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 4. lookups: one LDS read per 4 weight bits. A lane past the row's last word holds 0 and
+  // reads entry 0 of a table whose activations are 0.
+  const int al = ((lane >> 2) ^ ((lane >> 5) & 1)) & 7;
+  uint32_t cb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cb[i] = 32u * (uint32_t)(lane & 7) + 4u * (uint32_t)(i ^ al);
+  const uint32_t lh = (uint32_t)(lane >> 3) * 0x01010101u;
+  float acc[RW][KP];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int i = 0; i < KP; ++i) acc[r][i] = 0.0f;
+  // the tail (step 5 below) is spread over the lookups, a few of its steps after each word's
+  // LDS reads are issued: its ALU work fills the wait for them instead of running at the end,
+  // when every wave of the compute unit would run it at once
+  typedef _Float16 nib_h2 __attribute__((ext_vector_type(2)));
+  const nib_h2 neg1 = __builtin_bit_cast(nib_h2, 0xBC00BC00u);
+  float tt[RW][KP];
+  uint32_t w2[RW][KP];  // the lane's 16 bits: byte 2 h of the word in byte 0, byte 2 h + 1 in byte 2
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      tt[r][i] = 0.0f;
+      if constexpr (TAIL) w2[r][i] = __builtin_amdgcn_perm(wt[r][i], wt[r][i], thalf ? 0x0c030c02u : 0x0c010c00u);
+    }
+  // 5. tail step (c, plane i): columns c and c + 8 of the lane's 16 as one fp16 pair; bits c and
+  // c + 8 moved to the two sign positions flip them, and the dot product with (-1, -1) gives +x
+  // for a set bit, -x for a clear one
+  auto tail_step = [&](int r, int st) {
+    const int c = st / KP, i = st % KP;
+    const uint32_t pr = __builtin_amdgcn_perm(xt[4 + (c >> 1)], xt[c >> 1], (c & 1) ? 0x07060302u : 0x05040100u);
+    const uint32_t v = pr ^ ((w2[r][i] << (15 - c)) & 0x80008000u);
+    tt[r][i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(nib_h2, v), neg1, tt[r][i], false);
+  };
+  constexpr int kSteps = 8 * KP;
+  constexpr int kT0 = 0;            // first word that takes tail steps
+  constexpr int kWords = NG * KP;  // words that do
+#pragma unroll
+  for (int j = 0; j < NG; ++j)
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        if (NG1 < NG && j == NG1 && r == 0 && i == 0) {  // the second build is complete
+          __builtin_amdgcn_sched_barrier(0);
+          __syncthreads();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const uint32_t w = wd[r][j][i];
+        const uint32_t hiw = (uint32_t)(j >> 1) << 16;
+        const uint32_t o = kSbGroupBytes * (uint32_t)(j & 1);
+        const uint32_t ev = ((w << 3) & 0x78787878u) | lh;  // byte m: nibble 2 m in bits 3-6
+        const uint32_t od = ((w >> 1) & 0x78787878u) | lh;  // byte m: nibble 2 m + 1
+        auto at = [&](uint32_t src, int ci, uint32_t m) {
+          return lds_f32(__builtin_amdgcn_perm(src, cb[ci] | hiw, 0x0c020000u | ((4u + m) << 8)) + o);
+        };
+        float e[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          e[2 * m] = at(ev, 2 * m, m);
+          e[2 * m + 1] = at(od, 2 * m + 1, m);
+        }
+        if constexpr (TAIL) {
+          const int wi = (j * RW + r) * KP + i - kT0;  // this word's share of the tail steps (RW = 1 here)
+          if (wi >= 0) {
+#pragma unroll
+            for (int c = (kSteps * wi) / kWords; c < (kSteps * (wi + 1)) / kWords; ++c) tail_step(r, c);
+          }
+        }
+        float t = (e[0] + e[1]) + (e[2] + e[3]);
+        t += (e[4] + e[5]) + (e[6] + e[7]);
+        acc[r][i] += t;
+      }
+  if constexpr (TAIL) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int i = 0; i < KP; ++i) acc[r][i] += tt[r][i];
+  }
+
+  // 6. row sums
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) v += __half2float(__ushort_as_half((uint16_t)gr[r][i])) * wave_sum_dpp(acc[r][i]);
+    if (lane == 63 && n0 + r < N) y[n0 + r] = __float2half_rn(v);
+  }
+}
+
+// the single-build kernel's reach: K above one phase of the phased kernel, at most 320 words
+// in LDS, and a tail of at most 32 whole words (one lane per half word)
+bool nib1_fits(int kp, int64_t K) {
+  const int64_t Kw = (K + 31) / 32;
+  if (K <= 32 * kNibPhaseWords) return false;
+  if (Kw <= kSbMaxGroups * kSbGroupWords) return true;
+  return K % 32 == 0 && Kw - kSbMaxGroups * kSbGroupWords <= 32;
+}
+
+template <int KP, int NG, int NG1, bool TAIL, int RW>
+hipError_t launch_nib1_shape(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
+                             const void* x, void* y, hipStream_t s) {
+  constexpr size_t lds = (size_t)NG * kSbGroupBytes;
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib1_kernel<KP, NG, NG1, TAIL, RW>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned grid = (unsigned)((N + kNibWaves * RW - 1) / (kNibWaves * RW));
+  gemv_nib1_kernel<KP, NG, NG1, TAIL, RW><<<grid, 64 * kNibWaves, lds, s>>>(
+      planes, ldp, static_cast<const __half*>(g), N, K, static_cast<const __half*>(x), static_cast<__half*>(y));
+  return hipGetLastError();
+}
+
+template <int KP, int NG, bool TAIL>
+hipError_t launch_nib1_ng(int rw, const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
+                          const void* x, void* y, hipStream_t s) {
+  constexpr int NG1 = NG;  // one build (measured faster than building the later groups during the first lookups)
+  if constexpr (!TAIL) {  // two rows per wave with the tail's registers would spill
+    if (rw >= 2) return launch_nib1_shape<KP, NG, NG1, TAIL, 2>(planes, ldp, g, N, K, x, y, s);
+  }
+  return launch_nib1_shape<KP, NG, NG1, TAIL, 1>(planes, ldp, g, N, K, x, y, s);
+}
+
+template <int KP>
+hipError_t launch_nib1(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K, const void* x,
+                       void* y, hipStream_t s) {
+  const int64_t Kw = (K + 31) / 32;
+  const int64_t cus = device_cu_count();
+  const int rw = (N + kNibWaves - 1) / kNibWaves <= cus ? 1 : 2;
+  const int64_t ng = Kw >= kSbMaxGroups * kSbGroupWords ? kSbMaxGroups : (Kw + kSbGroupWords - 1) / kSbGroupWords;
+  const bool tail = Kw > kSbMaxGroups * kSbGroupWords;
+  switch (ng) {
+    case 3: return launch_nib1_ng<KP, 3, false>(rw, planes, ldp, g, N, K, x, y, s);
+    case 4: return launch_nib1_ng<KP, 4, false>(rw, planes, ldp, g, N, K, x, y, s);
+    default:
+      return tail ? launch_nib1_ng<KP, 5, true>(rw, planes, ldp, g, N, K, x, y, s)
+                  : launch_nib1_ng<KP, 5, false>(rw, planes, ldp, g, N, K, x, y, s);
+  }
+}
+
 template <typename TX, typename TS, typename TY, int KP, int VAR>
 hipError_t launch_nib_kp(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
                          const void* x, void* y, const NibExtra& ex, hipStream_t s) {
+  if constexpr (VAR == 0) {
+    if (nib1_fits(KP, K)) return launch_nib1<KP>(planes, ldp, g, N, K, x, y, s);
+  }
   const int64_t phases = ((K + 31) / 32 + kNibPhaseWords - 1) / kNibPhaseWords;
   const int64_t cus = device_cu_count();
   int rw = 3;

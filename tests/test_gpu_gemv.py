@@ -146,6 +146,35 @@ def test_gemv_m1_writes_nothing_past_y_and_is_deterministic(N, K, k):
     assert_product_close(y.float().cpu().numpy(), y_ref, sabs)
 
 
+@pytest.mark.parametrize("N,K,k", [(37, 4097, 1), (300, 6000, 2), (4113, 8192, 2), (1000, 10240, 2),
+                                   (4113, 10240, 1), (1000, 10272, 2), (515, 11264, 2), (70, 11008, 1),
+                                   (515, 11264, 1), (515, 11296, 1), (300, 11296, 2), (300, 11008, 2),
+                                   (300, 11007, 2)])
+def test_gemv_m1_one_table_build(N, K, k):
+    # the one-build kernel for 4096 < K: 3, 4 or 5 table groups (the last one partial), one or
+    # two rows per wave, no tail, a tail of 1 to 32 whole words, and shapes just past the tail's
+    # reach (11296: 33 words; 11007: not whole words; both run the phased kernel); repeated calls
+    # bit-identical, nothing written past y, every row (or 640 sampled ones, first and last
+    # included) against the oracle
+    W = wl.heavy_tailed_weights(90 + k, N, K)
+    x = wl.activations(91, 1, K)
+    pd, gd = rb.pack(torch.from_numpy(W).to(dev()), k)
+    xd = to_dev(x)
+    buf = torch.full((N + 64,), 12345.0, dtype=torch.float16, device=dev())
+    y = buf[:N].view(1, N)
+    rb.gemv(pd, gd, None, xd, K, y=y)
+    y1 = y.clone()
+    rb.gemv(pd, gd, None, xd, K, y=y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[N:] == 12345.0)
+    assert torch.equal(y1, y)
+    rows = np.arange(N)
+    if N * K > 4_000_000 and N > 640:
+        rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(N + K).choice(N, 638, replace=False)]))
+    y_ref, sabs = O.gemv(planes_np(pd, K)[:, rows], scales_np(gd, k, N)[:, rows], None, x, K)
+    assert_product_close(y.float().cpu().numpy()[:, rows], y_ref, sabs)
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 4])
 @pytest.mark.parametrize("K", [300, 301, 4096, 11008, 16384])
 def test_gemv_general_h_fp16_m1(k, K):

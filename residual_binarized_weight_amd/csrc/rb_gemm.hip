@@ -15,6 +15,13 @@
 //              plane then adds into the same fp32 accumulator (products are exact)
 //   ones mode  (fp32 g, h = 1): +-1, and y += g_i * acc_i in fp32 after each plane
 //   h mode     (fp16 g and h):  +-h_i[c], and y += g_i * acc_i in fp32 after each plane
+//   merge mode (fp16 g, h = 1, k = 2, two or more batch tiles): the two planes' weights
+//              +-g_0 +-g_1 of a column formed as one fp16 operand by a packed fma of the
+//              plane-1 signs with g_1 onto the plane-0 operand, so one MFMA serves both
+//              planes. The sum is rounded once to fp16 (relative error at most 2^-11 of
+//              |g_0| + |g_1|); both scales are first multiplied by the power of two that
+//              puts |g_0| + |g_1| in [2^14, 2^15), so no operand is subnormal or overflows,
+//              and the row's sum is divided by it at the end.
 // The activations are staged in LDS in the same permuted order, 128 columns per stage,
 // rows padded to 272 B so the 16-byte A reads of consecutive rows hit distinct banks.
 //
@@ -42,7 +49,8 @@ constexpr int kStageWords = kStageCols / 32;
 constexpr int kRowBytes = kStageCols * 2 + 16;  // 16 groups of 16 B + pad
 constexpr int kDepth = 2;                       // plane-word prefetch distance in stages
 
-enum { kModeFold = 0, kModeOnes = 1, kModeH = 2 };
+enum { kModeFold = 0, kModeOnes = 1, kModeH = 2, kModeMerge = 3 };
+typedef _Float16 h2g __attribute__((ext_vector_type(2)));
 
 template <typename T> __device__ __forceinline__ void gemm_store(T* p, float v);
 template <> __device__ __forceinline__ void gemm_store<float>(float* p, float v) { *p = v; }
@@ -153,7 +161,24 @@ __device__ __forceinline__ h8 expand_b(uint32_t nw, int t, int hh, u32x4g base) 
   return __builtin_bit_cast(h8, d);
 }
 
-// KP = planes multiplied per pass (fold mode: all k; otherwise 1).
+// merge mode: dword e of the operand is fma(+-1 of plane 1, g_1 pair, +-g_0 of plane 0), the
+// signs from the complemented bits nw0 (sign of g_0 folded in) and nw1 as in expand_b
+__device__ __forceinline__ h8 expand_merge(uint32_t nw0, uint32_t nw1, int t, int hh, uint32_t base0,
+                                           uint32_t g1pair) {
+  u32x4g d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 8 * t + 4 * hh + e;
+    const uint32_t b0 = base0 | ((nw0 << (15 - j)) & 0x80008000u);
+    const uint32_t b1 = 0x3C003C00u | ((nw1 << (15 - j)) & 0x80008000u);
+    const h2g r = __builtin_elementwise_fma(__builtin_bit_cast(h2g, b1), __builtin_bit_cast(h2g, g1pair),
+                                            __builtin_bit_cast(h2g, b0));
+    d[e] = __builtin_bit_cast(uint32_t, r);
+  }
+  return __builtin_bit_cast(h8, d);
+}
+
+// KP = planes multiplied per pass (fold and merge modes: all k; otherwise 1).
 // A group runs nch stages (group 0's count). The plane words of a stage past its half (or
 // past K in a 64-column tail) are whatever the row holds there, and they meet activations
 // that read as 0, so they add +-0 (a non-finite g, which no finite W packs to, would turn
@@ -211,9 +236,27 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
   for (int mt = 0; mt < MT; ++mt) yacc[mt] = (f32x16){};
 
   constexpr int XD = MT == 1 ? kDepth : 1;  // activation stages in flight (divides kDepth)
-  const int passes = MODE == kModeFold ? 1 : k / KP;
+  const int passes = (MODE == kModeFold || MODE == kModeMerge) ? 1 : k / KP;
+  // merge mode: plane 0's |g_0| 2^sh pair (its sign folded into the bits), g_1 2^sh in both
+  // halves, and 2^-sh for the row's sum
+  uint32_t mbase = 0u, mg1 = 0u, msgn = 0u;
+  float mscale = 1.0f;
+  if constexpr (MODE == kModeMerge) {
+    const float g0 = __half2float(*reinterpret_cast<const __half*>(g + nc));
+    const float g1 = __half2float(*reinterpret_cast<const __half*>(g + N + nc));
+    const float m = fabsf(g0) + fabsf(g1);
+    int ex = 0;
+    (void)frexpf(m, &ex);  // m = f 2^ex, f in [0.5, 1)
+    const int sh = m > 0.0f && __builtin_isfinite(m) ? 15 - ex : 0;
+    const uint32_t a = (uint32_t)__half_as_ushort(__float2half_rn(ldexpf(g0, sh)));  // exact: a power of two
+    const uint32_t b = (uint32_t)__half_as_ushort(__float2half_rn(ldexpf(g1, sh)));
+    mbase = (a & 0x7fffu) | ((a & 0x7fffu) << 16);
+    msgn = (a & 0x8000u) ? 0xffffffffu : 0u;
+    mg1 = b | (b << 16);
+    mscale = ldexpf(1.0f, -sh);
+  }
   for (int pass = 0; pass < passes; ++pass) {
-    const int i0 = MODE == kModeFold ? 0 : pass * KP;
+    const int i0 = (MODE == kModeFold || MODE == kModeMerge) ? 0 : pass * KP;
     __amdgpu_buffer_rsrc_t rw[KP];
     u32x4g base[KP];
     uint32_t gsgn[KP];
@@ -309,6 +352,13 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
               for (int mt = 0; mt < MT; ++mt)
                 anext[mt] = *reinterpret_cast<const h8*>(xb + (mt * 32 + nl) * kRowBytes + rn * 16);
             }
+            if constexpr (MODE == kModeMerge) {
+              const h8 b = expand_merge(~cur[0][w] ^ msgn, ~cur[1][w], t, hh, mbase, mg1);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mt], b, acc[0][mt], 0, 0, 0);
+              continue;
+            }
 #pragma unroll
             for (int p = 0; p < KP; ++p) {
               u32x4g bp = base[p];
@@ -335,6 +385,9 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
     if (MODE == kModeFold) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) yacc[mt] = acc[0][mt];
+    } else if (MODE == kModeMerge) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) yacc[mt] = acc[0][mt] * mscale;
     } else {
 #pragma unroll
       for (int q = 0; q < NH; ++q) {  // planes in order, as one pass per plane would add them
@@ -510,7 +563,11 @@ hipError_t launch_y(rb_dtype scale_dtype, const uint32_t* planes, int64_t ldp, c
   if (scale_dtype == RB_F32) return launch_mt<float, TY, kModeOnes, 1>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   switch (k) {
     case 1: return launch_mt<__half, TY, kModeFold, 1>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
-    case 2: return launch_mt<__half, TY, kModeFold, 2>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+    case 2:
+      // two or more batch tiles: both planes in one MFMA operand (one MFMA per step instead of
+      // two; measured faster where each operand feeds several tiles)
+      if (M > 32) return launch_mt<__half, TY, kModeMerge, 2>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
+      return launch_mt<__half, TY, kModeFold, 2>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
     case 3: return launch_mt<__half, TY, kModeFold, 3>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
     default: return launch_mt<__half, TY, kModeFold, 4>(planes, ldp, g, h, k, N, K, x, M, y, ws, s);
   }

@@ -109,6 +109,33 @@ def test_gemm_negative_fp16_scales():
     assert_product_close(y, y_ref, sabs, fp16_out=False)
 
 
+@pytest.mark.parametrize("M", [33, 100, 300])
+def test_gemm_two_planes_one_operand_scale_extremes(M):
+    # k = 2, fp16 scales, more than one batch tile: both planes go through one MFMA operand
+    # (+-g_0 +-g_1 rounded once to fp16 after a power-of-two rescaling per row). Rows with
+    # signed, subnormal, zero, large (|g_0| + |g_1| above the fp16 maximum), cancelling
+    # (g_1 = -g_0) and lopsided scales
+    N, K, k = 96, 704, 2
+    W = wl.heavy_tailed_weights(94, N, K)
+    planes = O.binarize(W, k)["planes"]
+    rng = np.random.default_rng(95)
+    g = np.empty((k, N))
+    g[:, 0::8] = rng.uniform(0.001, 0.05, (k, 12)) * rng.choice([-1.0, 1.0], (k, 12))
+    g[:, 1::8] = rng.uniform(1e-7, 5e-6, (k, 12))                       # subnormal fp16
+    g[0, 2::8], g[1, 2::8] = 0.0, rng.uniform(0.01, 0.02, 12)
+    g[:, 3::8] = 0.0
+    g[0, 4::8], g[1, 4::8] = rng.uniform(30000, 60000, 12), -rng.uniform(30000, 60000, 12)
+    g[0, 5::8] = rng.uniform(0.01, 0.02, 12)
+    g[1, 5::8] = -g[0, 5::8]
+    g[0, 6::8], g[1, 6::8] = rng.uniform(0.5, 1.0, 12), rng.uniform(1e-6, 1e-5, 12)
+    g[0, 7::8], g[1, 7::8] = -rng.uniform(1e-4, 1e-3, 12), rng.uniform(0.1, 0.2, 12)
+    g = g.astype(np.float16).astype(np.float64)
+    x = wl.activations(96, M, K)
+    y = gpu_gemm(planes, g, None, x, K, y_dtype=torch.float32)
+    y_ref, sabs = O.gemv(planes, g.reshape(k, N, 1), None, x, K)
+    assert_product_close(y, y_ref, sabs, fp16_out=False)
+
+
 @pytest.mark.parametrize("M", [40, 129])
 def test_gemm_fp32_scales(M):
     N, K, k = 333, 832, 2

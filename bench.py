@@ -47,7 +47,12 @@ COPIES = 40
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_nib_down_4096x11008_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "residual_binarized_weight_amd", "csrc", f)
                   for f in ("rb_gemv_nib.hip", "rb_device.hpp")]
-PRODUCT_KERNEL = "gemv_nib_kernel<__half, __half, __half, 2, 3, 1, 16, 0>"  # the dominant kernel of a step
+PRODUCT_KERNEL = "gemv_nib1_kernel<2, 5, 5, true, 1>"  # the dominant kernel of a step
+
+
+# the batched product at k = 2 with fp16 scales and more than one 32-row batch tile
+MERGE_NOTE = ("flops = 2 M N K k (one product per plane); the kernel forms +-g0 +-g1 as one fp16 operand "
+              "(rounded once), so the matrix cores run mfma_flops = 2 M N K")
 
 
 def algorithmic_bytes(N: int, K: int, k: int, M: int = 1) -> int:
@@ -443,7 +448,8 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
         flops = 2.0 * Mb * N * K * k
         rows[f"a6_gemm_small_down_4096x11008_k2_m{Mb}"] = roof(
             "mfma", flops / (us * 1e-6) / 1e12, PEAK_FP16_MFMA_TFLOPS, "TFLOP/s", us, flops=flops,
-            k_chunks=(wsg.numel() // (4 * Mb * N)) if wsg is not None else 1)
+            k_chunks=(wsg.numel() // (4 * Mb * N)) if wsg is not None else 1, mfma_flops=flops / k,
+            note=MERGE_NOTE)
     del copies_b, planes_b, copies_h, planes_h
     torch.cuda.synchronize()
 
@@ -480,7 +486,10 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
             us = graph_us(torch, [lambda c=c: rb.gemm_small(c, gk, None, x, KW, y=y) for c in cps], 3)
             flops = 2.0 * M * NW * KW * kk
             row = rows[f"a6_gemm_small_28672x8192_k{kk}_m{M}"] = roof(
-                "mfma", flops / (us * 1e-6) / 1e12, PEAK_FP16_MFMA_TFLOPS, "TFLOP/s", us, flops=flops)
+                "mfma", flops / (us * 1e-6) / 1e12, PEAK_FP16_MFMA_TFLOPS, "TFLOP/s", us, flops=flops,
+                mfma_flops=2.0 * M * NW * KW)
+            if kk == 2:
+                row["note"] = MERGE_NOTE
             if with_oracle:
                 row["cpu_oracle"] = oracle_rate(
                     lambda: O.gemv(pl_s[:kk], g_s[:kk], None, xh, KW), 2.0 * M * RS * KW * kk, 1e12, "TFLOP/s",

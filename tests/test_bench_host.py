@@ -35,7 +35,7 @@ def test_counter_calibration(tmp_path):
     stream_kib = (nbytes // 256 * 256) / 1024.0 / 2.0          # half of the true bytes
     Kw = (bench.K_COLS + 31) // 32
     copy_bytes = bench.K_PLANES * bench.N_ROWS * ((Kw + 31) // 32 * 32) * 4
-    prod = "void rb::(anonymous namespace)::gemv_nib_kernel<__half, __half, __half, 2, 3, 1, 16, 0>(unsigned int const*)"
+    prod = "void rb::(anonymous namespace)::gemv_nib1_kernel<2, 5, 5, true, 1>(unsigned int const*)"
     other = "void rb::(anonymous namespace)::gemv_nib_kernel<__half, __half, __half, 2, 3, 1, 16, 12>(unsigned int const*)"
     d = tmp_path / "run"
     d.mkdir()
@@ -43,7 +43,7 @@ def test_counter_calibration(tmp_path):
         {"Counter_Name": "FETCH_SIZE", "Kernel_Name": prod, "Dispatch_Id": 1, "Counter_Value": 2000.0},
         {"Counter_Name": "FETCH_SIZE", "Kernel_Name": prod, "Dispatch_Id": 1, "Counter_Value": 1000.0},
         {"Counter_Name": "FETCH_SIZE", "Kernel_Name": prod, "Dispatch_Id": 2, "Counter_Value": 3000.0},
-        # the general-h instance of the same kernel is another kernel: not counted
+        # the general-h kernel is another kernel: not counted
         {"Counter_Name": "FETCH_SIZE", "Kernel_Name": other, "Dispatch_Id": 6, "Counter_Value": 9000.0},
         {"Counter_Name": "FETCH_SIZE", "Kernel_Name": other, "Dispatch_Id": 7, "Counter_Value": 9000.0},
         {"Counter_Name": "FETCH_SIZE", "Kernel_Name": "stream_read_kernel", "Dispatch_Id": 3, "Counter_Value": stream_kib},

@@ -50,6 +50,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "residual_binarized_weight_amd", "csrc", f)
 PRODUCT_KERNEL = "gemv_nib1_kernel<2, 5, 5, true, 1>"  # the dominant kernel of a step
 
 
+SETTLE_S = 0.25   # untimed replays before each timed graph (see graph_us)
+
 # the batched product at k = 2 with fp16 scales and more than one 32-row batch tile
 MERGE_NOTE = ("flops = 2 M N K k (one product per plane); the kernel forms +-g0 +-g1 as one fp16 operand "
               "(rounded once), so the matrix cores run mfma_flops = 2 M N K")
@@ -162,9 +164,12 @@ def flush_cache(torch, _lib, dev, stream=None):
     del buf
 
 
-def graph_us(torch, calls, rounds: int = 5) -> float:
+def graph_us(torch, calls, rounds: int = 5, settle_s: float = SETTLE_S) -> float:
     """Capture the calls once in a HIP graph on a side stream, replay it `rounds` times and
-    return the average duration of one call (events on the replay stream)."""
+    return the average duration of one call (events on the replay stream). Before the timed
+    replays the graph is replayed untimed for `settle_s` seconds: the GPU raises its clock over
+    the first ~0.1 s of a load (a 5 ms burst of matrix-core work right after an idle second
+    measured 25 % slower than the same work after 0.4 s of it), and a steady rate is wanted."""
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(st):
@@ -178,6 +183,10 @@ def graph_us(torch, calls, rounds: int = 5) -> float:
                 c()
     gr.replay()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        gr.replay()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(rounds):

@@ -583,6 +583,11 @@ hipError_t launch_gemv_variant(const uint32_t* planes, int64_t ldp, const void* 
                                const void* mu, int zero_one, rb_dtype scale_dtype, int k, int64_t N, int64_t K,
                                const void* x, rb_dtype x_dtype, int64_t M, void* y, rb_dtype y_dtype, void* ws,
                                hipStream_t s) {
+  // two activation rows with h = 1 where the one-build nibble kernel applies: one launch that
+  // reads the planes once and runs the table build and lookups once per row
+  if (mu == nullptr && !zero_one && h == nullptr &&
+      gemv_nib_rows_fits(k, N, K, ldp, M, x_dtype, scale_dtype, y_dtype))
+    return launch_gemv_nib_rows(planes, ldp, g, k, N, K, x, M, y, s);
   if (mu == nullptr && !zero_one && ws != nullptr &&
       gemv_on_matrix_cores(k, N, K, ldp, M, h, x_dtype, scale_dtype))
     return launch_gemm_small(planes, ldp, g, h, scale_dtype, k, N, K, x, M, y, y_dtype,

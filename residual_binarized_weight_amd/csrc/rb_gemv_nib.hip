@@ -418,7 +418,10 @@ constexpr int kSbMaxGroups = 5;
 constexpr uint32_t kSbGroupBytes = 32768u;
 constexpr int kSbSH = 11;  // entry row = 2 KB
 
-template <int KP, int NG, bool TAIL, int RW>
+// MR activation rows (x [MR][K], y [MR][N]): the weights are loaded once, and the tables are
+// built and looked up once per activation row, one row after the other in the same LDS (a
+// barrier before each rebuild); the next row's activations are fetched behind the weights.
+template <int KP, int NG, bool TAIL, int RW, int MR>
 __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib1_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const __half* __restrict__ g, int64_t N, int64_t K,
     const __half* __restrict__ x, __half* __restrict__ y) {
@@ -435,35 +438,62 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
   const uint32_t ldp_b = (uint32_t)ldp * 4u;
   const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(planes, (uint32_t)((uint64_t)KP * N * ldp * 4));
   const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g, (uint32_t)((uint64_t)KP * N * 2));
-  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)((uint64_t)((K * 2 + 3) & ~3ll)));
+  // x rows start 16-byte aligned when MR > 1 (K a multiple of 8)
+  const __amdgpu_buffer_rsrc_t rx =
+      buffer_rsrc(x, (uint32_t)((uint64_t)(((MR - 1) * K * 2 + K * 2 + 3) & ~3ll)));
 
-  // 1. the activations of this thread's tables (nibbles tid + 1024 b), then of its tail word
-  auto table_of = [&](int b) -> uint32_t { return (uint32_t)(b * 64 * WV + tid); };
-  auto table_live = [&](int b) -> bool {  // wave-uniform (the table count is a multiple of 512)
-    return table_of(b) < (uint32_t)kTables;
+  // 1. the activations of this thread's tables (nibbles tid + 1024 b), then of its tail word.
+  // With several activation rows, row m + 1's table activations are fetched once row m's
+  // tables are built and its tail activations once row m's lookups are done (one register
+  // set each: two would spill)
+  uint32_t tq = (uint32_t)tid;  // opaque per activation row (see the row loop)
+  // With several activation rows, the threads past the last table (the upper 512 of the last
+  // round) build a copy of the table 512 below theirs: the same activations and the same
+  // operations write the same bits to the same place, and with every thread building in every
+  // round no load sits under a branch (the compiler moved such a load behind the weights,
+  // where the first build waited for all of them)
+  constexpr bool kDup = MR > 1;
+  auto table_of = [&](int b) -> uint32_t {
+    const uint32_t q = (uint32_t)(b * 64 * WV) + tq;
+    return kDup && (b * WV + wave) * 64 >= kTables ? q - 512u : q;
   };
-  nib_u32x2 xq[kTB];
-#pragma unroll
-  for (int b = 0; b < kTB; ++b)
-    xq[b] = table_live(b)
-                ? __builtin_bit_cast(nib_u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (int)(8u * table_of(b)), 0, 0))
-                : nib_u32x2{0u, 0u};
+  auto table_live = [&](int b) -> bool {  // uniform per wave (the table count is a multiple of 512)
+    return kDup || (uint32_t)(b * 64 * WV) + tq < (uint32_t)kTables;
+  };
   // tail: lane l < 2 TW takes half l & 1 (16 columns) of word 320 + (l >> 1), every plane
   constexpr uint32_t kTail0 = (uint32_t)(kSbGroupWords * NG);
   const uint32_t TW = TAIL ? Kw - kTail0 : 1u;
   const uint32_t tword = kTail0 + ((uint32_t)lane >> 1);
   const uint32_t thalf = (uint32_t)lane & 1u;
   const bool tlive = TAIL && (uint32_t)lane < 2u * TW;
+  nib_u32x2 xq[kTB];
   uint32_t xt[8];
-  if constexpr (TAIL) {
-    const uint32_t xo = tlive ? 64u * tword + 32u * thalf : kNibOob;
+  static_assert(kTB <= 3, "at most three tables per thread");
+  auto load_xq = [&](int m) {
+    const uint32_t xrow = (uint32_t)m * (uint32_t)K * 2u;
+    // written out (a loop here was left rolled inside the row lambda)
+    auto one = [&](int b) {
+      xq[b] = table_live(b) ? __builtin_bit_cast(nib_u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                             rx, (int)(xrow + 8u * table_of(b)), 0, 0))
+                            : nib_u32x2{0u, 0u};
+    };
+    one(0);
+    if constexpr (kTB > 1) one(1);
+    if constexpr (kTB > 2) one(2);
+  };
+  auto load_xt = [&](int m) {
+    if constexpr (TAIL) {
+      const uint32_t xo = tlive ? (uint32_t)m * (uint32_t)K * 2u + 64u * tword + 32u * thalf : kNibOob;
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo + 16u * v), 0, 0);
+      for (int v = 0; v < 2; ++v) {
+        const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo + 16u * v), 0, 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) xt[4 * v + c] = q4[c];
+        for (int c = 0; c < 4; ++c) xt[4 * v + c] = q4[c];
+      }
     }
-  }
+  };
+  load_xq(0);
+  load_xt(0);
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();  // every wave's activations are requested before any weights
   __builtin_amdgcn_sched_barrier(0);
@@ -520,24 +550,13 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
     for (int e = 0; e < 16; ++e)
       *(lds_f32p*)(size_t)(((uint32_t)e << kSbSH) + base) = lo[e & 3] + hi[e >> 2];
   };
-#pragma unroll
-  for (int b = 0; b < kTB; ++b) build(b);
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-  __builtin_amdgcn_sched_barrier(0);
-
   // 4. lookups: one LDS read per 4 weight bits. A lane past the row's last word holds 0 and
   // reads entry 0 of a table whose activations are 0.
   const int al = ((lane >> 2) ^ ((lane >> 5) & 1)) & 7;
   uint32_t cb[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) cb[i] = 32u * (uint32_t)(lane & 7) + 4u * (uint32_t)(i ^ al);
-  const uint32_t lh = (uint32_t)(lane >> 3) * 0x01010101u;
-  float acc[RW][KP];
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
-#pragma unroll
-    for (int i = 0; i < KP; ++i) acc[r][i] = 0.0f;
+  uint32_t lh = (uint32_t)(lane >> 3) * 0x01010101u;
   // the tail (step 5 below) is spread over the lookups, a few of its steps after each word's
   // LDS reads are issued: its ALU work fills the wait for them instead of running at the end,
   // when every wave of the compute unit would run it at once
@@ -545,13 +564,6 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
   const nib_h2 neg1 = __builtin_bit_cast(nib_h2, 0xBC00BC00u);
   float tt[RW][KP];
   uint32_t w2[RW][KP];  // the lane's 16 bits: byte 2 h of the word in byte 0, byte 2 h + 1 in byte 2
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      tt[r][i] = 0.0f;
-      if constexpr (TAIL) w2[r][i] = __builtin_amdgcn_perm(wt[r][i], wt[r][i], thalf ? 0x0c030c02u : 0x0c010c00u);
-    }
   // 5. tail step (c, plane i): columns c and c + 8 of the lane's 16 as one fp16 pair; bits c and
   // c + 8 moved to the two sign positions flip them, and the dot product with (-1, -1) gives +x
   // for a set bit, -x for a clear one
@@ -583,41 +595,96 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
       e[2 * m + 1] = lds_f32(__builtin_amdgcn_perm(od, cb[2 * m + 1] | hiw, 0x0c020000u | ((4u + m) << 8)) + o);
     }
   };
-  float ebuf[2][8];
-  if constexpr (kPipe) issue(0, ebuf[0]);
-#pragma unroll
-  for (int wi = 0; wi < kW; ++wi) {
-    if constexpr (kPipe) {
-      if (wi + 1 < kW) issue(wi + 1, ebuf[(wi + 1) & 1]);
+  // one activation row per call; rows after the first run in a loop that is not unrolled, which
+  // keeps the registers those of one row (unrolled, the compiler kept every row's addresses and
+  // activations live and spilled). The first row is outside the loop: at the loop's head the
+  // compiler waits for every load in flight, which must not delay the first table build.
+  auto row = [&](int m) {
+    if (m > 0) {  // every wave is done with the previous row's tables
+      __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-    } else {
-      issue(wi, ebuf[wi & 1]);
     }
-    if constexpr (TAIL) {  // this word's share of the tail steps (RW = 1 with a tail)
-#pragma unroll
-      for (int c = (kSteps * wi) / kW; c < (kSteps * (wi + 1)) / kW; ++c) tail_step(0, c);
-    }
-    const float* e = ebuf[wi & 1];
-    float t = (e[0] + e[1]) + (e[2] + e[3]);
-    t += (e[4] + e[5]) + (e[6] + e[7]);
-    acc[(wi / KP) % RW][wi % KP] += t;
-    if constexpr (kPipe) __builtin_amdgcn_sched_barrier(0);
-  }
-  if constexpr (TAIL) {
+    build(0);  // written out, as the loads
+    if constexpr (kTB > 1) build(1);
+    if constexpr (kTB > 2) build(2);
+    if (m + 1 < MR) load_xq(m + 1);  // the next row's table activations, behind the weights
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[RW][KP];
 #pragma unroll
     for (int r = 0; r < RW; ++r)
 #pragma unroll
-      for (int i = 0; i < KP; ++i) acc[r][i] += tt[r][i];
-  }
+      for (int i = 0; i < KP; ++i) {
+        acc[r][i] = 0.0f;
+        tt[r][i] = 0.0f;
+        // after the build: waits for the tail words, not before it
+        if constexpr (TAIL) w2[r][i] = __builtin_amdgcn_perm(wt[r][i], wt[r][i], thalf ? 0x0c030c02u : 0x0c010c00u);
+      }
+    float ebuf[2][8];
+    if constexpr (kPipe) issue(0, ebuf[0]);
+#pragma unroll
+    for (int wi = 0; wi < kW; ++wi) {
+      if constexpr (kPipe) {
+        if (wi + 1 < kW) issue(wi + 1, ebuf[(wi + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        issue(wi, ebuf[wi & 1]);
+      }
+      if constexpr (TAIL) {  // this word's share of the tail steps (RW = 1 with a tail)
+#pragma unroll
+        for (int c = (kSteps * wi) / kW; c < (kSteps * (wi + 1)) / kW; ++c) tail_step(0, c);
+      }
+      const float* e = ebuf[wi & 1];
+      float t = (e[0] + e[1]) + (e[2] + e[3]);
+      t += (e[4] + e[5]) + (e[6] + e[7]);
+      acc[(wi / KP) % RW][wi % KP] += t;
+      // (in the row loop, keep each word's tail steps with it: hoisted together they hold
+      // 8 k shifted words live through the lookups)
+      if constexpr (kPipe || MR > 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int i = 0; i < KP; ++i) acc[r][i] += tt[r][i];
+      if (m + 1 < MR) load_xt(m + 1);
+    }
 
-  // 6. row sums
+    // 6. row sums of activation row m
 #pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    float v = 0.0f;
+    for (int r = 0; r < RW; ++r) {
+      float v = 0.0f;
 #pragma unroll
-    for (int i = 0; i < KP; ++i) v += __half2float(__ushort_as_half((uint16_t)gr[r][i])) * wave_sum_dpp(acc[r][i]);
-    if (lane == 63 && n0 + r < N) y[n0 + r] = __float2half_rn(v);
-  }
+      for (int i = 0; i < KP; ++i) v += __half2float(__ushort_as_half((uint16_t)gr[r][i])) * wave_sum_dpp(acc[r][i]);
+      if (lane == 63 && n0 + r < N) y[(int64_t)m * N + n0 + r] = __float2half_rn(v);
+    }
+    if constexpr (MR > 1) {
+      // everything the table and lookup addresses and the row sums derive from is the same in
+      // every trip: hoisted out of the loop, those values would stay live across it (about 80
+      // registers, which spill) and the first trip would wait for every load before its table
+      // build; opaque copies made at the end of each trip (when every load has arrived) keep
+      // them inside the loop
+      asm volatile("" : "+v"(lh), "+v"(tq));
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+#pragma unroll
+          for (int i = 0; i < KP; ++i) asm volatile("" : "+v"(wd[r][j][i]));
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+          asm volatile("" : "+v"(gr[r][i]));
+          if constexpr (TAIL) asm volatile("" : "+v"(wt[r][i]));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(cb[i]));
+    }
+  };
+  row(0);
+#pragma unroll 1
+  for (int m = 1; m < MR; ++m) row(m);
 }
 
 // the single-build kernel's reach: K above one phase of the phased kernel, at most 320 words
@@ -629,19 +696,19 @@ bool nib1_fits(int kp, int64_t K) {
   return K % 32 == 0 && Kw - kSbMaxGroups * kSbGroupWords <= 32;
 }
 
-template <int KP, int NG, bool TAIL, int RW>
+template <int KP, int NG, bool TAIL, int RW, int MR = 1>
 hipError_t launch_nib1_shape(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
                              const void* x, void* y, hipStream_t s) {
   constexpr size_t lds = (size_t)NG * kSbGroupBytes;
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib1_kernel<KP, NG, TAIL, RW>,
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib1_kernel<KP, NG, TAIL, RW, MR>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const unsigned grid = (unsigned)((N + kNibWaves * RW - 1) / (kNibWaves * RW));
-  gemv_nib1_kernel<KP, NG, TAIL, RW><<<grid, 64 * kNibWaves, lds, s>>>(
+  gemv_nib1_kernel<KP, NG, TAIL, RW, MR><<<grid, 64 * kNibWaves, lds, s>>>(
       planes, ldp, static_cast<const __half*>(g), N, K, static_cast<const __half*>(x), static_cast<__half*>(y));
   return hipGetLastError();
 }
@@ -670,6 +737,35 @@ hipError_t launch_nib1(const uint32_t* planes, int64_t ldp, const void* g, int64
       return tail ? launch_nib1_ng<KP, 5, true>(rw, planes, ldp, g, N, K, x, y, s)
                   : launch_nib1_ng<KP, 5, false>(rw, planes, ldp, g, N, K, x, y, s);
   }
+}
+
+// two activation rows (h = 1, plain product): one launch, the weights read once. Measured on
+// 4096x11008 (us, against two single-row launches or the matrix cores): M = 2 k = 2 9.8 against
+// 10.8, k = 1 7.1 against 8.6; M = 3 k = 2 15.4 against 13.3 and M = 4 19.5 against 13.4 on the
+// matrix cores, so only M = 2 takes this path. Each further row costs a table build, its
+// barriers and a full set of lookups (about 4.2 us here), which the matrix cores undercut.
+constexpr int kNibMaxRows = 2;
+
+template <int KP, int MR>
+hipError_t launch_nib1_rows(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
+                            const void* x, void* y, hipStream_t s) {
+  const int64_t Kw = (K + 31) / 32;
+  const int64_t ng = Kw >= kSbMaxGroups * kSbGroupWords ? kSbMaxGroups : (Kw + kSbGroupWords - 1) / kSbGroupWords;
+  const bool tail = Kw > kSbMaxGroups * kSbGroupWords;
+  switch (ng) {
+    case 3: return launch_nib1_shape<KP, 3, false, 1, MR>(planes, ldp, g, N, K, x, y, s);
+    case 4: return launch_nib1_shape<KP, 4, false, 1, MR>(planes, ldp, g, N, K, x, y, s);
+    default:
+      return tail ? launch_nib1_shape<KP, 5, true, 1, MR>(planes, ldp, g, N, K, x, y, s)
+                  : launch_nib1_shape<KP, 5, false, 1, MR>(planes, ldp, g, N, K, x, y, s);
+  }
+}
+
+template <int KP>
+hipError_t launch_nib1_rows_m(int64_t M, const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
+                              const void* x, void* y, hipStream_t s) {
+  if (M == 2) return launch_nib1_rows<KP, 2>(planes, ldp, g, N, K, x, y, s);
+  return hipErrorNotSupported;
 }
 
 template <typename TX, typename TS, typename TY, int KP, int VAR>
@@ -723,6 +819,20 @@ bool gemv_nib_fits(int k, int64_t N, int64_t K, int64_t ldp, rb_dtype x_dtype, r
   return x_dtype == RB_F16 && scale_dtype == RB_F16 && y_dtype == RB_F16 && (k == 1 || k == 2) &&
          (K + 31) / 32 <= 4 * kNibPhaseWords && (uint64_t)k * N * ldp * 4 < lim && (uint64_t)k * N * 4 < lim &&
          (uint64_t)K * 4 + 16 < lim && (uint64_t)(N + kNibWaves * 3) * ldp * 4 < lim;
+}
+
+bool gemv_nib_rows_fits(int k, int64_t N, int64_t K, int64_t ldp, int64_t M, rb_dtype x_dtype, rb_dtype scale_dtype,
+                        rb_dtype y_dtype) {
+  // (planes of 2^27 bits and more go to the matrix cores from M = 2 on)
+  return M >= 2 && M <= kNibMaxRows && K % 8 == 0 && nib1_fits(k, K) && (double)k * N * K < 134217728.0 &&
+         gemv_nib_fits(k, N, K, ldp, x_dtype, scale_dtype, y_dtype) && (uint64_t)M * (uint64_t)K * 2u < 0x7fffffffull;
+}
+
+hipError_t launch_gemv_nib_rows(const uint32_t* planes, int64_t ldp, const void* g, int k, int64_t N, int64_t K,
+                                const void* x, int64_t M, void* y, hipStream_t s) {
+  if (k == 1) return launch_nib1_rows_m<1>(M, planes, ldp, g, N, K, x, y, s);
+  if (k == 2) return launch_nib1_rows_m<2>(M, planes, ldp, g, N, K, x, y, s);
+  return hipErrorNotSupported;
 }
 
 hipError_t launch_gemv_nib(const uint32_t* planes, int64_t ldp, const void* g, rb_dtype scale_dtype, int k,

@@ -42,6 +42,12 @@ bool gemv_nib_h_fits(int k, int64_t N, int64_t K, int64_t ldp, const void* h, rb
                      rb_dtype scale_dtype, rb_dtype y_dtype);
 hipError_t launch_gemv_nib_h(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
                              int64_t K, const void* x, void* y, int zero_one, float* acc, hipStream_t s);
+// two activation rows (fp16, h = 1, plain product, 4096 < K within the one-build kernel's
+// reach, K a multiple of 8, planes below 2^27 bits): one launch that reads the planes once
+bool gemv_nib_rows_fits(int k, int64_t N, int64_t K, int64_t ldp, int64_t M, rb_dtype x_dtype, rb_dtype scale_dtype,
+                        rb_dtype y_dtype);
+hipError_t launch_gemv_nib_rows(const uint32_t* planes, int64_t ldp, const void* g, int k, int64_t N, int64_t K,
+                                const void* x, int64_t M, void* y, hipStream_t s);
 // the product with {0, 1} planes (zero_one) and/or a per-row offset mu (h must be NULL with mu)
 hipError_t launch_gemv_variant(const uint32_t* planes, int64_t ldp, const void* g, const void* h,
                                const void* mu, int zero_one, rb_dtype scale_dtype, int k, int64_t N, int64_t K,

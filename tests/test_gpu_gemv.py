@@ -226,8 +226,8 @@ def test_gemv_general_h_fp16_small_batch(M):
 @pytest.mark.parametrize("general_h", [False, True])
 @pytest.mark.parametrize("M", [2, 3, 4, 7, 16])
 def test_gemv_batches_on_both_sides_of_the_matrix_core_switch(M, general_h):
-    # fp16, K a multiple of 64, small planes: M = 2 runs as nibble passes per row, M >= 3 (K >= 2 N)
-    # on the matrix cores (K split into chunks that meet in the workspace)
+    # fp16, K a multiple of 64, small planes (K <= 4096): M = 2 runs as nibble passes per row,
+    # M >= 3 (K >= 2 N) on the matrix cores (K split into chunks that meet in the workspace)
     N, K, k = 300, 2048, 2
     W = wl.heavy_tailed_weights(90 + M, N, K)
     h = wl.random_scales(91, k, K, negative_frac=0.2, dtype=np.float16) if general_h else None
@@ -236,6 +236,33 @@ def test_gemv_batches_on_both_sides_of_the_matrix_core_switch(M, general_h):
     y = gpu_gemv(planes, g, h, x, K)
     y_ref, sabs = O.gemv(planes, g, h, x, K)
     assert_product_close(y, y_ref, sabs)
+
+
+@pytest.mark.parametrize("N,K,k", [(300, 11008, 2), (4113, 8192, 2), (37, 6000, 1), (515, 11264, 1),
+                                   (1000, 10240, 2), (200, 10272, 2), (70, 6001, 2)])
+def test_gemv_two_rows_one_launch(N, K, k):
+    # M = 2, h = 1, 4096 < K: one launch of the one-build kernel that builds and looks up the
+    # tables once per activation row (3, 4 or 5 table groups, with and without the tail; K = 6001
+    # is not a multiple of 8 and takes another path); nothing written past y, repeated calls
+    # bit-identical, every row (or 640 sampled ones) of both outputs against the oracle
+    W = wl.heavy_tailed_weights(99 + k, N, K)
+    x = wl.activations(100, 2, K)
+    pd, gd = rb.pack(torch.from_numpy(W).to(dev()), k)
+    xd = to_dev(x)
+    ws = rb.workspace(rb.RB_OP_GEMV, k, N, K, 2)
+    buf = torch.full((2 * N + 64,), 12345.0, dtype=torch.float16, device=dev())
+    y = buf[:2 * N].view(2, N)
+    rb.gemv(pd, gd, None, xd, K, ws=ws, y=y)
+    y1 = y.clone()
+    rb.gemv(pd, gd, None, xd, K, ws=ws, y=y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[2 * N:] == 12345.0)
+    assert torch.equal(y1, y)
+    rows = np.arange(N)
+    if N * K > 4_000_000 and N > 640:
+        rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(N + K).choice(N, 638, replace=False)]))
+    y_ref, sabs = O.gemv(planes_np(pd, K)[:, rows], scales_np(gd, k, N)[:, rows], None, x, K)
+    assert_product_close(y.float().cpu().numpy()[:, rows], y_ref, sabs)
 
 
 def test_gemv_two_rows_on_large_planes_sampled():

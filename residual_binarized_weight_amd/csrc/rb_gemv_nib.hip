@@ -421,10 +421,16 @@ constexpr int kSbSH = 11;  // entry row = 2 KB
 // MR activation rows (x [MR][K], y [MR][N]): the weights are loaded once, and the tables are
 // built and looked up once per activation row, one row after the other in the same LDS (a
 // barrier before each rebuild); the next row's activations are fetched behind the weights.
-template <int KP, int NG, bool TAIL, int RW, int MR>
+// HM (column scales h, fp16 [KP][K], one activation row): one pass per plane instead, its
+// tables built from x (.) h_i (fp16 x fp16 is exact in fp32) and looked up with that plane's
+// words only; the passes' row sums add up in fp32 before y is written.
+template <int KP, int NG, bool TAIL, int RW, int MR, bool HM = false>
 __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_nib1_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const __half* __restrict__ g, int64_t N, int64_t K,
-    const __half* __restrict__ x, __half* __restrict__ y) {
+    const __half* __restrict__ x, __half* __restrict__ y, const __half* __restrict__ hcol) {
+  static_assert(!HM || (MR == 1 && RW == 1), "column scales: one activation row, one row per wave");
+  constexpr int NPASS = HM ? KP : MR;  // table builds
+  static_assert(NPASS <= 2, "at most two table builds");
   typedef __attribute__((address_space(3))) float lds_f32p;
   constexpr int WV = kNibWaves;
   constexpr int kTables = 8 * kSbGroupWords * NG;               // tables of the row
@@ -441,6 +447,8 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
   // x rows start 16-byte aligned when MR > 1 (K a multiple of 8)
   const __amdgpu_buffer_rsrc_t rx =
       buffer_rsrc(x, (uint32_t)((uint64_t)(((MR - 1) * K * 2 + K * 2 + 3) & ~3ll)));
+  // h rows start 16-byte aligned (K a multiple of 8, h 16-byte aligned)
+  const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(hcol, HM ? (uint32_t)((uint64_t)KP * K * 2) : 0u);
 
   // 1. the activations of this thread's tables (nibbles tid + 1024 b), then of its tail word.
   // With several activation rows, row m + 1's table activations are fetched once row m's
@@ -466,34 +474,39 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
   const uint32_t tword = kTail0 + ((uint32_t)lane >> 1);
   const uint32_t thalf = (uint32_t)lane & 1u;
   const bool tlive = TAIL && (uint32_t)lane < 2u * TW;
-  nib_u32x2 xq[kTB];
-  uint32_t xt[8];
+  nib_u32x2 xq[kTB], hq[kTB];
+  uint32_t xt[8], ht[8];
   static_assert(kTB <= 3, "at most three tables per thread");
-  auto load_xq = [&](int m) {
+  // the table values of row m of x (or of h) into q, the tail values into t
+  auto load_q = [&](__amdgpu_buffer_rsrc_t r, int m, nib_u32x2 (&q)[kTB]) {
     const uint32_t xrow = (uint32_t)m * (uint32_t)K * 2u;
     // written out (a loop here was left rolled inside the row lambda)
     auto one = [&](int b) {
-      xq[b] = table_live(b) ? __builtin_bit_cast(nib_u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                             rx, (int)(xrow + 8u * table_of(b)), 0, 0))
-                            : nib_u32x2{0u, 0u};
+      q[b] = table_live(b) ? __builtin_bit_cast(nib_u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                            r, (int)(xrow + 8u * table_of(b)), 0, 0))
+                           : nib_u32x2{0u, 0u};
     };
     one(0);
     if constexpr (kTB > 1) one(1);
     if constexpr (kTB > 2) one(2);
   };
-  auto load_xt = [&](int m) {
+  auto load_t = [&](__amdgpu_buffer_rsrc_t r, int m, uint32_t (&t)[8]) {
     if constexpr (TAIL) {
       const uint32_t xo = tlive ? (uint32_t)m * (uint32_t)K * 2u + 64u * tword + 32u * thalf : kNibOob;
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
-        const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo + 16u * v), 0, 0);
+        const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(xo + 16u * v), 0, 0);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xt[4 * v + c] = q4[c];
+        for (int c = 0; c < 4; ++c) t[4 * v + c] = q4[c];
       }
     }
   };
+  auto load_xq = [&](int m) { load_q(rx, m, xq); };
+  auto load_xt = [&](int m) { load_t(rx, m, xt); };
   load_xq(0);
+  if constexpr (HM) load_q(rh, 0, hq);
   load_xt(0);
+  if constexpr (HM) load_t(rh, 0, ht);
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();  // every wave's activations are requested before any weights
   __builtin_amdgcn_sched_barrier(0);
@@ -536,7 +549,8 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
     float xv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float v = __half2float(__ushort_as_half((uint16_t)((xq[b][c >> 1] >> (16 * (c & 1))) & 0xffffu)));
+      float v = __half2float(__ushort_as_half((uint16_t)((xq[b][c >> 1] >> (16 * (c & 1))) & 0xffffu)));
+      if constexpr (HM) v *= __half2float(__ushort_as_half((uint16_t)((hq[b][c >> 1] >> (16 * (c & 1))) & 0xffffu)));
       xv[c] = 4u * q + (uint32_t)c < Kc ? v : 0.0f;
     }
     const float s01 = xv[0] + xv[1], d01 = xv[0] - xv[1];
@@ -566,14 +580,22 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
   uint32_t w2[RW][KP];  // the lane's 16 bits: byte 2 h of the word in byte 0, byte 2 h + 1 in byte 2
   // 5. tail step (c, plane i): columns c and c + 8 of the lane's 16 as one fp16 pair; bits c and
   // c + 8 moved to the two sign positions flip them, and the dot product with (-1, -1) gives +x
-  // for a set bit, -x for a clear one
-  auto tail_step = [&](int r, int st) {
-    const int c = st / KP, i = st % KP;
-    const uint32_t pr = __builtin_amdgcn_perm(xt[4 + (c >> 1)], xt[c >> 1], (c & 1) ? 0x07060302u : 0x05040100u);
-    const uint32_t v = pr ^ ((w2[r][i] << (15 - c)) & 0x80008000u);
-    tt[r][i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(nib_h2, v), neg1, tt[r][i], false);
+  // for a set bit, -x for a clear one. With h the pair of h is flipped (and negated) instead and
+  // dotted with the pair of x: -(+-h) x = +-(h x), exact products in fp32.
+  auto tail_step = [&](int r, int c, int i) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t pr = __builtin_amdgcn_perm(xt[4 + (c >> 1)], xt[c >> 1], sel);
+    if constexpr (HM) {
+      const uint32_t ph = __builtin_amdgcn_perm(ht[4 + (c >> 1)], ht[c >> 1], sel);
+      const uint32_t v = ph ^ (~(w2[r][i] << (15 - c)) & 0x80008000u);
+      tt[r][i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(nib_h2, v), __builtin_bit_cast(nib_h2, pr), tt[r][i], false);
+    } else {
+      const uint32_t v = pr ^ ((w2[r][i] << (15 - c)) & 0x80008000u);
+      tt[r][i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(nib_h2, v), neg1, tt[r][i], false);
+    }
   };
-  constexpr int kSteps = 8 * KP;
+  constexpr int kPlanesPerPass = HM ? 1 : KP;
+  constexpr int kSteps = 8 * kPlanesPerPass;
   // Without a tail the lookups are software-pipelined: the 8 reads of word n + 1 are issued
   // before the sums of word n, so each wave keeps two words' reads in flight and its ALU work
   // runs while they are served (in straight order the compiler waits for every word's reads
@@ -581,9 +603,11 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
   // 21.8 us (k = 2), 14.1 -> 13.1 us (k = 1). With the tail, whose steps already fill those
   // waits, the straight order measured 1 % faster and is kept.
   constexpr bool kPipe = !TAIL;
-  constexpr int kW = NG * RW * KP;  // looked-up words, in (group, row, plane) order
-  auto issue = [&](int wi, float (&e)[8]) {
-    const int j = wi / (RW * KP), r = (wi / KP) % RW, i = wi % KP;
+  constexpr int kW = NG * RW * kPlanesPerPass;  // looked-up words per pass, in (group, row, plane) order
+  // plane of word wi in pass m (with h: the pass's plane)
+  auto plane_of = [&](int m, int wi) { return HM ? m : wi % KP; };
+  auto issue = [&](int m, int wi, float (&e)[8]) {
+    const int j = wi / (RW * kPlanesPerPass), r = (wi / kPlanesPerPass) % RW, i = plane_of(m, wi);
     const uint32_t w = wd[r][j][i];
     const uint32_t hiw = (uint32_t)(j >> 1) << 16;
     const uint32_t o = kSbGroupBytes * (uint32_t)(j & 1);
@@ -595,6 +619,9 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
       e[2 * m + 1] = lds_f32(__builtin_amdgcn_perm(od, cb[2 * m + 1] | hiw, 0x0c020000u | ((4u + m) << 8)) + o);
     }
   };
+  float vh[RW];  // with h: the row sums of the passes so far
+#pragma unroll
+  for (int r = 0; r < RW; ++r) vh[r] = 0.0f;
   // one activation row per call; rows after the first run in a loop that is not unrolled, which
   // keeps the registers those of one row (unrolled, the compiler kept every row's addresses and
   // activations live and spilled). The first row is outside the loop: at the loop's head the
@@ -607,7 +634,10 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
     build(0);  // written out, as the loads
     if constexpr (kTB > 1) build(1);
     if constexpr (kTB > 2) build(2);
-    if (m + 1 < MR) load_xq(m + 1);  // the next row's table activations, behind the weights
+    if (m + 1 < NPASS) {  // the next pass's table values, behind the weights
+      if constexpr (HM) load_q(rh, m + 1, hq);
+      else load_xq(m + 1);
+    }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
@@ -622,44 +652,54 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
         if constexpr (TAIL) w2[r][i] = __builtin_amdgcn_perm(wt[r][i], wt[r][i], thalf ? 0x0c030c02u : 0x0c010c00u);
       }
     float ebuf[2][8];
-    if constexpr (kPipe) issue(0, ebuf[0]);
+    if constexpr (kPipe) issue(m, 0, ebuf[0]);
 #pragma unroll
     for (int wi = 0; wi < kW; ++wi) {
       if constexpr (kPipe) {
-        if (wi + 1 < kW) issue(wi + 1, ebuf[(wi + 1) & 1]);
+        if (wi + 1 < kW) issue(m, wi + 1, ebuf[(wi + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
       } else {
-        issue(wi, ebuf[wi & 1]);
+        issue(m, wi, ebuf[wi & 1]);
       }
       if constexpr (TAIL) {  // this word's share of the tail steps (RW = 1 with a tail)
 #pragma unroll
-        for (int c = (kSteps * wi) / kW; c < (kSteps * (wi + 1)) / kW; ++c) tail_step(0, c);
+        for (int st = (kSteps * wi) / kW; st < (kSteps * (wi + 1)) / kW; ++st)
+          tail_step(0, st / kPlanesPerPass, HM ? m : st % KP);
       }
       const float* e = ebuf[wi & 1];
       float t = (e[0] + e[1]) + (e[2] + e[3]);
       t += (e[4] + e[5]) + (e[6] + e[7]);
-      acc[(wi / KP) % RW][wi % KP] += t;
+      acc[(wi / kPlanesPerPass) % RW][plane_of(m, wi)] += t;
       // (in the row loop, keep each word's tail steps with it: hoisted together they hold
       // 8 k shifted words live through the lookups)
-      if constexpr (kPipe || MR > 1) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kPipe || NPASS > 1) __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (TAIL) {
 #pragma unroll
       for (int r = 0; r < RW; ++r)
 #pragma unroll
         for (int i = 0; i < KP; ++i) acc[r][i] += tt[r][i];
-      if (m + 1 < MR) load_xt(m + 1);
+      if (m + 1 < NPASS) {
+        if constexpr (HM) load_t(rh, m + 1, ht);
+        else load_xt(m + 1);
+      }
     }
 
-    // 6. row sums of activation row m
+    // 6. row sums of activation row m (with h: the pass's plane, added up over the passes)
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       float v = 0.0f;
 #pragma unroll
-      for (int i = 0; i < KP; ++i) v += __half2float(__ushort_as_half((uint16_t)gr[r][i])) * wave_sum_dpp(acc[r][i]);
-      if (lane == 63 && n0 + r < N) y[(int64_t)m * N + n0 + r] = __float2half_rn(v);
+      for (int i = 0; i < KP; ++i)
+        if (!HM || i == m) v += __half2float(__ushort_as_half((uint16_t)gr[r][i])) * wave_sum_dpp(acc[r][i]);
+      if constexpr (HM) {
+        vh[r] += v;
+        if (m + 1 == NPASS && lane == 63 && n0 + r < N) y[n0 + r] = __float2half_rn(vh[r]);
+      } else {
+        if (lane == 63 && n0 + r < N) y[(int64_t)m * N + n0 + r] = __float2half_rn(v);
+      }
     }
-    if constexpr (MR > 1) {
+    if constexpr (NPASS > 1) {
       // everything the table and lookup addresses and the row sums derive from is the same in
       // every trip: hoisted out of the loop, those values would stay live across it (about 80
       // registers, which spill) and the first trip would wait for every load before its table
@@ -682,9 +722,14 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
       for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(cb[i]));
     }
   };
-  row(0);
+  if constexpr (HM) {  // the planes' passes, written out (the pass picks plane registers)
+    row(0);
+    if constexpr (KP > 1) row(1);
+  } else {
+    row(0);
 #pragma unroll 1
-  for (int m = 1; m < MR; ++m) row(m);
+    for (int m = 1; m < MR; ++m) row(m);
+  }
 }
 
 // the single-build kernel's reach: K above one phase of the phased kernel, at most 320 words
@@ -696,20 +741,21 @@ bool nib1_fits(int kp, int64_t K) {
   return K % 32 == 0 && Kw - kSbMaxGroups * kSbGroupWords <= 32;
 }
 
-template <int KP, int NG, bool TAIL, int RW, int MR = 1>
+template <int KP, int NG, bool TAIL, int RW, int MR = 1, bool HM = false>
 hipError_t launch_nib1_shape(const uint32_t* planes, int64_t ldp, const void* g, int64_t N, int64_t K,
-                             const void* x, void* y, hipStream_t s) {
+                             const void* x, void* y, hipStream_t s, const void* hcol = nullptr) {
   constexpr size_t lds = (size_t)NG * kSbGroupBytes;
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib1_kernel<KP, NG, TAIL, RW, MR>,
+    const hipError_t e = hipFuncSetAttribute((const void*)gemv_nib1_kernel<KP, NG, TAIL, RW, MR, HM>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const unsigned grid = (unsigned)((N + kNibWaves * RW - 1) / (kNibWaves * RW));
-  gemv_nib1_kernel<KP, NG, TAIL, RW, MR><<<grid, 64 * kNibWaves, lds, s>>>(
-      planes, ldp, static_cast<const __half*>(g), N, K, static_cast<const __half*>(x), static_cast<__half*>(y));
+  gemv_nib1_kernel<KP, NG, TAIL, RW, MR, HM><<<grid, 64 * kNibWaves, lds, s>>>(
+      planes, ldp, static_cast<const __half*>(g), N, K, static_cast<const __half*>(x), static_cast<__half*>(y),
+      static_cast<const __half*>(hcol));
   return hipGetLastError();
 }
 
@@ -766,6 +812,22 @@ hipError_t launch_nib1_rows_m(int64_t M, const uint32_t* planes, int64_t ldp, co
                               const void* x, void* y, hipStream_t s) {
   if (M == 2) return launch_nib1_rows<KP, 2>(planes, ldp, g, N, K, x, y, s);
   return hipErrorNotSupported;
+}
+
+// column scales h (fp16 [KP][K]), one activation row: one pass per plane in one launch
+template <int KP>
+hipError_t launch_nib1_h(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int64_t N, int64_t K,
+                         const void* x, void* y, hipStream_t s) {
+  const int64_t Kw = (K + 31) / 32;
+  const int64_t ng = Kw >= kSbMaxGroups * kSbGroupWords ? kSbMaxGroups : (Kw + kSbGroupWords - 1) / kSbGroupWords;
+  const bool tail = Kw > kSbMaxGroups * kSbGroupWords;
+  switch (ng) {
+    case 3: return launch_nib1_shape<KP, 3, false, 1, 1, true>(planes, ldp, g, N, K, x, y, s, h);
+    case 4: return launch_nib1_shape<KP, 4, false, 1, 1, true>(planes, ldp, g, N, K, x, y, s, h);
+    default:
+      return tail ? launch_nib1_shape<KP, 5, true, 1, 1, true>(planes, ldp, g, N, K, x, y, s, h)
+                  : launch_nib1_shape<KP, 5, false, 1, 1, true>(planes, ldp, g, N, K, x, y, s, h);
+  }
 }
 
 template <typename TX, typename TS, typename TY, int KP, int VAR>
@@ -868,6 +930,14 @@ bool gemv_nib_h_fits(int k, int64_t N, int64_t K, int64_t ldp, const void* h, rb
 
 hipError_t launch_gemv_nib_h(const uint32_t* planes, int64_t ldp, const void* g, const void* h, int k, int64_t N,
                              int64_t K, const void* x, void* y, int zero_one, float* acc, hipStream_t s) {
+  // 4096 < K within the one-build kernel's reach (K a multiple of 8, h 16-byte aligned, +-1
+  // planes, one row per wave fills at most one block per compute unit): every plane's pass in
+  // one launch, with one table build per plane. 4096x11008 k = 2 8.66 -> 8.35 us, k = 1 4.97 ->
+  // 4.85, 4096x8192 k = 2 6.38 -> 5.69; 28672x8192 measured 32.7 against 31.2 (more blocks than
+  // compute units: the phased kernel's three rows per wave share its builds) and keeps that.
+  if (!zero_one && (k == 1 || k == 2) && nib1_fits(k, K) && K % 8 == 0 &&
+      (reinterpret_cast<uintptr_t>(h) & 15u) == 0 && N <= (int64_t)kNibWaves * device_cu_count())
+    return k == 1 ? launch_nib1_h<1>(planes, ldp, g, h, N, K, x, y, s) : launch_nib1_h<2>(planes, ldp, g, h, N, K, x, y, s);
   if (k == 2) {  // both planes in one pass (h_1 follows h_0 at h + K); acc is not used
     NibExtra ex;
     ex.zero_one = zero_one;

@@ -176,10 +176,12 @@ def test_gemv_m1_one_table_build(N, K, k):
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4])
-@pytest.mark.parametrize("K", [300, 301, 4096, 11008, 16384])
+@pytest.mark.parametrize("K", [300, 301, 4096, 6000, 10240, 11008, 16384])
 def test_gemv_general_h_fp16_m1(k, K):
-    # per-column scales h (fp16, some negative), one activation row: the single-plane nibble
-    # pass per plane (K a multiple of 4) or the direct kernel (K = 301)
+    # per-column scales h (fp16, some negative), one activation row: for k <= 2 and 4096 < K <=
+    # 11264 one launch of the one-build kernel with a table build per plane (3 or 5 table groups,
+    # with and without the tail), else the single-plane nibble pass per plane (K a multiple of
+    # 4) or the direct kernel (K = 301)
     N = 96
     W = wl.heavy_tailed_weights(74 + k, N, K)
     h = wl.random_scales(12 + k, k, K, negative_frac=0.2, dtype=np.float16)

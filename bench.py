@@ -47,7 +47,7 @@ COPIES = 40
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_nib_down_4096x11008_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "residual_binarized_weight_amd", "csrc", f)
                   for f in ("rb_gemv_nib.hip", "rb_device.hpp")]
-PRODUCT_KERNEL = "gemv_nib1_kernel<2, 5, 5, true, 1>"  # the dominant kernel of a step
+PRODUCT_KERNEL = "gemv_nib1_kernel<2, 5, true, 1, 1, false>"  # the dominant kernel of a step
 
 
 SETTLE_S = 0.25   # untimed replays before each timed graph (see graph_us)

@@ -35,7 +35,7 @@ def test_counter_calibration(tmp_path):
     stream_kib = (nbytes // 256 * 256) / 1024.0 / 2.0          # half of the true bytes
     Kw = (bench.K_COLS + 31) // 32
     copy_bytes = bench.K_PLANES * bench.N_ROWS * ((Kw + 31) // 32 * 32) * 4
-    prod = "void rb::(anonymous namespace)::gemv_nib1_kernel<2, 5, 5, true, 1>(unsigned int const*)"
+    prod = "void rb::(anonymous namespace)::gemv_nib1_kernel<2, 5, true, 1, 1, false>(unsigned int const*)"
     other = "void rb::(anonymous namespace)::gemv_nib_kernel<__half, __half, __half, 2, 3, 1, 16, 12>(unsigned int const*)"
     d = tmp_path / "run"
     d.mkdir()

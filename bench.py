@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "k=2 4096×11008 M=1 binary GEMV µs; achieved HBM GB/s as % of MI355X peak"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 N_ROWS, K_COLS, K_PLANES = 4096, 11008, 2
+SHAPE_GATEUP = (11008, 4096)          # the gate/up projection of the same MLP
 COPIES = 40
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_nib_down_4096x11008_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "residual_binarized_weight_amd", "csrc", f)
@@ -391,13 +392,13 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
             f"the GPU's {2 * P_it + 1} passes per update")
         del Wso
 
-    # a3-a5 at M = 4 and 16 on the same layer (fp16, 40 rotated copies): the nibble kernel once
-    # per activation row, so the weight stream is read M times
+    # a3-a5 at M = 2, 4 and 16 on the same layer (fp16, 40 rotated copies): two rows in one
+    # launch of the nibble kernel; four or more on the matrix cores (one pass over the planes)
     Wb = torch.from_numpy(wl.weights_for("down")).to(dev)
     planes_b, g_b = rb.pack(Wb, k, ldp=((K + 31) // 32 + 31) // 32 * 32)   # rows padded to 128 bytes
     del Wb
     copies_b = [planes_b.clone() for _ in range(COPIES)]
-    for Mb in (4, 16):
+    for Mb in (2, 4, 16):
         xb = torch.from_numpy(wl.activations_for("down", Mb)).to(dev)
         yb = torch.empty((Mb, N), dtype=torch.float16, device=dev)
         wsb = rb.workspace(rb.RB_OP_GEMV, k, N, K, Mb, device=dev)
@@ -406,8 +407,9 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
         row = rows[f"a3_a5_gemv_down_4096x11008_k2_m{Mb}"] = roof(
             "hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us, algorithmic_bytes=byt,
             weight_bytes_streamed=k * N * K // 8,
-            note="a batch of 4 or more rows runs on the matrix cores: one pass over the planes, K split into "
-                 "chunks whose fp32 sums meet in the workspace")
+            note="two rows: one launch of the nibble kernel (tables built and looked up per row, planes read "
+                 "once); 4 or more rows on the matrix cores: one pass over the planes, K split into chunks whose "
+                 "fp32 sums meet in the workspace")
         if with_oracle:
             from oracle import rb_oracle as O
             RS = 512
@@ -416,6 +418,30 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
             xh = xb.cpu().numpy()
             row["cpu_oracle"] = oracle_rate(lambda: O.gemv(pl_s, g_s, None, xh, K), algorithmic_bytes(RS, K, k, Mb),
                                             1e9, "GB/s", f"first {RS} of the 4096 rows, M={Mb}, bytes scaled per row")
+    # the gate/up projection of the same MLP (11008x4096, k = 2) at M = 1, 4 and 16
+    Ng, Kg = SHAPE_GATEUP
+    Wg = torch.from_numpy(wl.weights_for("gateup")).to(dev)
+    planes_g, g_g = rb.pack(Wg, k, ldp=((Kg + 31) // 32 + 31) // 32 * 32)
+    del Wg
+    copies_g = [planes_g.clone() for _ in range(COPIES)]
+    for Mb in (1, 4, 16):
+        xb = torch.from_numpy(wl.activations_for("gateup", Mb)).to(dev)
+        yb = torch.empty((Mb, Ng), dtype=torch.float16, device=dev)
+        wsb = rb.workspace(rb.RB_OP_GEMV, k, Ng, Kg, Mb, device=dev)
+        us = graph_us(torch, [lambda c=c: rb.gemv(c, g_g, None, xb, Kg, ws=wsb, y=yb) for c in copies_g], 5)
+        byt = algorithmic_bytes(Ng, Kg, k, Mb)
+        row = rows[f"a3_a5_gemv_gateup_11008x4096_k2_m{Mb}"] = roof(
+            "hbm", byt / (us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", us, algorithmic_bytes=byt,
+            weight_bytes_streamed=k * Ng * Kg // 8)
+        if with_oracle and Mb == 1:
+            from oracle import rb_oracle as O
+            RS = 1024
+            pl_s = np.ascontiguousarray(planes_g[:, :RS].cpu().numpy().view(np.uint32)[:, :, :(Kg + 31) // 32])
+            g_s = g_g[:, :RS].float().cpu().numpy().astype(np.float64).reshape(k, RS, 1)
+            xh = xb.cpu().numpy()
+            row["cpu_oracle"] = oracle_rate(lambda: O.gemv(pl_s, g_s, None, xh, Kg), algorithmic_bytes(RS, Kg, k, Mb),
+                                            1e9, "GB/s", f"first {RS} of the 11008 rows, M=1, bytes scaled per row")
+    del copies_g, planes_g
     # ... and with per-column scales h (fp16, the RaBiT dual-scale form) at M = 1: one nibble pass
     # per plane with x (.) h_i in its tables, chained through the workspace
     hb = torch.from_numpy(wl.random_scales(5, k, K, dtype=np.float16)).to(dev)

@@ -184,8 +184,8 @@ __device__ __forceinline__ h8 expand_merge(uint32_t nw0, uint32_t nw1, int t, in
 // that read as 0, so they add +-0 (a non-finite g, which no finite W packs to, would turn
 // that row's +-0 into NaN). Activations are fetched XD stages ahead: kDepth for one 32-row
 // batch tile, whose MFMAs per stage are too few to cover a load's latency, else 1.
-// NG wave groups per block (1 or 2). With two, MSPLIT: they take two halves of the batch,
-// else two halves of K. blockIdx.z splits K further into chunks of kz columns (a multiple of
+// NG wave groups per block. MSPLIT (two groups): they take two halves of the batch, else
+// NG parts of K. blockIdx.z splits K further into chunks of kz columns (a multiple of
 // the stage width) when the row and batch tiles alone would leave compute units idle; each
 // chunk's partial sums then go to part[z][M][N] (fp32) for gemm_reduce_kernel, else to y.
 template <typename TS, typename TY, int MT, int MODE, int KP, int NG, bool MSPLIT>
@@ -194,6 +194,9 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
     int k, int64_t N, int64_t K, const __half* __restrict__ x, int64_t M, TY* __restrict__ y, int64_t kz,
     float* __restrict__ part) {
   extern __shared__ __align__(16) uint8_t smem[];
+  static_assert(!MSPLIT || NG == 2, "the batch split takes two groups");
+  // the K groups' hand-over below fits in the groups' activation buffers
+  static_assert((NG - 1) * kGemmWaves * MT * 16 * 64 * 4 <= NG * 2 * MT * 32 * kRowBytes, "hand-over space");
   const int tid_all = threadIdx.x;
   const int lane = tid_all & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(tid_all >> 6);  // uniform: keeps resources scalar
@@ -214,8 +217,9 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
   const int64_t nc = n < N ? n : N - 1;  // rows past N repeat the last row and are not stored
   const int64_t rb = n0 < N ? n0 : N - 1;
   // batch split: group g takes batch rows [m_base, m_base + 32 MT) of the block's 64 MT;
-  // K split: group 0 takes columns [0, kh), group 1 [kh, K), kh a whole number of stages,
-  // and both groups run group 0's stage count (group 1's extra stages read activations as 0)
+  // K split: group g takes columns [g kh, (g + 1) kh) of the chunk, kh a whole number of
+  // stages, and every group runs group 0's stage count (stages past a group's columns read
+  // activations as 0)
   const int64_t m_base = MSPLIT ? ((int64_t)blockIdx.y * NG + grp) * MT * 32 : (int64_t)blockIdx.y * MT * 32;
   const int64_t m_left = M - m_base;
   const int64_t m_rows = m_left < 0 ? 0 : (m_left < MT * 32 ? m_left : MT * 32);
@@ -223,10 +227,12 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
   const int64_t kz0 = (int64_t)blockIdx.z * kz;
   const int64_t kz1 = kz0 + kz < K ? kz0 + kz : K;
   const int64_t kl = kz1 - kz0;
-  const int64_t kh_raw = (((kl + 1) / 2 + kStageCols - 1) / kStageCols) * kStageCols;
+  const int64_t kh_raw = (((kl + NG - 1) / NG + kStageCols - 1) / kStageCols) * kStageCols;
   const int64_t kh = (MSPLIT || NG == 1) ? kl : (kh_raw < kl ? kh_raw : kl);
-  const int64_t kbeg = kz0 + (MSPLIT || grp == 0 ? 0 : kh);
-  const int64_t kend = kz0 + (MSPLIT || grp == 0 ? kh : kl);
+  const int64_t g0 = MSPLIT ? 0 : ((int64_t)grp * kh < kl ? (int64_t)grp * kh : kl);  // group's columns
+  const int64_t g1 = MSPLIT ? kh : (g0 + kh < kl ? g0 + kh : kl);                     // in the chunk
+  const int64_t kbeg = kz0 + g0;
+  const int64_t kend = kz0 + g1;
   const int nch = (int)((kh + kStageCols - 1) / kStageCols);
   const __amdgpu_buffer_rsrc_t rx = gemm_rsrc(x + (m_rows > 0 ? m_base : 0) * K, m_rows * K * 2);
   const uint32_t lane_off = (uint32_t)((nc - rb) * ldp * 4 + kbeg / 8);  // 4 bytes per 32 columns
@@ -398,22 +404,25 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
     }
   }
 
-  // group 1 hands its sums to group 0 through LDS (the stage loop ended on a barrier, so the
-  // activation buffers are free); group 0 adds them in a fixed order and stores
+  // groups 1 .. NG-1 hand their sums to group 0 through LDS (the stage loop ended on a
+  // barrier, so the activation buffers are free); group 0 adds them in group order and stores
   float* const ex = reinterpret_cast<float*>(smem);
-  if (NG == 2 && !MSPLIT && grp == 1) {
+  if (NG > 1 && !MSPLIT && grp > 0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) ex[((wave * MT + mt) * 16 + j) * 64 + lane] = yacc[mt][j];
+      for (int j = 0; j < 16; ++j) ex[((((grp - 1) * kGemmWaves + wave) * MT + mt) * 16 + j) * 64 + lane] = yacc[mt][j];
   }
-  if (NG == 2 && !MSPLIT) {
+  if (NG > 1 && !MSPLIT) {
     __syncthreads();
-    if (grp == 1) return;
+    if (grp > 0) return;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int gq = 1; gq < NG; ++gq)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) yacc[mt][j] += ex[((wave * MT + mt) * 16 + j) * 64 + lane];
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          yacc[mt][j] += ex[((((gq - 1) * kGemmWaves + wave) * MT + mt) * 16 + j) * 64 + lane];
   }
 
   // D of the 32x32 MFMA: lane l holds column n = l % 32 of the tile, element j holds
@@ -482,11 +491,12 @@ int64_t gemm_k_chunk(int64_t K, int z) {
   return ((stages + z - 1) / z) * kStageCols;
 }
 
-// Fewer chunks when the grid would not fit the blocks resident at once: tiles * z0 blocks
-// beyond `slots` (compute units times the blocks one unit holds) run in a second round, so
-// the count with the smallest rounds / z wins (86 row tiles at one block per unit: 3 chunks
-// make 258 blocks and two rounds, 2 chunks 172 blocks and one). Never more than z0, which
-// sizes the workspace.
+// Fewer chunks when the grid would not spread evenly: blocks beyond `slots` (the compute
+// units) put a second block on some units, which then finish last, so the count with the
+// smallest ceil(blocks / slots) / z wins (86 row tiles: 3 chunks make 258 blocks, two on two
+// units; 2 chunks make 172 blocks, one per unit). Measured on 11008x4096, k = 2, M = 4 / 16:
+// 18.1 / 19.6 us with 3 chunks (two blocks fit a unit at once), 14.4 / 15.3 us with 2. Never
+// more than z0, which sizes the workspace.
 int gemm_fit_split(int z0, int64_t tiles, int64_t slots) {
   if (slots < 1) slots = 1;
   int best = z0;
@@ -508,21 +518,17 @@ hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const 
                       int64_t K, const void* x, int64_t M, void* y, float* ws, hipStream_t s) {
   constexpr size_t lds = gemm_lds_bytes<MT, NG, MODE == kModeH ? KP : 1>();
   static bool attr_set = false;  // per instantiation
-  static int per_cu = 1;          // blocks of this instantiation one compute unit holds at once
   if (!attr_set) {
     const void* fn = (const void*)gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT>;
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kGemmGroupThreads * NG, lds) == hipSuccess && nb > 0)
-      per_cu = nb;
     attr_set = true;
   }
   const int64_t m_per_block = (int64_t)32 * MT * (MSPLIT ? NG : 1);
   const unsigned gx = (unsigned)((N + kGemmTileN - 1) / kGemmTileN);
   const unsigned gy = (unsigned)((M + m_per_block - 1) / m_per_block);
   int nz = gemm_k_split(N, K, M, MODE == kModeH);
-  if (nz > 1) nz = gemm_fit_split(nz, (int64_t)gx * gy, (int64_t)device_cu_count() * per_cu);
+  if (nz > 1) nz = gemm_fit_split(nz, (int64_t)gx * gy, (int64_t)device_cu_count());
   const int64_t kz = nz > 1 ? gemm_k_chunk(K, nz) : K;
   float* part = nz > 1 ? ws : nullptr;
   gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT><<<dim3(gx, gy, (unsigned)nz), kGemmGroupThreads * NG, lds, s>>>(

@@ -556,18 +556,20 @@ int device_cu_count() {
 }
 
 // Batches of a few rows on the matrix cores: the MFMA kernel's time is nearly flat in M up to
-// 16 (4096x11008, k = 2: 17.3 us at M = 2 and 18.7 us at M = 16), while the nibble kernel
-// streams the planes once per activation row (6.3 us per row). Measured crossovers on
-// 4096x4096, 11008x4096, 4096x11008 (k = 1, 2) fall at M = 3..4 (M = 3 where K >= 2 N: 4096x11008,
-// k = 2, 13.8 against 17.4 us), and at M = 2 on 28672x8192 (2^27 bits and more); with column
-// scales h likewise. The kernel takes fp16 x, K a multiple
-// of 64, an even ldp, and h only as fp16 (16-byte aligned).
+// 16 (4096x11008, k = 2: 13.6 us at M = 4 and 14.7 us at M = 16), while the nibble kernel
+// streams the planes once per activation row (5.6 us per row). Measured crossovers on
+// 4096x4096, 11008x4096, 4096x11008 (k = 1, 2) fall at M = 3..4: M = 3 goes to the matrix
+// cores on the two oblong layers (4096x11008, k = 2: 13.8 against 17.4 us; 11008x4096, k = 2:
+// 14.5 against 15.3 us, k = 1: 11.1 against 11.6 us) and stays on the nibble passes on
+// 4096x4096 (10.0 against 10.3 us); M = 2 goes there on 28672x8192 (2^27 bits and more). With
+// column scales h likewise. The kernel takes fp16 x, K a multiple of 64, an even ldp, and h
+// only as fp16 (16-byte aligned).
 static bool gemv_on_matrix_cores(int k, int64_t N, int64_t K, int64_t ldp, int64_t M, const void* h, rb_dtype x_dtype,
                                  rb_dtype scale_dtype) {
   if (M < 2 || x_dtype != RB_F16 || K % 64 != 0 || ldp % 2 != 0) return false;
   if (K > (int64_t(1) << 22) || ldp > (int64_t(1) << 20)) return false;
   if (h != nullptr && (scale_dtype != RB_F16 || (reinterpret_cast<uintptr_t>(h) & 15u) != 0)) return false;
-  return M >= 4 || (M == 3 && K >= 2 * N) || (double)k * (double)N * (double)K >= 134217728.0;
+  return M >= 4 || (M == 3 && (K >= 2 * N || N >= 2 * K)) || (double)k * (double)N * (double)K >= 134217728.0;
 }
 
 // Workspace: first the LUT path's region (M = 1: one 64-bit accumulator per row; the general-h

@@ -384,9 +384,11 @@ def test_gemv_matrix_core_batches_other_dtypes(fmt, general_h, y_dtype):
 
 
 @pytest.mark.parametrize("general_h", [False, True])
-def test_gemv_three_rows_when_n_exceeds_k_half(general_h):
-    # M = 3 with K < 2 N stays on the nibble passes (one per row)
-    N, K, k, M = 700, 1024, 2, 3
+@pytest.mark.parametrize("N", [700, 2100])
+def test_gemv_three_rows_both_routes(general_h, N):
+    # M = 3 on a near-square layer (K < 2 N and N < 2 K) stays on the nibble passes (one per
+    # row); with N >= 2 K it runs on the matrix cores
+    K, k, M = 1024, 2, 3
     W = wl.heavy_tailed_weights(120, N, K)
     h = wl.random_scales(121, k, K, negative_frac=0.2, dtype=np.float16) if general_h else None
     x = wl.activations(122, M, K)

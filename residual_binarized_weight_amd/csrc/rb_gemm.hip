@@ -188,6 +188,9 @@ __device__ __forceinline__ h8 expand_merge(uint32_t nw0, uint32_t nw1, int t, in
 // NG parts of K. blockIdx.z splits K further into chunks of kz columns (a multiple of
 // the stage width) when the row and batch tiles alone would leave compute units idle; each
 // chunk's partial sums then go to part[z][M][N] (fp32) for gemm_reduce_kernel, else to y.
+// With a K split the grid's x extent is rounded up to a multiple of 8 (blocks past the row
+// tiles return at once), so that every chunk of row tile x runs on the same XCD, x % 8
+// (consecutive blocks go to consecutive XCDs), where the reduce reads its partials.
 template <typename TS, typename TY, int MT, int MODE, int KP, int NG, bool MSPLIT>
 __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
     const uint32_t* __restrict__ planes, int64_t ldp, const TS* __restrict__ g, const __half* __restrict__ h,
@@ -195,6 +198,7 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
     float* __restrict__ part) {
   extern __shared__ __align__(16) uint8_t smem[];
   static_assert(!MSPLIT || NG == 2, "the batch split takes two groups");
+  if ((int64_t)blockIdx.x * kGemmTileN >= N) return;  // padding of the grid (uniform per block)
   // the K groups' hand-over below fits in the groups' activation buffers
   static_assert((NG - 1) * kGemmWaves * MT * 16 * 64 * 4 <= NG * 2 * MT * 32 * kRowBytes, "hand-over space");
   const int tid_all = threadIdx.x;
@@ -444,22 +448,26 @@ __global__ __launch_bounds__(kGemmGroupThreads * NG) void gemm_small_kernel(
   }
 }
 
-// y[m][n] = sum over the z chunks of part[z][m][n], in chunk order. All nz (<= kMaxChunks)
-// loads are issued before the first add, so their latencies overlap.
+// y[m][n] = sum over the z chunks of part[z][m][n], in chunk order. Block (x, m) takes the
+// 128 rows of tile x in batch row m; gridDim.x is the product kernel's padded x extent (a
+// multiple of 8), so the block runs on the XCD whose L2 holds that tile's partials. All nz
+// (<= kMaxChunks) loads are issued before the first add, so their latencies overlap.
 constexpr int kMaxChunks = 16;
 template <typename TY>
-__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int64_t MN, int nz,
-                                                          TY* __restrict__ y) {
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += (int64_t)gridDim.x * 256) {
-    float v[kMaxChunks];
+__global__ __launch_bounds__(kGemmTileN) void gemm_reduce_kernel(const float* __restrict__ part, int64_t N, int64_t M,
+                                                                 int nz, TY* __restrict__ y) {
+  const int64_t n = (int64_t)blockIdx.x * kGemmTileN + threadIdx.x;
+  if (n >= N) return;
+  const int64_t MN = M * N;
+  const int64_t e = (int64_t)blockIdx.y * N + n;
+  float v[kMaxChunks];
 #pragma unroll
-    for (int z = 0; z < kMaxChunks; ++z) v[z] = z < nz ? part[(int64_t)z * MN + e] : 0.0f;
-    float s = 0.0f;
+  for (int z = 0; z < kMaxChunks; ++z) v[z] = z < nz ? part[(int64_t)z * MN + e] : 0.0f;
+  float s = 0.0f;
 #pragma unroll
-    for (int z = 0; z < kMaxChunks; ++z)
-      if (z < nz) s += v[z];
-    gemm_store<TY>(&y[e], s);
-  }
+  for (int z = 0; z < kMaxChunks; ++z)
+    if (z < nz) s += v[z];
+  gemm_store<TY>(&y[e], s);
 }
 
 // batch rows per block for M (as launch_mt picks the tiles)
@@ -531,14 +539,13 @@ hipError_t launch_one(const uint32_t* planes, int64_t ldp, const void* g, const 
   if (nz > 1) nz = gemm_fit_split(nz, (int64_t)gx * gy, (int64_t)device_cu_count());
   const int64_t kz = nz > 1 ? gemm_k_chunk(K, nz) : K;
   float* part = nz > 1 ? ws : nullptr;
-  gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT><<<dim3(gx, gy, (unsigned)nz), kGemmGroupThreads * NG, lds, s>>>(
+  const unsigned gxp = nz > 1 ? (gx + 7u) / 8u * 8u : gx;  // K split: x extent padded to whole XCD rounds
+  gemm_small_kernel<TS, TY, MT, MODE, KP, NG, MSPLIT><<<dim3(gxp, gy, (unsigned)nz), kGemmGroupThreads * NG, lds, s>>>(
       planes, ldp, static_cast<const TS*>(g), static_cast<const __half*>(h), k, N, K,
       static_cast<const __half*>(x), M, static_cast<TY*>(y), kz, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nz == 1) return e;
-  const int64_t MN = M * N;
-  const int64_t rb = (MN + 255) / 256;
-  gemm_reduce_kernel<TY><<<(unsigned)(rb < 4096 ? rb : 4096), 256, 0, s>>>(part, MN, nz, static_cast<TY*>(y));
+  gemm_reduce_kernel<TY><<<dim3(gxp, (unsigned)M), kGemmTileN, 0, s>>>(part, N, M, nz, static_cast<TY*>(y));
   return hipGetLastError();
 }
 

@@ -274,11 +274,27 @@ def measure_qat_step(torch, np, rb, wl, dev, with_oracle: bool, M: int = 2048) -
 
     der_us = timed(lambda i: rb.qat_derive(Ws[i % C], g, h, planes=pls[i % C], What=Whs[i % C]))
     fwd_us, bwd_us, step_us = timed(fwd), timed(bwd), timed(step)
+    # the forward's product alone on each engine, and the product taken from the planes instead
+    # of What (rb_gemm_small: one matrix-core pass per plane with h_i in the fp16 operand)
+    mm_flops = 2.0 * M * N * K
+    mm = {}
+    for name, eng in (("mfma", rb.RB_QAT_ENGINE_MFMA), ("rocblas", rb.RB_QAT_ENGINE_ROCBLAS)):
+        us = timed(lambda i, eng=eng: rb.qat_matmul(X, Whs[i % C], Y=Y, engine=eng))
+        mm[name] = {"us": round(us, 2), "TFLOP/s": round(mm_flops / (us * 1e-6) / 1e12, 1),
+                    "frac": round(mm_flops / (us * 1e-6) / 1e12 / PEAK_BF16_MFMA_TFLOPS, 4)}
+    g16, h16, X16 = g.half(), h.half(), X.half()
+    Yp = torch.empty((M, N), dtype=torch.float16, device=dev)
+    wsp = torch.empty(max(16, rb.workspace_bytes(rb.RB_OP_GEMM_SMALL, k, N, K, M)), dtype=torch.uint8, device=dev)
+    us = timed(lambda i: rb.gemm_small(pls[i % C], g16, h16, X16, K, ws=wsp, y=Yp))
+    mm["planes_route"] = {"us": round(us, 2), "TFLOP/s": round(mm_flops / (us * 1e-6) / 1e12, 1),
+                          "note": "Y from the k planes on the matrix cores (fp16 x, g and h): one product per "
+                                  "plane, 2 k M N K flops of MFMA work against 2 M N K through What"}
     flops = 3 * 2.0 * M * N * K
     der_bytes = N * K * (4 + 2) + k * N * K // 8 + 4 * k * (N + K)   # W read, What + planes written
     row = roof("mfma", flops / (step_us * 1e-6) / 1e12, PEAK_BF16_MFMA_TFLOPS, "TFLOP/s", step_us, flops=flops,
                tokens=M, dtype="bf16 operands, fp32 accumulation, fp32 dW",
                forward_us=round(fwd_us, 2), backward_us=round(bwd_us, 2), autotune_s=round(tune_s, 2),
+               forward_product=mm,
                derive={"us": round(der_us, 2), "algorithmic_bytes": der_bytes, "bound": "hbm",
                        "achieved": round(der_bytes / (der_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
                        "unit": "GB/s", "frac": round(der_bytes / (der_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},

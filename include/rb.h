@@ -366,11 +366,28 @@ rb_status rb_qat_derive(const float* W, int64_t N, int64_t K, int64_t ldw, int32
                         int64_t ldwh, void* stream);
 
 /* rb_qat_forward -- rb_qat_derive, then Y [M][ldy] = X What^T (ldy >= N) with y_dtype RB_F32
- * or a_dtype. Planes and What are outputs kept for the backward. */
+ * or a_dtype. Planes and What are outputs kept for the backward. The product runs on rocBLAS,
+ * or on the library's matrix-core kernel (rb_qat_matmul, RB_QAT_ENGINE_MFMA) for a shape where
+ * rb_qat_autotune timed that kernel at least as fast. */
 rb_status rb_qat_forward(const float* W, int64_t N, int64_t K, int64_t ldw, int32_t k, const float* g,
                          const float* h, const void* X, rb_dtype a_dtype, int64_t M, int64_t ldx,
                          uint32_t* planes, int64_t ldp, void* What, int64_t ldwh, void* Y, rb_dtype y_dtype,
                          int64_t ldy, void* stream);
+
+/* rb_qat_matmul -- the forward's product alone, on a chosen engine.
+ *   [RaBiT "Method step details", Algorithm 2: the layer multiplies by the effective weight]
+ *   Y [M][ldy] = X What^T, X [M][ldx] and What [N][ldwh] in a_dtype (RB_F16 or RB_BF16), fp32
+ *   accumulation of the exact products, Y in RB_F32 or a_dtype (rounded to nearest even).
+ *   Rows of Y are M, columns N; elements past N in a row are not written.
+ *   engine  RB_QAT_ENGINE_AUTO: as rb_qat_forward chooses; RB_QAT_ENGINE_MFMA: the library's
+ *           matrix-core kernel (v_mfma_f32_32x32x16 on 128 x 256 output tiles), which needs
+ *           X and What 16-byte aligned, ldx and ldwh multiples of 8, K a multiple of 32, and
+ *           M*ldx and N*ldwh below 2^30 elements (else RB_ERR_UNSUPPORTED); RB_QAT_ENGINE_ROCBLAS: rocBLAS
+ *           (the autotuned kernel if rb_qat_autotune chose one). The engines sum in different
+ *           orders, so their results may differ in the last fp32 bits. */
+typedef enum rb_qat_engine { RB_QAT_ENGINE_AUTO = 0, RB_QAT_ENGINE_MFMA = 1, RB_QAT_ENGINE_ROCBLAS = 2 } rb_qat_engine;
+rb_status rb_qat_matmul(const void* X, rb_dtype a_dtype, int64_t M, int64_t ldx, const void* What, int64_t ldwh,
+                        int64_t N, int64_t K, void* Y, rb_dtype y_dtype, int64_t ldy, int32_t engine, void* stream);
 
 /* rb_qat_backward -- from the forward's X, What and planes and the incoming dY:
  *   dW   output [N][lddw] fp32 (lddw >= K), the shared weight's gradient
@@ -388,8 +405,9 @@ rb_status rb_qat_backward(const void* dY, rb_dtype a_dtype, int64_t M, int64_t l
 /* rb_qat_autotune -- choose the GEMM kernels of the training layer for one shape: for each of
  * the three products of rb_qat_forward / rb_qat_backward with these sizes, leading dimensions
  * and types, times rocBLAS's default and every kernel rocBLAS lists for the problem on the
- * caller's buffers, and records the fastest for this device (process-wide; later calls with
- * the same shape use it). A setup call: it runs a few thousand products and synchronises
+ * caller's buffers (for the forward product, the library's matrix-core kernel as well, where
+ * it applies), and records the fastest for this device (process-wide; later calls with the
+ * same shape use it). A setup call: it runs a few thousand products and synchronises
  * `stream` before returning. X, dY and What are read; Y, dW and dX are overwritten with
  * unspecified values. Arguments as in rb_qat_forward / rb_qat_backward. Different kernels
  * may round differently (all accumulate in fp32). */

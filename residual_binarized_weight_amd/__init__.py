@@ -25,11 +25,12 @@ import torch
 
 from . import _lib
 from ._lib import (RB_F16, RB_F32, RB_BF16, RB_OP_CODEBOOK_GEMV, RB_OP_GEMM_SMALL, RB_OP_GEMV,
-                   RB_OP_QAT_BACKWARD, RB_OP_SVID_INIT, RbError, check, lib)
+                   RB_OP_QAT_BACKWARD, RB_OP_SVID_INIT, RB_QAT_ENGINE_AUTO, RB_QAT_ENGINE_MFMA,
+                   RB_QAT_ENGINE_ROCBLAS, RbError, check, lib)
 
 __all__ = ["pack", "gemv", "gemv_variant", "gemm_small", "codebook_encode", "codebook_gemv", "codebook_mstep",
            "codebook_distinct", "codebook_learn", "svid_init", "qat_derive",
-           "qat_forward", "qat_backward", "qat_autotune", "workspace",
+           "qat_forward", "qat_matmul", "qat_backward", "qat_autotune", "workspace",
            "workspace_bytes", "storage_bits_per_weight", "version", "RbError", "lib"]
 
 _DT = {torch.float32: RB_F32, torch.float16: RB_F16, torch.bfloat16: RB_BF16}
@@ -285,6 +286,20 @@ def qat_forward(W: torch.Tensor, g: torch.Tensor, h: torch.Tensor, X: torch.Tens
                                                _ptr_rows(What), What.stride(0), _ptr_rows(Y), _dt(Y.dtype), Y.stride(0),
                                                _stream()))
     return Y, planes, What
+
+
+def qat_matmul(X: torch.Tensor, What: torch.Tensor, Y: torch.Tensor | None = None, y_dtype=None,
+               engine: int = RB_QAT_ENGINE_AUTO):
+    """The coupled-training forward's product alone: Y [M][N] = X What^T for X [M][K] and What
+    [N][K] (fp16 or bf16, rows may be strided), Y fp32 or the operand type (default), on
+    `engine` (RB_QAT_ENGINE_AUTO, _MFMA: the library's matrix-core kernel, _ROCBLAS)."""
+    M, K = X.shape
+    N = What.shape[0]
+    Y = torch.empty((M, N), dtype=y_dtype or X.dtype, device=X.device) if Y is None else Y
+    check("rb_qat_matmul", lib.rb_qat_matmul(_ptr_rows(X), _dt(X.dtype), M, X.stride(0), _ptr_rows(What),
+                                             What.stride(0), N, K, _ptr_rows(Y), _dt(Y.dtype), Y.stride(0), engine,
+                                             _stream()))
+    return Y
 
 
 def qat_backward(dY: torch.Tensor, X: torch.Tensor, What: torch.Tensor, planes: torch.Tensor, g: torch.Tensor,

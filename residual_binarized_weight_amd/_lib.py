@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(HERE, "librb.so")
 
 RB_OK, RB_ERR_INVALID_ARG, RB_ERR_UNSUPPORTED, RB_ERR_MISALIGNED, RB_ERR_WORKSPACE, RB_ERR_HIP = range(6)
 RB_F32, RB_F16, RB_BF16 = 0, 1, 2
+RB_QAT_ENGINE_AUTO, RB_QAT_ENGINE_MFMA, RB_QAT_ENGINE_ROCBLAS = 0, 1, 2
 (RB_OP_PACK, RB_OP_GEMV, RB_OP_GEMM_SMALL, RB_OP_CODEBOOK_ENCODE, RB_OP_CODEBOOK_GEMV, RB_OP_SVID_INIT,
  RB_OP_QAT_BACKWARD) = range(7)
 
@@ -50,6 +51,8 @@ SIGNATURES = {
                                      _i64, _vp]),
     "rb_qat_forward": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, ctypes.c_int, _i64, _i64,
                                       _vp, _i64, _vp, _i64, _vp, ctypes.c_int, _i64, _vp]),
+    "rb_qat_matmul": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _vp, _i64, _i64, _i64, _vp, ctypes.c_int, _i64,
+                                     _i32, _vp]),
     "rb_qat_backward": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                                        _vp, _i32, _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _i64, _vp, _vp,
                                        _vp, _sz, _vp]),

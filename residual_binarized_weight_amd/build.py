@@ -27,7 +27,7 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-I", os.path.join(ROOT, "include")]
 
 SOURCES = ["rb_api.cpp", "rb_pack.hip", "rb_gemv.hip", "rb_gemv_nib.hip", "rb_gemm.hip", "rb_codebook.hip", "rb_svid.hip",
-           "rb_qat.hip", "rb_bench.hip", "rb_noalloc.hip"]
+           "rb_qat.hip", "rb_qat_gemm.hip", "rb_bench.hip", "rb_noalloc.hip"]
 
 
 def _compile(src: str) -> str:

@@ -387,6 +387,22 @@ rb_status rb_qat_backward(const void* dY, rb_dtype a_dtype, int64_t M, int64_t l
                                           static_cast<hipStream_t>(stream)));
 }
 
+rb_status rb_qat_matmul(const void* X, rb_dtype a_dtype, int64_t M, int64_t ldx, const void* What, int64_t ldwh,
+                        int64_t N, int64_t K, void* Y, rb_dtype y_dtype, int64_t ldy, int32_t engine, void* stream) {
+  if (!X || !What || !Y) return RB_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || M < 1 || N > kMaxDim || K > kMaxDim || M > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (ldx < K || ldx > kMaxDim || ldwh < K || ldwh > kMaxDim || ldy < N || ldy > kMaxDim) return RB_ERR_INVALID_ARG;
+  if (engine < RB_QAT_ENGINE_AUTO || engine > RB_QAT_ENGINE_ROCBLAS) return RB_ERR_INVALID_ARG;
+  if (!valid_dtype(a_dtype) || !valid_dtype(y_dtype)) return RB_ERR_INVALID_ARG;
+  if (!act_dtype(a_dtype) || (y_dtype != RB_F32 && y_dtype != a_dtype)) return RB_ERR_UNSUPPORTED;
+  if (!elem_aligned(X, a_dtype) || !elem_aligned(What, a_dtype) || !elem_aligned(Y, y_dtype)) return RB_ERR_MISALIGNED;
+  if (engine == RB_QAT_ENGINE_MFMA && !rb::qat_gemm_tn_supported(X, ldx, What, ldwh, M, N, K))
+    return RB_ERR_UNSUPPORTED;
+  log_call("rb_qat_matmul", N, K, M, engine);
+  return from_hip(rb::launch_qat_forward_gemm(X, a_dtype, M, ldx, What, ldwh, N, K, Y, y_dtype, ldy,
+                                              static_cast<hipStream_t>(stream), engine));
+}
+
 rb_status rb_qat_autotune(const void* X, const void* dY, rb_dtype a_dtype, int64_t M, int64_t ldx, int64_t lddy,
                           const void* What, int64_t ldwh, int64_t N, int64_t K, void* Y, rb_dtype y_dtype,
                           int64_t ldy, float* dW, int64_t lddw, void* dX, rb_dtype dx_dtype, int64_t lddx,

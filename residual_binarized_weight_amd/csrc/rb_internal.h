@@ -94,9 +94,16 @@ size_t qat_backward_workspace_bytes(int k, int64_t N, int64_t K);
 hipError_t launch_qat_derive(const float* W, int64_t N, int64_t K, int64_t ldw, int k, const float* g,
                              const float* h, uint32_t* planes, int64_t ldp, void* What, rb_dtype what_dtype,
                              int64_t ldwh, hipStream_t stream);
+// the forward product Y = X What^T: engine 0 the layer's choice (rocBLAS, or the matrix-core
+// kernel where rb_qat_autotune timed it at least as fast for the shape), 1 the matrix-core
+// kernel, 2 rocBLAS
 hipError_t launch_qat_forward_gemm(const void* X, rb_dtype a_dtype, int64_t M, int64_t ldx, const void* What,
                                    int64_t ldwh, int64_t N, int64_t K, void* Y, rb_dtype y_dtype, int64_t ldy,
-                                   hipStream_t stream);
+                                   hipStream_t stream, int engine = 0);
+// the matrix-core kernel of that product (rb_qat_gemm.hip) and the operands it takes
+bool qat_gemm_tn_supported(const void* X, int64_t ldx, const void* Wh, int64_t ldw, int64_t M, int64_t N, int64_t K);
+hipError_t launch_qat_gemm_tn(const void* X, rb_dtype a_dtype, int64_t ldx, const void* Wh, int64_t ldw, int64_t M,
+                              int64_t N, int64_t K, void* Y, rb_dtype y_dtype, int64_t ldy, hipStream_t s);
 hipError_t launch_qat_backward(const void* dY, rb_dtype a_dtype, int64_t M, int64_t lddy, const void* X, int64_t ldx,
                                const void* What, int64_t ldwh, const uint32_t* planes, int64_t ldp, const float* g,
                                const float* h, int k, int64_t N, int64_t K, float* dW, int64_t lddw, void* dX,

@@ -15,8 +15,10 @@
 //   qat_scale_grad_kernel  one pass over dW and the planes: per 256-column strip row partials
 //                          of dg and per 256-row tile column partials of dh, fixed order.
 //   qat_scale_grad_finish  the partials summed in a fixed order.
-// The three dense products (Y, dW, dX) are plain GEMMs on matrix cores, run by rocBLAS with
-// fp32 accumulation on one handle per device.
+// The three dense products (Y, dW, dX) are rocBLAS GEMMs with fp32 accumulation on one handle
+// per device; the forward product Y = X What^T also has this library's matrix-core kernel
+// (rb_qat_gemm.hip), which rb_qat_forward uses for a shape where rb_qat_autotune timed it at
+// least as fast as rocBLAS's best.
 #define ROCBLAS_BETA_FEATURES_API  // rocblas_gemm_ex_get_solutions
 #include <rocblas/rocblas.h>
 
@@ -24,6 +26,7 @@
 #include <array>
 #include <cstdio>
 #include <cstdlib>
+#include <functional>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -311,9 +314,11 @@ struct GemmShape {
 };
 
 // Solutions chosen by rb_qat_autotune, per device and shape; a shape not in the table runs
-// rocBLAS's default choice.
+// rocBLAS's default choice. g_blas_slower holds the forward shapes for which the matrix-core
+// kernel of this library was timed at least as fast as rocBLAS's best.
 using GemmKey = std::array<int64_t, 11>;
 std::map<GemmKey, int32_t> g_tuned;
+std::map<GemmKey, bool> g_blas_slower;
 
 GemmKey gemm_key(int dev, const GemmShape& s) {
   return {dev, (int64_t)s.ta, (int64_t)s.tb, s.m, s.n, s.kk, s.lda, s.ldb, s.ldc, (int64_t)s.at, (int64_t)s.ct};
@@ -354,9 +359,11 @@ float time_solution(rocblas_handle hd, const GemmShape& s, const void* A, const 
 }
 
 // Times rocBLAS's default and every solution it lists for the shape (2 runs each), re-times
-// the 8 fastest (5 runs each) and records the fastest in g_tuned. Caller holds g_blas_mu.
+// the 8 fastest (5 runs each) and records the fastest in g_tuned; with `mine` (the forward
+// product on the matrix-core kernel of this library) that kernel is timed as well (5 runs)
+// and g_blas_slower records whether it was at least as fast. Caller holds g_blas_mu.
 hipError_t autotune_locked(rocblas_handle hd, int dev, const GemmShape& s, const void* A, const void* B, void* C,
-                           hipStream_t stream) {
+                           hipStream_t stream, const std::function<hipError_t()>& mine = nullptr) {
   const float one = 1.0f, zero = 0.0f;
   rocblas_int count = 0;
 #pragma clang diagnostic push
@@ -395,10 +402,24 @@ hipError_t autotune_locked(rocblas_handle hd, int dev, const GemmShape& s, const
     tv.first = t > 0.0f ? t : 1e30f;
   }
   std::sort(timed.begin(), timed.end());
+  float t_mine = -1.0f;
+  if (mine && mine() == hipSuccess && hipEventRecord(e0, stream) == hipSuccess) {
+    bool ok = true;
+    for (int r = 0; r < 5 && ok; ++r) ok = mine() == hipSuccess;
+    float ms = 0.0f;
+    if (ok && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+        hipEventElapsedTime(&ms, e0, e1) == hipSuccess)
+      t_mine = ms / 5.0f;
+  }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
-  if (timed.empty()) return blas_fail("autotune", rocblas_status_not_implemented);
-  g_tuned[gemm_key(dev, s)] = timed.front().second;
+  const GemmKey key = gemm_key(dev, s);
+  if (mine) g_blas_slower[key] = t_mine > 0.0f && (timed.empty() || t_mine <= timed.front().first);
+  if (timed.empty()) {
+    if (mine && g_blas_slower[key]) return hipStreamSynchronize(stream);
+    return blas_fail("autotune", rocblas_status_not_implemented);
+  }
+  g_tuned[key] = timed.front().second;
   return hipStreamSynchronize(stream);
 }
 
@@ -497,13 +518,34 @@ GemmShape shape_dx(rb_dtype at, int64_t M, int64_t ldwh, int64_t lddy, int64_t N
 
 hipError_t launch_qat_forward_gemm(const void* X, rb_dtype a_dtype, int64_t M, int64_t ldx, const void* What,
                                    int64_t ldwh, int64_t N, int64_t K, void* Y, rb_dtype y_dtype, int64_t ldy,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, int engine) {
+  const bool mine = qat_gemm_tn_supported(X, ldx, What, ldwh, M, N, K);
+  if (engine == 1) {
+    if (!mine) return hipErrorNotSupported;
+    return launch_qat_gemm_tn(X, a_dtype, ldx, What, ldwh, M, N, K, Y, y_dtype, ldy, stream);
+  }
+  const GemmShape sh = shape_y(a_dtype, M, ldx, ldwh, N, K, y_dtype, ldy);
+  if (engine == 0 && mine) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    bool mine_faster = false;
+    {
+      std::lock_guard<std::mutex> lock(g_blas_mu);
+      const auto it = g_blas_slower.find(gemm_key(dev, sh));
+      mine_faster = it != g_blas_slower.end() && it->second;
+    }
+    if (mine_faster) return launch_qat_gemm_tn(X, a_dtype, ldx, What, ldwh, M, N, K, Y, y_dtype, ldy, stream);
+  }
   std::lock_guard<std::mutex> lock(g_blas_mu);
   rocblas_handle hd;
   int dev;
   hipError_t e = blas_handle_locked(stream, &hd, &dev);
   if (e != hipSuccess) return e;
-  return gemm_locked(hd, dev, shape_y(a_dtype, M, ldx, ldwh, N, K, y_dtype, ldy), What, X, Y);
+  const auto it = g_tuned.find(gemm_key(dev, sh));
+  const int32_t sol = it == g_tuned.end() ? 0 : it->second;
+  const rocblas_status st = gemm_run(hd, sh, What, X, Y, sol);
+  return blas_ok(st) ? hipSuccess : blas_fail("gemm_ex", st);
 }
 
 // the two backward products, then the scale gradients from dW and the planes
@@ -539,7 +581,10 @@ hipError_t launch_qat_autotune(const void* X, const void* dY, rb_dtype a_dtype, 
   int dev;
   hipError_t e = blas_handle_locked(stream, &hd, &dev);
   if (e != hipSuccess) return e;
-  e = autotune_locked(hd, dev, shape_y(a_dtype, M, ldx, ldwh, N, K, y_dtype, ldy), What, X, Y, stream);
+  std::function<hipError_t()> mine = nullptr;
+  if (qat_gemm_tn_supported(X, ldx, What, ldwh, M, N, K))
+    mine = [&]() { return launch_qat_gemm_tn(X, a_dtype, ldx, What, ldwh, M, N, K, Y, y_dtype, ldy, stream); };
+  e = autotune_locked(hd, dev, shape_y(a_dtype, M, ldx, ldwh, N, K, y_dtype, ldy), What, X, Y, stream, mine);
   if (e != hipSuccess) return e;
   e = autotune_locked(hd, dev, shape_dw(a_dtype, M, ldx, lddy, N, K, lddw), X, dY, dW, stream);
   if (e != hipSuccess) return e;

@@ -389,6 +389,43 @@ def test_qat_autotune_rejects(kw, status):
     assert _qat_autotune(**kw) == status
 
 
+def _qat_matmul(**kw):
+    a = dict(X=P, adt=_lib.RB_BF16, M=8, ldx=64, What=P, ldwh=64, N=16, K=64, Y=P, ydt=_lib.RB_F32, ldy=16,
+             engine=_lib.RB_QAT_ENGINE_MFMA, stream=None)
+    a.update(kw)
+    return L.rb_qat_matmul(a["X"], a["adt"], a["M"], a["ldx"], a["What"], a["ldwh"], a["N"], a["K"], a["Y"],
+                           a["ydt"], a["ldy"], a["engine"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(What=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(Y=None), _lib.RB_ERR_INVALID_ARG),
+    (dict(M=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(N=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(K=0), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldx=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldwh=63), _lib.RB_ERR_INVALID_ARG),
+    (dict(ldy=15), _lib.RB_ERR_INVALID_ARG),
+    (dict(engine=3), _lib.RB_ERR_INVALID_ARG),
+    (dict(engine=-1), _lib.RB_ERR_INVALID_ARG),
+    (dict(adt=7), _lib.RB_ERR_INVALID_ARG),
+    (dict(adt=_lib.RB_F32), _lib.RB_ERR_UNSUPPORTED),
+    (dict(ydt=_lib.RB_F16), _lib.RB_ERR_UNSUPPORTED),   # operands are bf16 here
+    (dict(X=P_ODD), _lib.RB_ERR_MISALIGNED),
+    (dict(Y=P2), _lib.RB_ERR_MISALIGNED),
+    # the matrix-core engine's layout: 16-byte aligned operands, strides multiples of 8, K of 32
+    (dict(K=60, ldx=64, ldwh=64), _lib.RB_ERR_UNSUPPORTED),
+    (dict(K=40, ldx=64, ldwh=64), _lib.RB_ERR_UNSUPPORTED),  # a multiple of 8, not of 32
+    (dict(ldx=68), _lib.RB_ERR_UNSUPPORTED),
+    (dict(ldwh=66), _lib.RB_ERR_UNSUPPORTED),
+    (dict(What=P2), _lib.RB_ERR_UNSUPPORTED),
+    (dict(M=(1 << 24), ldx=64), _lib.RB_ERR_UNSUPPORTED),     # 2^30 elements of X
+])
+def test_qat_matmul_rejects(kw, status):
+    assert _qat_matmul(**kw) == status
+
+
 def test_codebook_learn_workspace_bytes():
     # the largest of: 3 c counters + 64 block totals + one word per block (standalone M-step),
     # c (v + 1) counters (learning loop), the 2^v-bit bitmap (distinct count)

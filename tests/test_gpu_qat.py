@@ -121,7 +121,7 @@ def test_derive_strided_rows_and_padding():
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("ydt", ["f32", "act"])
-@pytest.mark.parametrize("M,N,K,k", [(1, 96, 300, 2), (7, 130, 1000, 1), (64, 257, 640, 3)])
+@pytest.mark.parametrize("M,N,K,k", [(1, 96, 300, 2), (7, 130, 1024, 1), (64, 257, 640, 3), (130, 300, 1000, 2)])
 def test_forward_matches_oracle(dt, ydt, M, N, K, k):
     W, g, h = layer(550 + M, N, K, k)
     X, Xv = act(wl.activations(550, M, K, dtype=np.float32), dt)

@@ -529,7 +529,8 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const uint32_t w = (uint32_t)(kSbGroupWords * j + lane);
-      const uint32_t voff = w < Kw ? row_off + 4u * w : kNibOob;
+      // with a tail every group word lies inside the row
+      const uint32_t voff = (TAIL || w < Kw) ? row_off + 4u * w : kNibOob;
 #pragma unroll
       for (int i = 0; i < KP; ++i) wd[r][j][i] = buf_u32(rp, voff, (uint32_t)i * (uint32_t)N * ldp_b);
     }
@@ -551,7 +552,7 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
     for (int c = 0; c < 4; ++c) {
       float v = __half2float(__ushort_as_half((uint16_t)((xq[b][c >> 1] >> (16 * (c & 1))) & 0xffffu)));
       if constexpr (HM) v *= __half2float(__ushort_as_half((uint16_t)((hq[b][c >> 1] >> (16 * (c & 1))) & 0xffffu)));
-      xv[c] = 4u * q + (uint32_t)c < Kc ? v : 0.0f;
+      xv[c] = (TAIL || 4u * q + (uint32_t)c < Kc) ? v : 0.0f;  // with a tail every table column is < K
     }
     const float s01 = xv[0] + xv[1], d01 = xv[0] - xv[1];
     const float s23 = xv[2] + xv[3], d23 = xv[2] - xv[3];
@@ -559,7 +560,10 @@ __global__ __launch_bounds__(64 * kNibWaves) __attribute__((amdgpu_waves_per_eu(
     const float hi[4] = {-s23, d23, -d23, s23};
     const uint32_t w = q >> 3, i = q & 7, wl = w & 63u;
     const uint32_t slot = 8u * wl + (i ^ (((wl >> 2) ^ ((wl >> 5) & 1u)) & 7u));
-    const uint32_t base = (w >> 6) * kSbGroupBytes + slot * 4u;
+    uint32_t base = (w >> 6) * kSbGroupBytes + slot * 4u;
+    // opaque: the 16 entry rows are then immediate offsets (at most 30 KB) from one address
+    // register; otherwise groups past 64 KB had an OR per write
+    asm volatile("" : "+v"(base));
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       *(lds_f32p*)(size_t)(((uint32_t)e << kSbSH) + base) = lo[e & 3] + hi[e >> 2];

@@ -773,6 +773,8 @@ def main() -> int:
     ap.add_argument("--summarize-trace", metavar="DIR", help="per-dispatch durations of the product kernel "
                                                               "from rocprofv3 kernel-trace CSVs")
     ap.add_argument("--kernel", default=PRODUCT_KERNEL, help="kernel name for --summarize-trace")
+    ap.add_argument("--only-row", choices=["qat"], help="run one row's measurement alone (for profiling) "
+                                                        "and print it as the JSON line")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
@@ -793,6 +795,9 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_row == "qat":
+        print(json.dumps(measure_qat_step(torch, np, rb, wl, dev, with_oracle=False)))
+        return 0
     N, K, k = N_ROWS, K_COLS, K_PLANES
     Kw = (K + 31) // 32
     ldp = (Kw + 31) // 32 * 32          # rows padded to 128-byte multiples

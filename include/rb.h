@@ -380,7 +380,7 @@ rb_status rb_qat_forward(const float* W, int64_t N, int64_t K, int64_t ldw, int3
  *   accumulation of the exact products, Y in RB_F32 or a_dtype (rounded to nearest even).
  *   Rows of Y are M, columns N; elements past N in a row are not written.
  *   engine  RB_QAT_ENGINE_AUTO: as rb_qat_forward chooses; RB_QAT_ENGINE_MFMA: the library's
- *           matrix-core kernel (v_mfma_f32_32x32x16 on 128 x 256 output tiles), which needs
+ *           matrix-core kernel (v_mfma_f32_32x32x16, 8 waves per 128 x 256 output tile), which needs
  *           X and What 16-byte aligned, ldx and ldwh multiples of 8, K a multiple of 32, and
  *           M*ldx and N*ldwh below 2^30 elements (else RB_ERR_UNSUPPORTED); RB_QAT_ENGINE_ROCBLAS: rocBLAS
  *           (the autotuned kernel if rb_qat_autotune chose one). The engines sum in different

@@ -5,16 +5,17 @@
 // X [M][K] and What [N][K] in fp16 or bf16 (both K-contiguous), fp32 accumulation, Y in fp32
 // or the operand type.
 //
-// Tiles. A block is 4 waves and owns a 128 (batch rows) x 256 (weight rows) tile of Y; wave w
-// owns rows 64 (w & 1) .. +63 of the batch tile and 128 (w >> 1) .. +127 of the weight tile,
-// i.e. 2 x 4 output tiles of 32 x 32 (v_mfma_f32_32x32x16_{bf16,f16}, 8 accumulators of 16
-// fp32 per lane). K advances in tiles of 32 columns held in a ring of 6 LDS stages (24 KB
+// Tiles. A block is 8 waves (two per SIMD, so one wave's LDS reads and barrier waits overlap
+// the other's MFMAs) and owns a 128 (batch rows) x 256 (weight rows) tile of Y; wave w owns
+// rows 64 (w & 1) .. +63 of the batch tile and 64 (w >> 1) .. +63 of the weight tile, i.e.
+// 2 x 2 output tiles of 32 x 32 (v_mfma_f32_32x32x16_{bf16,f16}, 4 accumulators of 16 fp32
+// per lane). K advances in tiles of 32 columns held in a ring of 6 LDS stages (24 KB
 // each: the 128 x 32 slice of X, then the 256 x 32 slice of What). The stages are filled by
 // direct-to-LDS buffer loads (16 bytes per lane, 1 KB per wave instruction = 16 rows of 64
 // bytes), issued 5 tiles ahead of the multiplication: a wave waits only for its own loads of
 // the tile it is about to read (vmcnt), then one barrier per tile makes every wave's loads
 // visible and frees the stage of the tile before. Each tile's fragments are read from LDS one
-// tile ahead of its MFMAs; every fragment read feeds 2 (What) or 4 (X) MFMAs.
+// tile ahead of its MFMAs; every fragment read feeds 2 MFMAs.
 //
 // Stage layout: row r takes 64 bytes, its 16-byte chunk c (columns 8c .. 8c+7) in slot
 // c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which spreads the rows of a fragment read over
@@ -46,9 +47,9 @@ constexpr int kQABytes = kQM * kQRowB;    // X slice: 8 KB
 constexpr int kQStage = kQABytes + kQN * kQRowB;  // + What slice: 24 KB
 constexpr int kQStages = 6;               // ring depth: 144 KB of LDS
 constexpr int kQLead = kQStages - 1;      // tiles loaded ahead
-constexpr int kQThreads = 256;
+constexpr int kQThreads = 512;
 constexpr int kQGroups = kQStage / 1024;  // 1 KB load groups per tile: 24
-constexpr int kQGroupsPerWave = kQGroups / (kQThreads / 64);  // 6
+constexpr int kQGroupsPerWave = kQGroups / (kQThreads / 64);  // 3
 constexpr uint32_t kQOob = 0x80000000u;  // an offset past every resource below
 constexpr int kQXcds = 8;
 
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kQThreads) void qat_gemm_tn_kernel(const uint16_t* 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1, wn = wave >> 1;  // wn 0..3
   const int lr = lane & 31, hh = lane >> 5;
 
   // buffer resources start at the block's first row; a row past M (N) lies past the end
@@ -117,14 +118,14 @@ __global__ __launch_bounds__(kQThreads) void qat_gemm_tn_kernel(const uint16_t* 
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(X + m0 * ldx, (uint32_t)(ma * ldx * 2));
   const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(Wh + n0 * ldw, (uint32_t)(na * ldw * 2));
 
-  // load group G = wave + 4 i of a tile (1 KB at LDS offset 1024 G): groups 0..7 are X rows
+  // load group G = wave + 8 i of a tile (1 KB at LDS offset 1024 G): groups 0..7 are X rows
   // 16 G .. +15, groups 8..23 What rows 16 (G - 8) .. +15. Lane l fills slot l % 4 of row
   // l / 4 of the group with the chunk that belongs there: c = slot ^ f(row).
   auto swz = [](uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; };
   uint32_t goff[kQGroupsPerWave];
 #pragma unroll
   for (int i = 0; i < kQGroupsPerWave; ++i) {
-    const int G = wave + 4 * i;
+    const int G = wave + 8 * i;
     const uint32_t r = (uint32_t)(16 * (G < 8 ? G : G - 8) + (lane >> 2));
     goff[i] = (uint32_t)((int64_t)r * (G < 8 ? ldx : ldw) * 2 + ((lane & 3) ^ swz(r)) * 16);
   }
@@ -134,24 +135,24 @@ __global__ __launch_bounds__(kQThreads) void qat_gemm_tn_kernel(const uint16_t* 
     uint8_t* const base = q_smem + (int)(tk % kQStages) * kQStage;
 #pragma unroll
     for (int i = 0; i < kQGroupsPerWave; ++i) {
-      const int G = wave + 4 * i;
+      const int G = wave + 8 * i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(G < 8 ? rx : rw, (q_lds_void*)(base + G * 1024), 16,
                                                live ? goff[i] + kb : kQOob, 0, 0, 0);
     }
   };
 
-  q_f16x acc[2][4];
+  q_f16x acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (q_f16x){};
+    for (int j = 0; j < 2; ++j) acc[i][j] = (q_f16x){};
 
   // fragment rows of the lane (f is the same for rows 32 apart)
-  const uint32_t ra = (uint32_t)(wm * 64 + lr), rb = (uint32_t)(wn * 128 + lr);
+  const uint32_t ra = (uint32_t)(wm * 64 + lr), rb = (uint32_t)(wn * 64 + lr);
   const uint32_t sa = swz(ra), sb = swz(rb);
   const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)q_smem;
-  // two fragment sets: a tile's 2 steps of 16 columns, 2 X and 4 What fragments each
-  q_u4 fr[2][2][6];
+  // two fragment sets: a tile's 2 steps of 16 columns, 2 X and 2 What fragments each
+  q_u4 fr[2][2][4];
   auto read = [&](int p, int64_t tk) {  // all fragments of tile tk into set p
     const uint32_t st = lds0 + (uint32_t)((tk % kQStages) * kQStage);
 #pragma unroll
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kQThreads) void qat_gemm_tn_kernel(const uint16_t* 
 #pragma unroll
       for (int i = 0; i < 2; ++i) fr[p][s][i] = q_lds_read(st + (ra + 32u * i) * kQRowB + 16u * (c ^ sa));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fr[p][s][2 + j] = q_lds_read(st + kQABytes + (rb + 32u * j) * kQRowB + 16u * (c ^ sb));
+      for (int j = 0; j < 2; ++j) fr[p][s][2 + j] = q_lds_read(st + kQABytes + (rb + 32u * j) * kQRowB + 16u * (c ^ sb));
     }
   };
 
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kQThreads) void qat_gemm_tn_kernel(const uint16_t* 
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = QMfma<BF16>::run(fr[p][s][i], fr[p][s][2 + j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = QMfma<BF16>::run(fr[p][s][i], fr[p][s][2 + j], acc[i][j]);
     __builtin_amdgcn_sched_barrier(0);
   };
   // pairs of trips with no branch inside, then the last odd one
@@ -209,8 +210,8 @@ __global__ __launch_bounds__(kQThreads) void qat_gemm_tn_kernel(const uint16_t* 
 
   // D: lane column lr is weight row n, element e batch row 8 (e / 4) + 4 hh + e % 4
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 128 + j * 32 + lr;
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = n0 + wn * 64 + j * 32 + lr;
     if (n >= N) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {

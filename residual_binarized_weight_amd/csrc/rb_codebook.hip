@@ -337,102 +337,168 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = val;
 }
 
-// M-step as a counting sort of the blocks by codeword, then a vote per codeword:
-//   hist     members[c] = number of blocks with idx == c              (one atomic per block)
-//   offsets  start[c] = exclusive prefix sum of members (one block)
-//   scatter  each block's pattern goes to bucket[start[c] + cursor[c]++] (one atomic per block)
-//   vote     thread c counts each bit over its bucket and sets the bits with 2 ones >= members
-//            (sum of +-1 >= 0: ties go to +1); a codeword without members keeps its value.
-// The order inside a bucket depends on the scheduling, the counts do not: the result is exact.
-__global__ __launch_bounds__(256) void mstep_hist_kernel(const uint16_t* __restrict__ idx, int64_t total, int c,
-                                                         uint32_t* __restrict__ members) {
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const uint32_t id = idx[e];
-    if (id < (uint32_t)c) atomicAdd(members + id, 1u);  // indices must be < c; others are skipped
-  }
-}
+// M-step as one radix pass of the blocks on the high byte of their codeword index, then a
+// count per codeword in LDS (no global atomics; each index is read twice):
+//   hist     chunk q of 8192 blocks: H[bucket][q] = its blocks with idx >> 8 == bucket
+//   scan     per bucket, H[bucket][.] becomes the exclusive prefix over the chunks, and
+//            btot[bucket] the bucket's total
+//   scatter  chunk q writes each block's position e into E at the bucket's start + H[bucket][q]
+//            + a rank from an LDS counter (the order inside a bucket is the scheduler's)
+//   vote     block b reads bucket b (codewords 256 b .. 256 b + 255), counts members and their
+//            bits with LDS atomics, and sets the bits with 2 ones >= members (ties go to +1);
+//            a codeword without members keeps its value.
+// Integer counts, so the result does not depend on any order: exact and deterministic.
+constexpr int kMsChunk = 8192;    // blocks per histogram / scatter chunk
+constexpr int kMsThreads = 256;   // one thread per bucket in the chunk kernels
+constexpr int kMsBuckets = 256;   // idx >> 8
 
-constexpr int kScanThreads = 1024;
-
-// start[c] = sum of members[0..c), in two passes: each block of 1024 codewords scans its own
-// range (exclusive, in LDS) and writes its total; then each block adds the totals of the
-// blocks before it.
-__global__ __launch_bounds__(kScanThreads) void mstep_scan_local_kernel(const uint32_t* __restrict__ members, int c,
-                                                                        uint32_t* __restrict__ start,
-                                                                        uint32_t* __restrict__ totals) {
-  __shared__ uint32_t scan[2][kScanThreads];
-  const int t = threadIdx.x;
-  const int i = blockIdx.x * kScanThreads + t;
-  const uint32_t mine = i < c ? members[i] : 0u;
-  scan[0][t] = mine;
+// buckets' exclusive starts from their totals, in LDS (one thread per bucket)
+__device__ __forceinline__ void ms_bucket_starts(const uint32_t* __restrict__ btot, uint32_t* start, int tid) {
+  start[tid] = btot[tid];
   __syncthreads();
-  int src = 0;
-  for (int off = 1; off < kScanThreads; off <<= 1) {  // inclusive scan, double-buffered
-    scan[src ^ 1][t] = scan[src][t] + (t >= off ? scan[src][t - off] : 0u);
-    src ^= 1;
+  for (int off = 1; off < kMsBuckets; off <<= 1) {  // inclusive scan in place (Hillis-Steele)
+    const uint32_t add = tid >= off ? start[tid - off] : 0u;
+    __syncthreads();
+    start[tid] += add;
     __syncthreads();
   }
-  if (i < c) start[i] = scan[src][t] - mine;
-  if (t == kScanThreads - 1) totals[blockIdx.x] = scan[src][t];
+  const uint32_t incl = start[tid];
+  __syncthreads();
+  start[tid] = incl - btot[tid];
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(kScanThreads) void mstep_scan_add_kernel(const uint32_t* __restrict__ totals, int c,
-                                                                      uint32_t* __restrict__ start) {
-  uint32_t pre = 0u;
-  for (unsigned b = 0; b < blockIdx.x; ++b) pre += totals[b];  // at most 63 totals
-  const int i = blockIdx.x * kScanThreads + threadIdx.x;
-  if (i < c) start[i] += pre;
+__global__ __launch_bounds__(kMsThreads) void mstep_hist_kernel(const uint16_t* __restrict__ idx, int64_t total,
+                                                                int c, int64_t nchunk, uint32_t* __restrict__ H) {
+  __shared__ uint32_t h[kMsBuckets];
+  const int tid = threadIdx.x;
+  h[tid] = 0u;
+  __syncthreads();
+  const int64_t e0 = (int64_t)blockIdx.x * kMsChunk;
+#pragma unroll 4
+  for (int k = 0; k < kMsChunk / kMsThreads; ++k) {
+    const int64_t e = e0 + k * kMsThreads + tid;
+    if (e < total) {
+      const uint32_t id = idx[e];
+      if (id < (uint32_t)c) atomicAdd(&h[id >> 8], 1u);  // indices >= c are skipped
+    }
+  }
+  __syncthreads();
+  H[(int64_t)tid * nchunk + blockIdx.x] = h[tid];
 }
 
-__global__ __launch_bounds__(256) void mstep_scatter_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
-                                                            int64_t N, int64_t K, int v,
-                                                            const uint16_t* __restrict__ idx, int c,
-                                                            const uint32_t* __restrict__ start,
-                                                            uint32_t* __restrict__ cursor,
-                                                            uint32_t* __restrict__ bucket) {
+// block b: exclusive prefix of H[b][0 .. nchunk) over the chunks, 256 at a time with a carry
+__global__ __launch_bounds__(kMsThreads) void mstep_scan_kernel(uint32_t* __restrict__ H, int64_t nchunk,
+                                                                uint32_t* __restrict__ btot) {
+  __shared__ uint32_t t[kMsThreads];
+  const int tid = threadIdx.x;
+  uint32_t* __restrict__ row = H + (int64_t)blockIdx.x * nchunk;
+  uint32_t carry = 0u;
+  for (int64_t q0 = 0; q0 < nchunk; q0 += kMsThreads) {
+    const int64_t q = q0 + tid;
+    const uint32_t mine = q < nchunk ? row[q] : 0u;
+    t[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < kMsThreads; off <<= 1) {
+      const uint32_t add = tid >= off ? t[tid - off] : 0u;
+      __syncthreads();
+      t[tid] += add;
+      __syncthreads();
+    }
+    if (q < nchunk) row[q] = carry + t[tid] - mine;
+    carry += t[kMsThreads - 1];
+    __syncthreads();
+  }
+  if (tid == 0) btot[blockIdx.x] = carry;
+}
+
+__global__ __launch_bounds__(kMsThreads) void mstep_scatter_kernel(const uint16_t* __restrict__ idx, int64_t total,
+                                                                   int c, int64_t nchunk,
+                                                                   const uint32_t* __restrict__ H,
+                                                                   const uint32_t* __restrict__ btot,
+                                                                   uint32_t* __restrict__ E) {
+  __shared__ uint32_t cur[kMsBuckets];
+  const int tid = threadIdx.x;
+  ms_bucket_starts(btot, cur, tid);
+  cur[tid] += H[(int64_t)tid * nchunk + blockIdx.x];
+  __syncthreads();
+  const int64_t e0 = (int64_t)blockIdx.x * kMsChunk;
+#pragma unroll 4
+  for (int k = 0; k < kMsChunk / kMsThreads; ++k) {
+    const int64_t e = e0 + k * kMsThreads + tid;
+    if (e < total) {
+      const uint32_t id = idx[e];
+      if (id < (uint32_t)c) E[atomicAdd(&cur[id >> 8], 1u)] = (uint32_t)e;
+    }
+  }
+}
+
+constexpr int kMsVoteThreads = 1024;  // the vote's block: the bucket's members are dealt over its threads
+constexpr int kMsVoteUnroll = 4;      // members in flight per thread
+
+__global__ __launch_bounds__(kMsVoteThreads) void mstep_vote_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
+                                                                    int64_t K, int v, const uint16_t* __restrict__ idx,
+                                                                    const uint32_t* __restrict__ E,
+                                                                    const uint32_t* __restrict__ btot, int c,
+                                                                    uint32_t* __restrict__ codebook,
+                                                                    uint32_t* __restrict__ counts) {
+  __shared__ uint32_t cnt[kMsBuckets * 33];  // [codeword][v + 1]: bit counts, then members
+  __shared__ uint32_t start[kMsBuckets];
+  const int tid = threadIdx.x;
+  const int stride = v + 1;
+  for (int i = tid; i < kMsBuckets * stride; i += kMsVoteThreads) cnt[i] = 0u;
+  if (tid < kMsBuckets) {  // the bucket starts, by the first 256 threads (all threads pass the barriers)
+    start[tid] = btot[tid];
+  }
+  __syncthreads();
+  for (int off = 1; off < kMsBuckets; off <<= 1) {
+    const uint32_t add = (tid < kMsBuckets && tid >= off) ? start[tid - off] : 0u;
+    __syncthreads();
+    if (tid < kMsBuckets) start[tid] += add;
+    __syncthreads();
+  }
   const int64_t nb = (K + v - 1) / v;
-  const int64_t total = N * nb;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const uint32_t id = idx[e];
-    if (id >= (uint32_t)c) continue;
-    const int64_t n = e / nb;
-    const uint32_t b = extract_block(plane + n * ldp, K, (e - n * nb) * v, v);
-    bucket[start[id] + atomicAdd(cursor + id, 1u)] = b;
-  }
-}
-
-// one wave per codeword: its bucket is read 64 blocks at a time and each bit's count is the
-// popcount of a ballot; bits with 2 ones >= members are set (ties go to +1)
-__global__ __launch_bounds__(256) void mstep_vote_kernel(const uint32_t* __restrict__ members,
-                                                         const uint32_t* __restrict__ start,
-                                                         const uint32_t* __restrict__ bucket, int c, int v,
-                                                         uint32_t* __restrict__ codebook,
-                                                         uint32_t* __restrict__ counts) {
-  const int lane = threadIdx.x & 63;
-  const int id = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (id >= c) return;  // uniform per wave
-  const uint32_t n = members[id];
-  if (counts && lane == 0) counts[id] = n;
-  if (n == 0) return;
-  const uint32_t* __restrict__ bk = bucket + start[id];
-  uint32_t ones[32];
+  const uint32_t m = btot[blockIdx.x];
+  const uint32_t s0 = start[blockIdx.x] - m;  // inclusive prefix minus own total
+  // members kMsVoteUnroll at a time per thread: the position, index and pattern loads of all of
+  // them are issued before any count
+  for (uint32_t q0 = 0; q0 < m; q0 += kMsVoteThreads * kMsVoteUnroll) {
+    int64_t e[kMsVoteUnroll];
+    bool live[kMsVoteUnroll];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) ones[t] = 0u;
-  for (uint32_t j0 = 0; j0 < n; j0 += 64) {
-    const bool ok = j0 + (uint32_t)lane < n;
-    const uint32_t b = ok ? bk[j0 + lane] : 0u;
+    for (int u = 0; u < kMsVoteUnroll; ++u) {
+      const uint32_t q = q0 + (uint32_t)(u * kMsVoteThreads + tid);
+      live[u] = q < m;
+      e[u] = live[u] ? (int64_t)E[s0 + q] : 0;
+    }
+    uint32_t r[kMsVoteUnroll], b[kMsVoteUnroll];
 #pragma unroll
-    for (int t = 0; t < 32; ++t)
-      if (t < v) ones[t] += (uint32_t)__popcll(__ballot((b >> t) & 1u));
+    for (int u = 0; u < kMsVoteUnroll; ++u) {
+      r[u] = (uint32_t)idx[e[u]] & 0xffu;
+      const int64_t n = e[u] / nb;
+      b[u] = extract_block(plane + n * ldp, K, (e[u] - n * nb) * v, v);
+    }
+#pragma unroll
+    for (int u = 0; u < kMsVoteUnroll; ++u) {
+      if (!live[u]) continue;
+      uint32_t* row = cnt + r[u] * (uint32_t)stride;
+      atomicAdd(row + v, 1u);
+      for (int t = 0; t < v; ++t)
+        if ((b[u] >> t) & 1u) atomicAdd(row + t, 1u);
+    }
   }
+  __syncthreads();
+  if (tid >= kMsBuckets) return;
+  const uint32_t id = blockIdx.x * (uint32_t)kMsBuckets + (uint32_t)tid;
+  if (id >= (uint32_t)c) return;
+  const uint32_t n = cnt[tid * stride + v];
+  if (counts) counts[id] = n;
+  if (n == 0u) return;
   uint32_t w = 0u;
-#pragma unroll
-  for (int t = 0; t < 32; ++t)
-    if (t < v && 2ull * ones[t] >= n) w |= 1u << t;
-  if (lane == 0) codebook[id] = w;
+  for (int t = 0; t < v; ++t) w |= (2ull * cnt[tid * stride + t] >= n ? 1u : 0u) << t;
+  codebook[id] = w;
 }
 
-// the vote from the counters cnt[c][v + 1] filled by the counting E-step
 __global__ __launch_bounds__(256) void mstep_vote_counts_kernel(const uint32_t* __restrict__ cnt, int c, int v,
                                                                 uint32_t* __restrict__ codebook) {
   const int id = blockIdx.x * 256 + threadIdx.x;
@@ -623,12 +689,12 @@ hipError_t launch_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, i
   return hipGetLastError();
 }
 
-// workspace, used by one step at a time: the standalone M-step's members, start, cursor ([c]
-// each), block totals (64) and bucket (one word per block); the learning loop's counters
-// [c][v + 1]; the 2^v-bit bitmap of the distinct count
+// workspace, used by one step at a time: the standalone M-step's block list (one word per
+// block), chunk histograms (256 per 8192 blocks) and bucket totals (256); the learning loop's
+// counters [c][v + 1]; the 2^v-bit bitmap of the distinct count
 size_t codebook_learn_workspace_bytes(int64_t N, int64_t K, int c, int v) {
   const size_t blocks = (size_t)N * (size_t)((K + v - 1) / v);
-  const size_t mstep = 4u * (3u * (size_t)c + 64u + blocks);
+  const size_t mstep = 4u * (blocks + (size_t)kMsBuckets * ((blocks + kMsChunk - 1) / kMsChunk) + kMsBuckets);
   const size_t counters = 4u * (size_t)c * (size_t)(v + 1);
   const size_t bitmap = v <= 24 ? ((size_t)1 << (v > 5 ? v - 3 : 2)) : 0u;
   const size_t table = codebook_use_table(N, K, c, v) ? codebook_table_bytes(v) : 0u;
@@ -640,19 +706,18 @@ size_t codebook_learn_workspace_bytes(int64_t N, int64_t K, int c, int v) {
 hipError_t launch_codebook_mstep(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
                                  const uint16_t* idx, uint32_t* codebook, int c, uint32_t* counts, void* ws,
                                  hipStream_t s) {
-  uint32_t* members = static_cast<uint32_t*>(ws);
-  uint32_t* start = members + c;
-  uint32_t* cursor = start + c;
-  uint32_t* totals = cursor + c;
-  uint32_t* bucket = totals + 64;
   const int64_t total = N * ((K + v - 1) / v);
-  const unsigned nscan = (unsigned)((c + kScanThreads - 1) / kScanThreads);
-  fill_u32_kernel<<<stride_grid(3 * (int64_t)c), 256, 0, s>>>(members, 3 * (int64_t)c, 0u);
-  mstep_hist_kernel<<<stride_grid(total), 256, 0, s>>>(idx, total, c, members);
-  mstep_scan_local_kernel<<<nscan, kScanThreads, 0, s>>>(members, c, start, totals);
-  mstep_scan_add_kernel<<<nscan, kScanThreads, 0, s>>>(totals, c, start);
-  mstep_scatter_kernel<<<stride_grid(total), 256, 0, s>>>(plane, ldp, N, K, v, idx, c, start, cursor, bucket);
-  mstep_vote_kernel<<<(unsigned)((c + 3) / 4), 256, 0, s>>>(members, start, bucket, c, v, codebook, counts);
+  const int64_t nchunk = (total + kMsChunk - 1) / kMsChunk;
+  if (total <= 0) return hipSuccess;
+  if (total > 0xffffffffLL) return hipErrorInvalidValue;  // block positions are 32-bit words
+  uint32_t* E = static_cast<uint32_t*>(ws);
+  uint32_t* H = E + total;
+  uint32_t* btot = H + (int64_t)kMsBuckets * nchunk;
+  mstep_hist_kernel<<<(unsigned)nchunk, kMsThreads, 0, s>>>(idx, total, c, nchunk, H);
+  mstep_scan_kernel<<<kMsBuckets, kMsThreads, 0, s>>>(H, nchunk, btot);
+  mstep_scatter_kernel<<<(unsigned)nchunk, kMsThreads, 0, s>>>(idx, total, c, nchunk, H, btot, E);
+  mstep_vote_kernel<<<(unsigned)((c + kMsBuckets - 1) / kMsBuckets), kMsVoteThreads, 0, s>>>(plane, ldp, K, v, idx, E,
+                                                                                         btot, c, codebook, counts);
   return hipGetLastError();
 }
 

@@ -427,9 +427,11 @@ def test_qat_matmul_rejects(kw, status):
 
 
 def test_codebook_learn_workspace_bytes():
-    # the largest of: 3 c counters + 64 block totals + one word per block (standalone M-step),
-    # c (v + 1) counters (learning loop), the 2^v-bit bitmap (distinct count)
-    assert L.rb_codebook_learn_workspace_bytes(4096, 11008, 65536, 20) == 4 * (3 * 65536 + 64 + 4096 * 551)
+    # the largest of: one word per block + 256 chunk counts per 8192 blocks + 256 bucket totals
+    # (the M-step's radix pass), c (v + 1) counters (learning loop), the 2^v-bit bitmap (distinct
+    # count)
+    blocks = 4096 * 551
+    assert L.rb_codebook_learn_workspace_bytes(4096, 11008, 65536, 20) == 4 * (blocks + 256 * (-(-blocks // 8192)) + 256)
     assert L.rb_codebook_learn_workspace_bytes(1, 40, 65536, 20) == 4 * 65536 * 21
     assert L.rb_codebook_learn_workspace_bytes(16, 64, 16, 24) == 1 << 21
     assert L.rb_codebook_learn_workspace_bytes(16, 64, 0, 20) == 0

@@ -670,14 +670,18 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
     set_bits = int(np.bitwise_count(np.ascontiguousarray(words_np)).sum())
     # one per block (member) + one per +1 bit, the last block's padding columns counting as +1
     loop_atomics = Nc * nb + set_bits + Nc * (nb * 20 - Kc)
-    # standalone M-step: the plane read, idx read three times (histogram, scatter, vote), the
-    # block positions written to and read from their buckets, the codebook read and written
+    # standalone M-step: idx read twice (histogram, scatter), the plane once, the records (a
+    # pattern word and an index byte per block) written and read, the slice tables written and
+    # read, the codebook read and written
     nblk = Nc * nb
-    ms_bytes = pl[0].numel() * 4 + 3 * idx.numel() * 2 + 2 * nblk * 4 + 2 * 4 * C.numel()
+    n_slices = nblk // 4096 + min(-(-C.numel() // 256), nblk)
+    ms_bytes = (pl[0].numel() * 4 + 2 * idx.numel() * 2 + 2 * nblk * 5 + 2 * n_slices * 256 * 21 * 4
+                + 2 * 4 * C.numel())
     rows["next_f3_codebook_learn_4096x11008_v20_c65536"] = {
         "mstep": roof("hbm", ms_bytes / (ms_us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", ms_us, algorithmic_bytes=ms_bytes,
-                      note="radix pass of the blocks on idx >> 8 (LDS counters), then one block per bucket "
-                           "counts members and bits with LDS atomics; no global atomics"),
+                      note="radix pass of the blocks on idx >> 8 writing (pattern, index byte) records, "
+                           "sliced counting with LDS atomics, per-codeword sums of the slices; no global "
+                           "atomics"),
         "distinct_us": round(ds_us, 2),
         "learn_0_iterations_us": round(l0_us, 1),
         "learn_1_iteration_us": round(lr_us, 1),
@@ -686,7 +690,7 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
         "loop_counting_atomics": loop_atomics,
         "note": "learn with 0 iterations = distinct + the final E-step; each iteration adds an E-step and an "
                 "M-step; at this size the E-steps go through the nearest-codeword table and the M-step is the "
-                "radix pass + per-bucket vote (e_step_alone_us is the brute-force search, for comparison)",
+                "radix pass + sliced vote (e_step_alone_us is the brute-force search, for comparison)",
     }
     if with_oracle:
         pats = O.sign_blocks(words_np, Kc, 20)

@@ -337,16 +337,19 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = val;
 }
 
-// M-step as one radix pass of the blocks on the high byte of their codeword index, then a
-// count per codeword in LDS (no global atomics; each index is read twice):
+// M-step as one radix pass of the blocks on the high byte of their codeword index, then counts
+// per codeword in LDS (no global atomics; idx and the plane are read in order, never gathered):
 //   hist     chunk q of 8192 blocks: H[bucket][q] = its blocks with idx >> 8 == bucket
 //   scan     per bucket, H[bucket][.] becomes the exclusive prefix over the chunks, and
 //            btot[bucket] the bucket's total
-//   scatter  chunk q writes each block's position e into E at the bucket's start + H[bucket][q]
-//            + a rank from an LDS counter (the order inside a bucket is the scheduler's)
-//   vote     block b reads bucket b (codewords 256 b .. 256 b + 255), counts members and their
-//            bits with LDS atomics, and sets the bits with 2 ones >= members (ties go to +1);
-//            a codeword without members keeps its value.
+//   scatter  chunk q extracts each block's v-bit pattern and writes it to Rp, and the low byte of
+//            its index to Rb, at the bucket's start + H[bucket][q] + a rank from an LDS counter
+//            (the order inside a bucket is the scheduler's)
+//   vote     one block per slice of up to 4096 consecutive records of one bucket: members and
+//            ones per bit of each of the bucket's 256 codewords, counted with LDS atomics and
+//            written as the slice's table
+//   finish   per codeword, the sums over its bucket's slices; a bit is set when 2 ones >=
+//            members (ties go to +1); a codeword without members keeps its value.
 // Integer counts, so the result does not depend on any order: exact and deterministic.
 constexpr int kMsChunk = 8192;    // blocks per histogram / scatter chunk
 constexpr int kMsThreads = 256;   // one thread per bucket in the chunk kernels
@@ -412,91 +415,187 @@ __global__ __launch_bounds__(kMsThreads) void mstep_scan_kernel(uint32_t* __rest
   if (tid == 0) btot[blockIdx.x] = carry;
 }
 
-__global__ __launch_bounds__(kMsThreads) void mstep_scatter_kernel(const uint16_t* __restrict__ idx, int64_t total,
-                                                                   int c, int64_t nchunk,
+__global__ __launch_bounds__(kMsThreads) void mstep_scatter_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
+                                                                   int64_t K, int v, const uint16_t* __restrict__ idx,
+                                                                   int64_t total, int c, int64_t nchunk,
                                                                    const uint32_t* __restrict__ H,
                                                                    const uint32_t* __restrict__ btot,
-                                                                   uint32_t* __restrict__ E) {
+                                                                   uint32_t* __restrict__ Rp, uint8_t* __restrict__ Rb) {
   __shared__ uint32_t cur[kMsBuckets];
   const int tid = threadIdx.x;
   ms_bucket_starts(btot, cur, tid);
   cur[tid] += H[(int64_t)tid * nchunk + blockIdx.x];
   __syncthreads();
-  const int64_t e0 = (int64_t)blockIdx.x * kMsChunk;
-#pragma unroll 4
-  for (int k = 0; k < kMsChunk / kMsThreads; ++k) {
-    const int64_t e = e0 + k * kMsThreads + tid;
-    if (e < total) {
-      const uint32_t id = idx[e];
-      if (id < (uint32_t)c) E[atomicAdd(&cur[id >> 8], 1u)] = (uint32_t)e;
+  const uint32_t nb = (uint32_t)((K + v - 1) / v);  // blocks per row; total < 2^32
+  const int64_t Kw = (K + 31) >> 5;
+  const uint32_t vmask = v == 32 ? 0xffffffffu : ((1u << v) - 1u);
+  const uint32_t e0 = blockIdx.x * (uint32_t)kMsChunk;
+  constexpr int kU = 4;  // blocks per thread whose loads are in flight together
+  for (int k0 = 0; k0 < kMsChunk / kMsThreads; k0 += kU) {
+    uint32_t id[kU], lo[kU], hi[kU];
+    int64_t col[kU];
+    bool ok[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {  // loads at clamped addresses, unconditionally
+      const int64_t e64 = (int64_t)e0 + (k0 + u) * kMsThreads + tid;
+      ok[u] = e64 < total;
+      const uint32_t e = ok[u] ? (uint32_t)e64 : (uint32_t)(total - 1);
+      id[u] = idx[e];
+      const uint32_t n = e / nb;
+      col[u] = (int64_t)(e - n * nb) * v;
+      const int64_t w = col[u] >> 5;
+      const uint32_t* __restrict__ prow = plane + (int64_t)n * ldp;
+      lo[u] = prow[w < Kw ? w : Kw - 1];
+      hi[u] = prow[w + 1 < Kw ? w + 1 : Kw - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (!ok[u] || id[u] >= (uint32_t)c) continue;  // indices >= c are skipped
+      const int64_t w = col[u] >> 5;
+      // the block's v bits from columns col .. col + v - 1; columns past K count as +1
+      const uint64_t both = ((uint64_t)(w + 1 < Kw ? hi[u] : 0u) << 32) | (w < Kw ? lo[u] : 0u);
+      uint32_t pat = (uint32_t)(both >> (col[u] & 31)) & vmask;
+      const int64_t real = K - col[u];
+      if (real < v) pat |= vmask & ~((1u << real) - 1u);
+      const uint32_t pos = atomicAdd(&cur[id[u] >> 8], 1u);
+      Rp[pos] = pat;
+      Rb[pos] = (uint8_t)(id[u] & 0xffu);
     }
   }
 }
 
-constexpr int kMsVoteThreads = 1024;  // the vote's block: the bucket's members are dealt over its threads
+constexpr int kMsVoteThreads = 1024;  // the vote's block
 constexpr int kMsVoteUnroll = 4;      // members in flight per thread
+constexpr int kMsSlice = kMsVoteThreads * kMsVoteUnroll;  // members per vote block
 
-__global__ __launch_bounds__(kMsVoteThreads) void mstep_vote_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
-                                                                    int64_t K, int v, const uint16_t* __restrict__ idx,
-                                                                    const uint32_t* __restrict__ E,
-                                                                    const uint32_t* __restrict__ btot, int c,
-                                                                    uint32_t* __restrict__ codebook,
-                                                                    uint32_t* __restrict__ counts) {
-  __shared__ uint32_t cnt[kMsBuckets * 33];  // [codeword][v + 1]: bit counts, then members
-  __shared__ uint32_t start[kMsBuckets];
+// A bucket's members are cut into slices of kMsSlice, so a popular bucket does not hold up the
+// launch: slice counts per bucket = ceil(members / kMsSlice), their exclusive prefix gives each
+// bucket's first slice. Computed in LDS by the first 256 threads of any block size (every thread
+// passes the barriers): start[b] = first member, first[b] = first slice, nsl[b] = slices.
+__device__ __forceinline__ void ms_slices(const uint32_t* __restrict__ btot, uint32_t* start, uint32_t* first,
+                                          uint32_t* nsl, int tid) {
+  const bool own = tid < kMsBuckets;
+  const uint32_t m = own ? btot[tid] : 0u;
+  const uint32_t ns = (m + kMsSlice - 1) / kMsSlice;
+  if (own) {
+    start[tid] = m;
+    first[tid] = ns;
+    nsl[tid] = ns;
+  }
+  __syncthreads();
+  for (int off = 1; off < kMsBuckets; off <<= 1) {  // inclusive scans in place (Hillis-Steele)
+    const uint32_t a0 = (own && tid >= off) ? start[tid - off] : 0u;
+    const uint32_t a1 = (own && tid >= off) ? first[tid - off] : 0u;
+    __syncthreads();
+    if (own) {
+      start[tid] += a0;
+      first[tid] += a1;
+    }
+    __syncthreads();
+  }
+  if (own) {
+    start[tid] -= m;
+    first[tid] -= ns;
+  }
+  __syncthreads();
+}
+
+// one slice: its members' counts (members, ones per bit) per codeword of the bucket, written as
+// P[slice][t][256] (t = 0..v-1 the bits, t = v the members); blocks past the last slice exit
+__global__ __launch_bounds__(kMsVoteThreads) void mstep_vote_kernel(int v, const uint32_t* __restrict__ Rp,
+                                                                    const uint8_t* __restrict__ Rb,
+                                                                    const uint32_t* __restrict__ btot,
+                                                                    uint32_t* __restrict__ P) {
+  __shared__ uint32_t cnt[kMsBuckets * 33];  // [codeword][v + 1]
+  __shared__ uint32_t start[kMsBuckets], first[kMsBuckets], nsl[kMsBuckets];
   const int tid = threadIdx.x;
   const int stride = v + 1;
   for (int i = tid; i < kMsBuckets * stride; i += kMsVoteThreads) cnt[i] = 0u;
-  if (tid < kMsBuckets) {  // the bucket starts, by the first 256 threads (all threads pass the barriers)
-    start[tid] = btot[tid];
+  ms_slices(btot, start, first, nsl, tid);
+  const uint32_t slice = blockIdx.x;
+  if (slice >= first[kMsBuckets - 1] + nsl[kMsBuckets - 1]) return;  // whole block
+  // the bucket whose slices cover this one: the last with first <= slice. It is never empty: an
+  // empty bucket shares its first slice with the next bucket, and slice < the total slice count.
+  int bk = 0;
+  for (int step = kMsBuckets / 2; step > 0; step >>= 1)
+    if (first[bk + step] <= slice) bk += step;
+  const uint32_t j = slice - first[bk];
+  const uint32_t lo = start[bk] + j * (uint32_t)kMsSlice;
+  const uint32_t hi = min(lo + (uint32_t)kMsSlice, start[bk] + btot[bk]);
+  uint32_t pat[kMsVoteUnroll], r[kMsVoteUnroll];
+  bool live[kMsVoteUnroll];
+#pragma unroll
+  for (int u = 0; u < kMsVoteUnroll; ++u) {  // the slice's records, all loads issued first
+    const uint32_t q = lo + (uint32_t)(u * kMsVoteThreads + tid);
+    live[u] = q < hi;
+    pat[u] = live[u] ? Rp[q] : 0u;
+    r[u] = live[u] ? (uint32_t)Rb[q] : 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < kMsVoteUnroll; ++u) {
+    if (!live[u]) continue;
+    uint32_t* row = cnt + r[u] * (uint32_t)stride;
+    atomicAdd(row + v, 1u);
+    for (int t = 0; t < v; ++t)
+      if ((pat[u] >> t) & 1u) atomicAdd(row + t, 1u);
   }
   __syncthreads();
-  for (int off = 1; off < kMsBuckets; off <<= 1) {
-    const uint32_t add = (tid < kMsBuckets && tid >= off) ? start[tid - off] : 0u;
-    __syncthreads();
-    if (tid < kMsBuckets) start[tid] += add;
-    __syncthreads();
+  uint32_t* __restrict__ out = P + (size_t)slice * (size_t)(kMsBuckets * stride);
+  for (int i = tid; i < kMsBuckets * stride; i += kMsVoteThreads) {
+    const int t = i / kMsBuckets, cw = i % kMsBuckets;
+    out[i] = cnt[cw * stride + t];
   }
-  const int64_t nb = (K + v - 1) / v;
-  const uint32_t m = btot[blockIdx.x];
-  const uint32_t s0 = start[blockIdx.x] - m;  // inclusive prefix minus own total
-  // members kMsVoteUnroll at a time per thread: the position, index and pattern loads of all of
-  // them are issued before any count
-  for (uint32_t q0 = 0; q0 < m; q0 += kMsVoteThreads * kMsVoteUnroll) {
-    int64_t e[kMsVoteUnroll];
-    bool live[kMsVoteUnroll];
-#pragma unroll
-    for (int u = 0; u < kMsVoteUnroll; ++u) {
-      const uint32_t q = q0 + (uint32_t)(u * kMsVoteThreads + tid);
-      live[u] = q < m;
-      e[u] = live[u] ? (int64_t)E[s0 + q] : 0;
-    }
-    uint32_t r[kMsVoteUnroll], b[kMsVoteUnroll];
-#pragma unroll
-    for (int u = 0; u < kMsVoteUnroll; ++u) {
-      r[u] = (uint32_t)idx[e[u]] & 0xffu;
-      const int64_t n = e[u] / nb;
-      b[u] = extract_block(plane + n * ldp, K, (e[u] - n * nb) * v, v);
-    }
-#pragma unroll
-    for (int u = 0; u < kMsVoteUnroll; ++u) {
-      if (!live[u]) continue;
-      uint32_t* row = cnt + r[u] * (uint32_t)stride;
-      atomicAdd(row + v, 1u);
-      for (int t = 0; t < v; ++t)
-        if ((b[u] >> t) & 1u) atomicAdd(row + t, 1u);
-    }
-  }
-  __syncthreads();
-  if (tid >= kMsBuckets) return;
+}
+
+// block b, thread = codeword 256 b + tid: sums the bucket's slices and votes; a bit is set when
+// 2 ones >= members (ties go to +1); a codeword without members keeps its value. All v + 1 sums
+// stay in registers, so each slice costs one round of loads.
+// one wave per SIMD at most (256 blocks of 4 waves): registers for all v + 1 loads of a slice
+// in flight matter more than occupancy
+__global__ __launch_bounds__(kMsBuckets) __attribute__((amdgpu_waves_per_eu(1, 2))) void mstep_finish_kernel(const uint32_t* __restrict__ P,
+                                                                  const uint32_t* __restrict__ btot, int v, int c,
+                                                                  uint32_t* __restrict__ codebook,
+                                                                  uint32_t* __restrict__ counts) {
+  __shared__ uint32_t start[kMsBuckets], first[kMsBuckets], nsl[kMsBuckets];
+  const int tid = threadIdx.x;
+  ms_slices(btot, start, first, nsl, tid);
   const uint32_t id = blockIdx.x * (uint32_t)kMsBuckets + (uint32_t)tid;
   if (id >= (uint32_t)c) return;
-  const uint32_t n = cnt[tid * stride + v];
+  const size_t per = (size_t)kMsBuckets * (size_t)(v + 1);
+  const uint32_t* __restrict__ base = P + (size_t)first[blockIdx.x] * per + tid;
+  const uint32_t ns = nsl[blockIdx.x];
+  uint32_t acc[33];
+#pragma unroll
+  for (int t = 0; t < 33; ++t) acc[t] = 0u;
+  for (uint32_t j = 0; j < ns; ++j) {  // rows past v re-read row v (no branch, so no wait per load)
+    const uint32_t* __restrict__ src = base + (size_t)j * per;
+#pragma unroll
+    for (int t = 0; t < 33; ++t) acc[t] += src[(t < v ? t : v) * kMsBuckets];
+  }
+  uint32_t n = 0u;
+#pragma unroll
+  for (int t = 0; t < 33; ++t) n = t == v ? acc[t] : n;
   if (counts) counts[id] = n;
   if (n == 0u) return;
   uint32_t w = 0u;
-  for (int t = 0; t < v; ++t) w |= (2ull * cnt[tid * stride + t] >= n ? 1u : 0u) << t;
+#pragma unroll
+  for (int t = 0; t < 32; ++t)
+    if (t < v) w |= (2ull * acc[t] >= n ? 1u : 0u) << t;
   codebook[id] = w;
+}
+
+// slices the vote may need: floor(total / kMsSlice) full ones plus at most one partial slice per
+// non-empty bucket (buckets at or past ceil(c / 256) are empty)
+int64_t ms_max_slices(int64_t total, int c) {
+  const int64_t nbk = ((int64_t)c + kMsBuckets - 1) / kMsBuckets;
+  return total / kMsSlice + (nbk < total ? nbk : total);
+}
+
+// words before the slice tables: the records' patterns (one word each) and index bytes, chunk
+// histograms, bucket totals, rounded up to 64
+int64_t ms_head_words(int64_t total) {
+  const int64_t nchunk = (total + kMsChunk - 1) / kMsChunk;
+  return (total + (total + 3) / 4 + (int64_t)kMsBuckets * nchunk + kMsBuckets + 63) & ~(int64_t)63;
 }
 
 __global__ __launch_bounds__(256) void mstep_vote_counts_kernel(const uint32_t* __restrict__ cnt, int c, int v,
@@ -689,12 +788,14 @@ hipError_t launch_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, i
   return hipGetLastError();
 }
 
-// workspace, used by one step at a time: the standalone M-step's block list (one word per
-// block), chunk histograms (256 per 8192 blocks) and bucket totals (256); the learning loop's
+// workspace, used by one step at a time: the standalone M-step's records (a pattern word and an
+// index byte per block), chunk histograms (256 per 8192 blocks), bucket totals (256) and slice counts (256 (v + 1)
+// words per slice of 4096 members); the learning loop's
 // counters [c][v + 1]; the 2^v-bit bitmap of the distinct count
 size_t codebook_learn_workspace_bytes(int64_t N, int64_t K, int c, int v) {
   const size_t blocks = (size_t)N * (size_t)((K + v - 1) / v);
-  const size_t mstep = 4u * (blocks + (size_t)kMsBuckets * ((blocks + kMsChunk - 1) / kMsChunk) + kMsBuckets);
+  const size_t mstep = 4u * ((size_t)ms_head_words((int64_t)blocks) +
+                             (size_t)ms_max_slices((int64_t)blocks, c) * kMsBuckets * (size_t)(v + 1));
   const size_t counters = 4u * (size_t)c * (size_t)(v + 1);
   const size_t bitmap = v <= 24 ? ((size_t)1 << (v > 5 ? v - 3 : 2)) : 0u;
   const size_t table = codebook_use_table(N, K, c, v) ? codebook_table_bytes(v) : 0u;
@@ -710,14 +811,18 @@ hipError_t launch_codebook_mstep(const uint32_t* plane, int64_t ldp, int64_t N, 
   const int64_t nchunk = (total + kMsChunk - 1) / kMsChunk;
   if (total <= 0) return hipSuccess;
   if (total > 0xffffffffLL) return hipErrorInvalidValue;  // block positions are 32-bit words
-  uint32_t* E = static_cast<uint32_t*>(ws);
-  uint32_t* H = E + total;
+  uint32_t* Rp = static_cast<uint32_t*>(ws);
+  uint8_t* Rb = reinterpret_cast<uint8_t*>(Rp + total);
+  uint32_t* H = Rp + total + (total + 3) / 4;
   uint32_t* btot = H + (int64_t)kMsBuckets * nchunk;
+  uint32_t* P = Rp + ms_head_words(total);
   mstep_hist_kernel<<<(unsigned)nchunk, kMsThreads, 0, s>>>(idx, total, c, nchunk, H);
   mstep_scan_kernel<<<kMsBuckets, kMsThreads, 0, s>>>(H, nchunk, btot);
-  mstep_scatter_kernel<<<(unsigned)nchunk, kMsThreads, 0, s>>>(idx, total, c, nchunk, H, btot, E);
-  mstep_vote_kernel<<<(unsigned)((c + kMsBuckets - 1) / kMsBuckets), kMsVoteThreads, 0, s>>>(plane, ldp, K, v, idx, E,
-                                                                                         btot, c, codebook, counts);
+  mstep_scatter_kernel<<<(unsigned)nchunk, kMsThreads, 0, s>>>(plane, ldp, K, v, idx, total, c, nchunk, H, btot, Rp,
+                                                               Rb);
+  mstep_vote_kernel<<<(unsigned)ms_max_slices(total, c), kMsVoteThreads, 0, s>>>(v, Rp, Rb, btot, P);
+  mstep_finish_kernel<<<(unsigned)((c + kMsBuckets - 1) / kMsBuckets), kMsBuckets, 0, s>>>(P, btot, v, c, codebook,
+                                                                                           counts);
   return hipGetLastError();
 }
 

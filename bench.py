@@ -358,6 +358,68 @@ def measure_variants(torch, np, rb, wl, dev, with_oracle: bool) -> dict:
     return {"next_f4_gemv_variants_down_4096x11008_m1": out}
 
 
+def measure_codebook_learn(torch, np, rb, dev, pl, Kc: int, idx, C, enc_us, with_oracle: bool) -> dict:
+    """Binary codebook learning on the sign plane pl[0] (Kc columns, v = 20, c = C.numel(), idx the
+    indices of C): one standalone M-step (radix pass of the blocks, sliced counting, majority
+    vote), the distinct-block count, and whole learning calls with 0 and 1 iterations (distinct +
+    E-step + M-step + final E-step). enc_us is the brute-force E-step's time, None if unmeasured."""
+    Nc, nb = idx.shape
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ws_l = torch.empty(rb.lib.rb_codebook_learn_workspace_bytes(Nc, Kc, C.numel(), 20), dtype=torch.uint8, device=dev)
+    Cl = C.clone()
+
+    def ev_us(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+    ms_us = ev_us(lambda: rb.codebook_mstep(pl[0], Kc, idx, Cl, 20, counts=False, ws=ws_l), 10)
+    ds_us = ev_us(lambda: rb.codebook_distinct(pl[0], Kc, Cl, 20, ws=ws_l), 10)
+    l0_us = ev_us(lambda: rb.codebook_learn(pl[0], Kc, C.clone(), 20, 0, ws=ws_l), 2)
+    lr_us = ev_us(lambda: rb.codebook_learn(pl[0], Kc, C.clone(), 20, 1, ws=ws_l), 2)
+    words_np = pl[0].cpu().numpy().view(np.uint32)[:, :(Kc + 31) // 32]
+    idx_np = idx.cpu().numpy().view(np.uint16)
+    set_bits = int(np.bitwise_count(np.ascontiguousarray(words_np)).sum())
+    # one per block (member) + one per +1 bit, the last block's padding columns counting as +1
+    loop_atomics = Nc * nb + set_bits + Nc * (nb * 20 - Kc)
+    # standalone M-step: idx read twice (histogram, scatter), the plane once, the records (a
+    # pattern word and an index byte per block) written and read, the slice tables written and
+    # read, the codebook read and written
+    nblk = Nc * nb
+    n_slices = nblk // 4096 + min(-(-C.numel() // 256), nblk)
+    ms_bytes = (pl[0].numel() * 4 + 2 * idx.numel() * 2 + 2 * nblk * 5 + 2 * n_slices * 256 * 21 * 4
+                + 2 * 4 * C.numel())
+    row = {
+        "mstep": roof("hbm", ms_bytes / (ms_us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", ms_us, algorithmic_bytes=ms_bytes,
+                      note="radix pass of the blocks on idx >> 8 writing (pattern, index byte) records, "
+                           "sliced counting with LDS atomics, per-codeword sums of the slices; no global "
+                           "atomics"),
+        "distinct_us": round(ds_us, 2),
+        "learn_0_iterations_us": round(l0_us, 1),
+        "learn_1_iteration_us": round(lr_us, 1),
+        "iteration_us": round(lr_us - l0_us, 1),
+        "e_step_alone_us": None if enc_us is None else round(enc_us, 1),
+        "loop_counting_atomics": loop_atomics,
+        "note": "learn with 0 iterations = distinct + the final E-step; each iteration adds an E-step and an "
+                "M-step; at this size the E-steps go through the nearest-codeword table and the M-step is the "
+                "radix pass + sliced vote (e_step_alone_us is the brute-force search, for comparison)",
+    }
+    if with_oracle:
+        from oracle import rb_oracle as O
+        pats = O.sign_blocks(words_np, Kc, 20)
+        Cn = C.cpu().numpy().view(np.uint32)
+        row["mstep"]["cpu_oracle"] = oracle_rate(
+            lambda: O.codebook_mstep(pats, idx_np, Cn, 20), ms_bytes, 1e9, "GB/s",
+            "the whole M-step (all 2.26 M blocks), bytes as for the GPU")
+    del ws_l, Cl
+    torch.cuda.synchronize()
+    return row
+
+
 def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = True) -> dict:
     """Every step of the path besides the metric product, each on its own workload, timed
     on the GPU against the roofline that bounds it (inputs are seeded synthetic data). With
@@ -645,60 +707,8 @@ def measure_rows(torch, np, rb, wl, dev, pack_ms: float, with_oracle: bool = Tru
         rows["a8_codebook_gemv_4096x11008_m1"]["cpu_oracle"] = oracle_rate(
             lambda: O.codebook_gemv(idx_s, Ch, 20, s_s, 16, xch, Kc), RG * per_row + C.numel() * 4 + 2 * Kc,
             1e9, "GB/s", f"first {RG} of the 4096 rows, M=1, index and scale bytes scaled per row")
-    # next row: binary codebook learning on the same sign matrix (v = 20, c = 65536): one M-step
-    # (member counters by integer atomics, then the majority vote), the distinct-block count, and
-    # a whole learning call with one iteration (distinct + E-step + M-step + final E-step)
-    ws_l = torch.empty(rb.lib.rb_codebook_learn_workspace_bytes(Nc, Kc, C.numel(), 20), dtype=torch.uint8, device=dev)
-    Cl = C.clone()
-
-    def ev_us(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
-    ms_us = ev_us(lambda: rb.codebook_mstep(pl[0], Kc, idx, Cl, 20, counts=False, ws=ws_l), 10)
-    ds_us = ev_us(lambda: rb.codebook_distinct(pl[0], Kc, Cl, 20, ws=ws_l), 10)
-    l0_us = ev_us(lambda: rb.codebook_learn(pl[0], Kc, C.clone(), 20, 0, ws=ws_l), 2)
-    lr_us = ev_us(lambda: rb.codebook_learn(pl[0], Kc, C.clone(), 20, 1, ws=ws_l), 2)
-    enc_us = rows["a7_codebook_encode_4096x11008_v20_c65536"]["us"]
-    words_np = pl[0].cpu().numpy().view(np.uint32)[:, :(Kc + 31) // 32]
-    idx_np = idx.cpu().numpy().view(np.uint16)
-    set_bits = int(np.bitwise_count(np.ascontiguousarray(words_np)).sum())
-    # one per block (member) + one per +1 bit, the last block's padding columns counting as +1
-    loop_atomics = Nc * nb + set_bits + Nc * (nb * 20 - Kc)
-    # standalone M-step: idx read twice (histogram, scatter), the plane once, the records (a
-    # pattern word and an index byte per block) written and read, the slice tables written and
-    # read, the codebook read and written
-    nblk = Nc * nb
-    n_slices = nblk // 4096 + min(-(-C.numel() // 256), nblk)
-    ms_bytes = (pl[0].numel() * 4 + 2 * idx.numel() * 2 + 2 * nblk * 5 + 2 * n_slices * 256 * 21 * 4
-                + 2 * 4 * C.numel())
-    rows["next_f3_codebook_learn_4096x11008_v20_c65536"] = {
-        "mstep": roof("hbm", ms_bytes / (ms_us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", ms_us, algorithmic_bytes=ms_bytes,
-                      note="radix pass of the blocks on idx >> 8 writing (pattern, index byte) records, "
-                           "sliced counting with LDS atomics, per-codeword sums of the slices; no global "
-                           "atomics"),
-        "distinct_us": round(ds_us, 2),
-        "learn_0_iterations_us": round(l0_us, 1),
-        "learn_1_iteration_us": round(lr_us, 1),
-        "iteration_us": round(lr_us - l0_us, 1),
-        "e_step_alone_us": round(enc_us, 1),
-        "loop_counting_atomics": loop_atomics,
-        "note": "learn with 0 iterations = distinct + the final E-step; each iteration adds an E-step and an "
-                "M-step; at this size the E-steps go through the nearest-codeword table and the M-step is the "
-                "radix pass + sliced vote (e_step_alone_us is the brute-force search, for comparison)",
-    }
-    if with_oracle:
-        pats = O.sign_blocks(words_np, Kc, 20)
-        Cn = C.cpu().numpy().view(np.uint32)
-        rows["next_f3_codebook_learn_4096x11008_v20_c65536"]["mstep"]["cpu_oracle"] = oracle_rate(
-            lambda: O.codebook_mstep(pats, idx_np, Cn, 20), ms_bytes, 1e9, "GB/s",
-            "the whole M-step (all 2.26 M blocks), bytes as for the GPU")
-    del ws_l, Cl
+    rows["next_f3_codebook_learn_4096x11008_v20_c65536"] = measure_codebook_learn(
+        torch, np, rb, dev, pl, Kc, idx, C, rows["a7_codebook_encode_4096x11008_v20_c65536"]["us"], with_oracle)
     del icp, scp
     torch.cuda.synchronize()
     return rows
@@ -777,7 +787,7 @@ def main() -> int:
     ap.add_argument("--summarize-trace", metavar="DIR", help="per-dispatch durations of the product kernel "
                                                               "from rocprofv3 kernel-trace CSVs")
     ap.add_argument("--kernel", default=PRODUCT_KERNEL, help="kernel name for --summarize-trace")
-    ap.add_argument("--only-row", choices=["qat"], help="run one row's measurement alone (for profiling) "
+    ap.add_argument("--only-row", choices=["qat", "codebook_learn"], help="run one row's measurement alone (for profiling) "
                                                         "and print it as the JSON line")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -801,6 +811,15 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.only_row == "qat":
         print(json.dumps(measure_qat_step(torch, np, rb, wl, dev, with_oracle=False)))
+        return 0
+    if args.only_row == "codebook_learn":
+        Wc = torch.from_numpy(wl.weights_for("codebook")).to(dev)
+        Kc = Wc.shape[1]
+        pl, _ = rb.pack(Wc, 1, group=16)
+        del Wc
+        C = torch.from_numpy(wl.codebook().view(np.int32)).to(dev)
+        idx = rb.codebook_encode(pl[0], Kc, C, 20, table=True)
+        print(json.dumps(measure_codebook_learn(torch, np, rb, dev, pl, Kc, idx, C, None, with_oracle=False)))
         return 0
     N, K, k = N_ROWS, K_COLS, K_PLANES
     Kw = (K + 31) // 32

@@ -246,14 +246,16 @@ rb_status rb_codebook_encode_table(const uint32_t* sign_plane, int64_t ldp, int6
  * results are exact and deterministic.
  *
  * rb_codebook_learn_workspace_bytes -- workspace of the three calls below for an N x K plane
- *   and c codewords of v bits: the M-step's uint32 pattern and byte of index per block (the
- *   blocks sorted by the high byte of their codeword index), 256 counts per 8192 blocks and 256 bucket totals (together
- *   rounded up to 64 words), then 256 (v + 1) counts per slice of at most 4096 blocks, for
- *   floor(blocks / 4096) + min(ceil(c / 256), blocks) slices; the per-codeword counters of the learning loop (c (v + 1) uint32), the 2^v-bit pattern bitmap of
- *   rb_codebook_distinct, or, when rb_codebook_learn encodes through the nearest-codeword table
- *   (v <= 24 and N ceil(K/v) c > 64 x 2^v, where the table is the cheaper search), that table,
- *   whichever is largest (0 for invalid sizes). N ceil(K/v) must be below 2^32 (else
- *   RB_ERR_UNSUPPORTED).
+ *   and c codewords of v bits (blocks = N ceil(K/v)); the largest of:
+ *   - the M-step's records, a uint32 pattern and a byte of index per block (the blocks sorted
+ *     by the high byte of their codeword index), 256 counts per 8192 blocks and 256 bucket
+ *     totals (together rounded up to 64 words), then 256 (v + 1) counts per slice of at most
+ *     4096 blocks, for floor(blocks / 4096) + min(ceil(c / 256), blocks) slices;
+ *   - the per-codeword counters of the learning loop (c (v + 1) uint32);
+ *   - rb_codebook_distinct's 2^v-byte pattern map (rounded up to 16 bytes) and 2^v-bit bitmap;
+ *   - when rb_codebook_learn encodes through the nearest-codeword table (v <= 24 and
+ *     N ceil(K/v) c > 64 x 2^v, where the table is the cheaper search), that table.
+ *   0 for invalid sizes. N ceil(K/v) must be below 2^32 (else RB_ERR_UNSUPPORTED).
  */
 size_t rb_codebook_learn_workspace_bytes(int64_t N, int64_t K, int32_t c, int32_t v);
 

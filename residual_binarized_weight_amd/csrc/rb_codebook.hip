@@ -610,17 +610,65 @@ __global__ __launch_bounds__(256) void mstep_vote_counts_kernel(const uint32_t* 
   codebook[id] = w;
 }
 
-// bitmap of the 2^v possible patterns: bit p set when pattern p occurs
+// distinct count: a flag byte per possible pattern, then the bitmap of the 2^v patterns (bit p
+// set when pattern p occurs), then its count and list
+constexpr int kMarkPerThread = 4;  // blocks per thread, their loads in flight together
+
+// map[p] = 1 for every pattern p that occurs: plain byte stores, no atomics (every writer of a
+// byte stores the same value, and the per-XCD caches merge their dirty bytes when written back)
 __global__ __launch_bounds__(256) void distinct_mark_kernel(const uint32_t* __restrict__ plane, int64_t ldp,
-                                                            int64_t N, int64_t K, int v,
-                                                            uint32_t* __restrict__ bitmap) {
-  const int64_t nb = (K + v - 1) / v;
-  const int64_t total = N * nb;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t n = e / nb;
-    const uint32_t b = extract_block(plane + n * ldp, K, (e - n * nb) * v, v);
-    atomicOr(bitmap + (b >> 5), 1u << (b & 31u));
+                                                            int64_t K, int v, int64_t total,
+                                                            uint8_t* __restrict__ map) {
+  const uint32_t nb = (uint32_t)((K + v - 1) / v);  // blocks per row; total < 2^32
+  const int64_t Kw = (K + 31) >> 5;
+  const uint32_t vmask = v == 32 ? 0xffffffffu : ((1u << v) - 1u);
+  uint32_t lo[kMarkPerThread], hi[kMarkPerThread];
+  int64_t col[kMarkPerThread];
+  bool ok[kMarkPerThread];
+#pragma unroll
+  for (int u = 0; u < kMarkPerThread; ++u) {  // loads at clamped addresses, unconditionally
+    const int64_t e64 = ((int64_t)blockIdx.x * kMarkPerThread + u) * 256 + threadIdx.x;
+    ok[u] = e64 < total;
+    const uint32_t e = ok[u] ? (uint32_t)e64 : (uint32_t)(total - 1);
+    const uint32_t n = e / nb;
+    col[u] = (int64_t)(e - n * nb) * v;
+    const int64_t w = col[u] >> 5;
+    const uint32_t* __restrict__ prow = plane + (int64_t)n * ldp;
+    lo[u] = prow[w < Kw ? w : Kw - 1];
+    hi[u] = prow[w + 1 < Kw ? w + 1 : Kw - 1];
   }
+#pragma unroll
+  for (int u = 0; u < kMarkPerThread; ++u) {
+    if (!ok[u]) continue;
+    const int64_t w = col[u] >> 5;
+    // the block's v bits from columns col .. col + v - 1; columns past K count as +1
+    const uint64_t both = ((uint64_t)(w + 1 < Kw ? hi[u] : 0u) << 32) | (w < Kw ? lo[u] : 0u);
+    uint32_t b = (uint32_t)(both >> (col[u] & 31)) & vmask;
+    const int64_t real = K - col[u];
+    if (real < v) b |= vmask & ~((1u << real) - 1u);
+    map[b] = 1u;
+  }
+}
+
+// bitmap word w = the flags map[32 w .. 32 w + 31] as bits (npat = 2^v flags)
+__global__ __launch_bounds__(256) void distinct_pack_kernel(const uint8_t* __restrict__ map, int64_t npat,
+                                                            int64_t nwords, uint32_t* __restrict__ bitmap) {
+  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= nwords) return;
+  uint32_t word = 0u;
+  if (npat >= 32) {  // 32 whole flags, eight 4-byte loads (the workspace is 4-byte aligned)
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(map + w * 32);
+    uint32_t part[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[i] = src[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) word |= (((part[i] >> (8 * j)) & 0xffu) != 0u ? 1u : 0u) << (4 * i + j);
+  } else {
+    for (int64_t i = 0; i < npat; ++i) word |= (map[i] != 0u ? 1u : 0u) << i;
+  }
+  bitmap[w] = word;
 }
 
 constexpr int kDistinctThreads = 1024;
@@ -791,13 +839,14 @@ hipError_t launch_codebook_gemv(const uint16_t* idx, const uint32_t* codebook, i
 // workspace, used by one step at a time: the standalone M-step's records (a pattern word and an
 // index byte per block), chunk histograms (256 per 8192 blocks), bucket totals (256) and slice counts (256 (v + 1)
 // words per slice of 4096 members); the learning loop's
-// counters [c][v + 1]; the 2^v-bit bitmap of the distinct count
+// counters [c][v + 1]; the 2^v-byte map (rounded up to 16 bytes) and 2^v-bit bitmap of the
+// distinct count
 size_t codebook_learn_workspace_bytes(int64_t N, int64_t K, int c, int v) {
   const size_t blocks = (size_t)N * (size_t)((K + v - 1) / v);
   const size_t mstep = 4u * ((size_t)ms_head_words((int64_t)blocks) +
                              (size_t)ms_max_slices((int64_t)blocks, c) * kMsBuckets * (size_t)(v + 1));
   const size_t counters = 4u * (size_t)c * (size_t)(v + 1);
-  const size_t bitmap = v <= 24 ? ((size_t)1 << (v > 5 ? v - 3 : 2)) : 0u;
+  const size_t bitmap = v <= 24 ? ((((size_t)1 << v) + 15u) & ~(size_t)15) + ((size_t)1 << (v > 5 ? v - 3 : 2)) : 0u;
   const size_t table = codebook_use_table(N, K, c, v) ? codebook_table_bytes(v) : 0u;
   size_t m = mstep > counters ? mstep : counters;
   m = m > table ? m : table;
@@ -828,11 +877,19 @@ hipError_t launch_codebook_mstep(const uint32_t* plane, int64_t ldp, int64_t N, 
 
 hipError_t launch_codebook_distinct(const uint32_t* plane, int64_t ldp, int64_t N, int64_t K, int v,
                                     uint32_t* codebook, int c, int32_t* n_distinct, void* ws, hipStream_t s) {
-  uint32_t* bitmap = static_cast<uint32_t*>(ws);
+  // workspace: the 2^v-byte map (rounded up to 16 bytes), then the 2^v-bit bitmap
+  const int64_t npat = (int64_t)1 << v;
   const int64_t nwords = v > 5 ? (int64_t)1 << (v - 5) : 1;
-  fill_u32_kernel<<<stride_grid(nwords), 256, 0, s>>>(bitmap, nwords, 0u);
+  uint8_t* map = static_cast<uint8_t*>(ws);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(map + ((npat + 15) & ~(int64_t)15));
   const int64_t total = N * ((K + v - 1) / v);
-  distinct_mark_kernel<<<stride_grid(total), 256, 0, s>>>(plane, ldp, N, K, v, bitmap);
+  if (total > 0xffffffffLL) return hipErrorInvalidValue;  // block positions are 32-bit
+  fill_u32_kernel<<<stride_grid((npat + 3) / 4), 256, 0, s>>>(reinterpret_cast<uint32_t*>(map), (npat + 3) / 4, 0u);
+  if (total > 0) {
+    const int64_t grid = (total + 256 * kMarkPerThread - 1) / (256 * kMarkPerThread);
+    distinct_mark_kernel<<<(unsigned)grid, 256, 0, s>>>(plane, ldp, K, v, total, map);
+  }
+  distinct_pack_kernel<<<(unsigned)((nwords + 255) / 256), 256, 0, s>>>(map, npat, nwords, bitmap);
   distinct_compact_kernel<<<1, kDistinctThreads, 0, s>>>(bitmap, nwords, c, codebook, n_distinct);
   return hipGetLastError();
 }

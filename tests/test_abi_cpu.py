@@ -429,13 +429,13 @@ def test_qat_matmul_rejects(kw, status):
 def test_codebook_learn_workspace_bytes():
     # the largest of: a word and a byte per block + 256 chunk counts per 8192 blocks + 256 bucket
     # totals, rounded up to 64 words, + 256 (v + 1) counts per vote slice (the M-step's radix pass
-    # and vote), c (v + 1) counters (learning loop), the 2^v-bit bitmap (distinct count)
+    # and vote), c (v + 1) counters (learning loop), the 2^v-byte map + 2^v-bit bitmap (distinct count)
     blocks = 4096 * 551
     head = -(-(blocks + blocks // 4 + 256 * (-(-blocks // 8192)) + 256) // 64) * 64
     slices = blocks // 4096 + 256
     assert L.rb_codebook_learn_workspace_bytes(4096, 11008, 65536, 20) == 4 * (head + slices * 256 * 21)
     assert L.rb_codebook_learn_workspace_bytes(1, 40, 65536, 20) == 4 * 65536 * 21
-    assert L.rb_codebook_learn_workspace_bytes(16, 64, 16, 24) == 1 << 21
+    assert L.rb_codebook_learn_workspace_bytes(16, 64, 16, 24) == (1 << 24) + (1 << 21)
     assert L.rb_codebook_learn_workspace_bytes(16, 64, 0, 20) == 0
     assert L.rb_codebook_learn_workspace_bytes(16, 64, 16, 33) == 0
     assert L.rb_codebook_learn_workspace_bytes(0, 64, 16, 20) == 0

@@ -378,13 +378,17 @@ __global__ __launch_bounds__(kMsThreads) void mstep_hist_kernel(const uint16_t* 
   h[tid] = 0u;
   __syncthreads();
   const int64_t e0 = (int64_t)blockIdx.x * kMsChunk;
-#pragma unroll 4
-  for (int k = 0; k < kMsChunk / kMsThreads; ++k) {
-    const int64_t e = e0 + k * kMsThreads + tid;
-    if (e < total) {
-      const uint32_t id = idx[e];
-      if (id < (uint32_t)c) atomicAdd(&h[id >> 8], 1u);  // indices >= c are skipped
+  constexpr int kU = 8;  // indices per thread loaded together, at clamped addresses
+  for (int k0 = 0; k0 < kMsChunk / kMsThreads; k0 += kU) {
+    uint32_t id[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t e = e0 + (k0 + u) * kMsThreads + tid;
+      id[u] = e < total ? (uint32_t)idx[e] : 0xffffffffu;  // past the end: skipped below
     }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (id[u] < (uint32_t)c) atomicAdd(&h[id[u] >> 8], 1u);  // indices >= c are skipped
   }
   __syncthreads();
   H[(int64_t)tid * nchunk + blockIdx.x] = h[tid];
@@ -676,22 +680,55 @@ constexpr int kDistinctThreads = 1024;
 // One block: M = number of set bits -> *n_distinct. If M < c, the patterns in ascending order
 // go to codebook[0..M) and codebook[M..c) repeats the largest one. Thread t owns a contiguous
 // range of bitmap words; its first output position is the exclusive scan of the ranges' counts.
-__global__ __launch_bounds__(kDistinctThreads) void distinct_compact_kernel(const uint32_t* __restrict__ bitmap,
+// one block on the whole chip: registers for a batch of loads matter more than occupancy
+__global__ __launch_bounds__(kDistinctThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void distinct_compact_kernel(const uint32_t* __restrict__ bitmap,
                                                                             int64_t nwords, int c,
                                                                             uint32_t* __restrict__ codebook,
                                                                             int32_t* __restrict__ n_distinct) {
   __shared__ uint32_t scan[2][kDistinctThreads];
   __shared__ int32_t top;
+  __shared__ uint32_t count;
   const int t = threadIdx.x;
+  constexpr int kB = 8;  // words per batch, loaded together at clamped addresses
+  // the count alone first, with coalesced reads (thread t takes words t, t + 1024, ...): when it
+  // reaches c, nothing is listed
+  {
+    uint32_t n = 0u;
+    for (int64_t w0 = t; w0 < nwords; w0 += (int64_t)kDistinctThreads * kB) {
+      uint32_t b[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int64_t w = w0 + (int64_t)u * kDistinctThreads;
+        b[u] = bitmap[w < nwords ? w : nwords - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) n += w0 + (int64_t)u * kDistinctThreads < nwords ? (uint32_t)__popc(b[u]) : 0u;
+    }
+    if (t == 0) count = 0u;
+    __syncthreads();
+    atomicAdd(&count, n);
+    __syncthreads();
+    if (count >= (uint32_t)c) {  // the whole block leaves here
+      if (t == 0) *n_distinct = (int32_t)count;
+      return;
+    }
+  }
+  // fewer than c: thread t owns a contiguous range of words, listed in ascending order
   const int64_t per = (nwords + kDistinctThreads - 1) / kDistinctThreads;
   const int64_t lo = (int64_t)t * per < nwords ? (int64_t)t * per : nwords;
   const int64_t hi = lo + per < nwords ? lo + per : nwords;
   uint32_t mine = 0u;
   int32_t last = -1;
-  for (int64_t w = lo; w < hi; ++w) {
-    const uint32_t b = bitmap[w];
-    mine += (uint32_t)__popc(b);
-    if (b) last = (int32_t)(w * 32 + 31 - __builtin_clz(b));
+  for (int64_t w0 = lo; w0 < hi; w0 += kB) {
+    uint32_t b[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) b[u] = bitmap[w0 + u < hi ? w0 + u : hi - 1];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {  // selects, no branches: the loads stay ahead of their uses
+      const uint32_t bu = w0 + u < hi ? b[u] : 0u;
+      mine += (uint32_t)__popc(bu);
+      last = bu ? (int32_t)((w0 + u) * 32 + 31 - __builtin_clz(bu)) : last;
+    }
   }
   if (t == 0) top = -1;
   scan[0][t] = mine;

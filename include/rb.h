@@ -228,7 +228,8 @@ rb_status rb_codebook_encode(const uint32_t* sign_plane, int64_t ldp, int64_t N,
  *   distance-d neighbours, which is the lowest index among the nearest codewords). The result is
  *   identical to rb_codebook_encode's, bit for bit; the work is about 2^v x (a few layers) table
  *   visits plus one lookup per block instead of N ceil(K/v) c distance evaluations.
- *   v 1..24 (else RB_ERR_UNSUPPORTED); codewords must hold only their low v bits (the table is
+ *   v 1..24 and N ceil(K/v) below 2^32 (else RB_ERR_UNSUPPORTED); codewords must hold only
+ *   their low v bits (the table is
  *   indexed by them); ws rb_codebook_table_bytes(v) bytes (4 << v, plus 128), 4-byte aligned,
  *   scratch (no zero-filling needed). Other arguments as rb_codebook_encode.
  */

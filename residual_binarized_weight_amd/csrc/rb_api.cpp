@@ -222,6 +222,7 @@ rb_status rb_codebook_encode_table(const uint32_t* sign_plane, int64_t ldp, int6
   if (ldp < (K + 31) / 32) return RB_ERR_INVALID_ARG;
   if (c < 1 || c > 65536 || v < 1 || v > 32) return RB_ERR_INVALID_ARG;
   if (v > 24) return RB_ERR_UNSUPPORTED;
+  if (N * ((K + v - 1) / v) > 0xffffffffll) return RB_ERR_UNSUPPORTED;  // 32-bit block positions
   if (!ws || ws_bytes < rb::codebook_table_bytes(v)) return RB_ERR_WORKSPACE;
   if (!aligned(sign_plane, 16) || !aligned(codebook, 4) || !aligned(idx, 2) || !aligned(ws, 4))
     return RB_ERR_MISALIGNED;

@@ -26,6 +26,27 @@ __device__ __forceinline__ uint32_t extract_block(const uint32_t* __restrict__ p
   return b;
 }
 
+// extract_block from the two words already loaded: lo = word col / 32 of the row, hi = the next
+// (their loads may be clamped; words at or past Kw count as zero here)
+__device__ __forceinline__ uint32_t block_from_words(uint32_t lo, uint32_t hi, int64_t col, int64_t K, int64_t Kw,
+                                                     int v) {
+  const int64_t w = col >> 5;
+  const uint64_t both = ((uint64_t)(w + 1 < Kw ? hi : 0u) << 32) | (w < Kw ? lo : 0u);
+  const uint32_t vmask = v == 32 ? 0xffffffffu : ((1u << v) - 1u);
+  uint32_t b = (uint32_t)(both >> (col & 31)) & vmask;
+  const int64_t real = K - col;  // columns of this block that exist
+  if (real < v) b |= vmask & ~((1u << real) - 1u);
+  return b;
+}
+
+// the two words block_from_words needs, loaded unconditionally at clamped addresses
+__device__ __forceinline__ void load_block_words(const uint32_t* __restrict__ prow, int64_t col, int64_t Kw,
+                                                 uint32_t& lo, uint32_t& hi) {
+  const int64_t w = col >> 5;
+  lo = prow[w < Kw ? w : Kw - 1];
+  hi = prow[w + 1 < Kw ? w + 1 : Kw - 1];
+}
+
 constexpr int kEncodeTile = 8192;  // codewords staged in LDS per round (32 KB)
 constexpr int kPatternsPerThread = 4;
 
@@ -432,7 +453,6 @@ __global__ __launch_bounds__(kMsThreads) void mstep_scatter_kernel(const uint32_
   __syncthreads();
   const uint32_t nb = (uint32_t)((K + v - 1) / v);  // blocks per row; total < 2^32
   const int64_t Kw = (K + 31) >> 5;
-  const uint32_t vmask = v == 32 ? 0xffffffffu : ((1u << v) - 1u);
   const uint32_t e0 = blockIdx.x * (uint32_t)kMsChunk;
   constexpr int kU = 4;  // blocks per thread whose loads are in flight together
   for (int k0 = 0; k0 < kMsChunk / kMsThreads; k0 += kU) {
@@ -447,20 +467,12 @@ __global__ __launch_bounds__(kMsThreads) void mstep_scatter_kernel(const uint32_
       id[u] = idx[e];
       const uint32_t n = e / nb;
       col[u] = (int64_t)(e - n * nb) * v;
-      const int64_t w = col[u] >> 5;
-      const uint32_t* __restrict__ prow = plane + (int64_t)n * ldp;
-      lo[u] = prow[w < Kw ? w : Kw - 1];
-      hi[u] = prow[w + 1 < Kw ? w + 1 : Kw - 1];
+      load_block_words(plane + (int64_t)n * ldp, col[u], Kw, lo[u], hi[u]);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (!ok[u] || id[u] >= (uint32_t)c) continue;  // indices >= c are skipped
-      const int64_t w = col[u] >> 5;
-      // the block's v bits from columns col .. col + v - 1; columns past K count as +1
-      const uint64_t both = ((uint64_t)(w + 1 < Kw ? hi[u] : 0u) << 32) | (w < Kw ? lo[u] : 0u);
-      uint32_t pat = (uint32_t)(both >> (col[u] & 31)) & vmask;
-      const int64_t real = K - col[u];
-      if (real < v) pat |= vmask & ~((1u << real) - 1u);
+      const uint32_t pat = block_from_words(lo[u], hi[u], col[u], K, Kw, v);
       const uint32_t pos = atomicAdd(&cur[id[u] >> 8], 1u);
       Rp[pos] = pat;
       Rb[pos] = (uint8_t)(id[u] & 0xffu);
@@ -625,7 +637,6 @@ __global__ __launch_bounds__(256) void distinct_mark_kernel(const uint32_t* __re
                                                             uint8_t* __restrict__ map) {
   const uint32_t nb = (uint32_t)((K + v - 1) / v);  // blocks per row; total < 2^32
   const int64_t Kw = (K + 31) >> 5;
-  const uint32_t vmask = v == 32 ? 0xffffffffu : ((1u << v) - 1u);
   uint32_t lo[kMarkPerThread], hi[kMarkPerThread];
   int64_t col[kMarkPerThread];
   bool ok[kMarkPerThread];
@@ -636,22 +647,11 @@ __global__ __launch_bounds__(256) void distinct_mark_kernel(const uint32_t* __re
     const uint32_t e = ok[u] ? (uint32_t)e64 : (uint32_t)(total - 1);
     const uint32_t n = e / nb;
     col[u] = (int64_t)(e - n * nb) * v;
-    const int64_t w = col[u] >> 5;
-    const uint32_t* __restrict__ prow = plane + (int64_t)n * ldp;
-    lo[u] = prow[w < Kw ? w : Kw - 1];
-    hi[u] = prow[w + 1 < Kw ? w + 1 : Kw - 1];
+    load_block_words(plane + (int64_t)n * ldp, col[u], Kw, lo[u], hi[u]);
   }
 #pragma unroll
-  for (int u = 0; u < kMarkPerThread; ++u) {
-    if (!ok[u]) continue;
-    const int64_t w = col[u] >> 5;
-    // the block's v bits from columns col .. col + v - 1; columns past K count as +1
-    const uint64_t both = ((uint64_t)(w + 1 < Kw ? hi[u] : 0u) << 32) | (w < Kw ? lo[u] : 0u);
-    uint32_t b = (uint32_t)(both >> (col[u] & 31)) & vmask;
-    const int64_t real = K - col[u];
-    if (real < v) b |= vmask & ~((1u << real) - 1u);
-    map[b] = 1u;
-  }
+  for (int u = 0; u < kMarkPerThread; ++u)
+    if (ok[u]) map[block_from_words(lo[u], hi[u], col[u], K, Kw, v)] = 1u;
 }
 
 // bitmap word w = the flags map[32 w .. 32 w + 31] as bits (npat = 2^v flags)
@@ -789,11 +789,14 @@ __global__ __launch_bounds__(256) void table_layer_kernel(uint32_t* __restrict__
   __syncthreads();
   const uint32_t p = blockIdx.x * 256u + threadIdx.x;  // the grid covers the 2^v patterns (more when v < 8)
   if (p < (1u << v) && table[p] == kTableUnreached) {
+    uint32_t e[kTableMaxV];
+#pragma unroll
+    for (int t = 0; t < kTableMaxV; ++t)  // all neighbours' loads in flight; bits past v re-read bit v - 1
+      e[t] = table[p ^ (1u << (t < v ? t : v - 1))];
     uint32_t best = kTableUnreached;
-    for (int t = 0; t < v; ++t) {
-      const uint32_t e = table[p ^ (1u << t)];
-      if ((e >> 24) == (uint32_t)d) best = (e & 0xffffffu) < best ? (e & 0xffffffu) : best;
-    }
+#pragma unroll
+    for (int t = 0; t < kTableMaxV; ++t)
+      if ((e[t] >> 24) == (uint32_t)d) best = (e[t] & 0xffffffu) < best ? (e[t] & 0xffffffu) : best;
     if (best != kTableUnreached) {
       table[p] = ((uint32_t)(d + 1) << 24) | best;
       any = 1;
@@ -803,17 +806,30 @@ __global__ __launch_bounds__(256) void table_layer_kernel(uint32_t* __restrict__
   if (threadIdx.x == 0 && any) flag[d + 1] = 1u;
 }
 
-// encode by lookup: the same blocks as encode_kernel, the same answer
-__global__ __launch_bounds__(256) void encode_table_kernel(const uint32_t* __restrict__ plane, int64_t ldp, int64_t N,
-                                                           int64_t K, int v, const uint32_t* __restrict__ table,
+// encode by lookup: the same blocks as encode_kernel, the same answer; kEncPerThread blocks per
+// thread, each stage's loads in flight together
+constexpr int kEncPerThread = 4;
+
+__global__ __launch_bounds__(256) void encode_table_kernel(const uint32_t* __restrict__ plane, int64_t ldp, int64_t K,
+                                                           int v, int64_t total, const uint32_t* __restrict__ table,
                                                            uint16_t* __restrict__ idx) {
-  const int64_t nb = (K + v - 1) / v;
-  const int64_t total = N * nb;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t n = e / nb;
-    const int64_t j = e - n * nb;
-    idx[e] = (uint16_t)(table[extract_block(plane + n * ldp, K, j * v, v)] & 0xffffu);
+  const uint32_t nb = (uint32_t)((K + v - 1) / v);  // blocks per row; total < 2^32
+  const int64_t Kw = (K + 31) >> 5;
+  uint32_t lo[kEncPerThread], hi[kEncPerThread], ent[kEncPerThread];
+  int64_t col[kEncPerThread], e[kEncPerThread];
+#pragma unroll
+  for (int u = 0; u < kEncPerThread; ++u) {
+    e[u] = ((int64_t)blockIdx.x * kEncPerThread + u) * 256 + threadIdx.x;
+    const uint32_t ec = e[u] < total ? (uint32_t)e[u] : (uint32_t)(total - 1);
+    const uint32_t n = ec / nb;
+    col[u] = (int64_t)(ec - n * nb) * v;
+    load_block_words(plane + (int64_t)n * ldp, col[u], Kw, lo[u], hi[u]);
   }
+#pragma unroll
+  for (int u = 0; u < kEncPerThread; ++u) ent[u] = table[block_from_words(lo[u], hi[u], col[u], K, Kw, v)];
+#pragma unroll
+  for (int u = 0; u < kEncPerThread; ++u)
+    if (e[u] < total) idx[e[u]] = (uint16_t)(ent[u] & 0xffffu);
 }
 
 unsigned stride_grid(int64_t items) {
@@ -952,8 +968,11 @@ hipError_t launch_codebook_encode_table(const uint32_t* plane, int64_t ldp, int6
                                         hipStream_t s) {
   const hipError_t e = launch_codebook_table(codebook, c, v, ws, s);
   if (e != hipSuccess) return e;
-  encode_table_kernel<<<stride_grid(N * ((K + v - 1) / v)), 256, 0, s>>>(plane, ldp, N, K, v,
-                                                                        static_cast<const uint32_t*>(ws), idx);
+  const int64_t total = N * ((K + v - 1) / v);
+  if (total > 0xffffffffLL) return hipErrorInvalidValue;  // block positions are 32-bit
+  if (total > 0)
+    encode_table_kernel<<<(unsigned)((total + 256 * kEncPerThread - 1) / (256 * kEncPerThread)), 256, 0, s>>>(
+        plane, ldp, K, v, total, static_cast<const uint32_t*>(ws), idx);
   return hipGetLastError();
 }
 

@@ -544,9 +544,11 @@ def test_codebook_table_sizes_and_validation():
     assert L.rb_codebook_table_bytes(25) == 0 and L.rb_codebook_table_bytes(0) == 0
     need = L.rb_codebook_table_bytes(12)
 
-    def call(v=12, ws=P, wsb=None, plane=P, cb=P, idx=P, c=40):
-        return L.rb_codebook_encode_table(plane, 4, 3, 100, cb, c, v, idx, ws, need if wsb is None else wsb, None)
+    def call(v=12, ws=P, wsb=None, plane=P, cb=P, idx=P, c=40, N=3, K=100, ldp=4):
+        return L.rb_codebook_encode_table(plane, ldp, N, K, cb, c, v, idx, ws, need if wsb is None else wsb, None)
     assert call(plane=None) == _lib.RB_ERR_INVALID_ARG
+    # 2^20 rows x 2^17 blocks of 12 columns: 2^37 block positions, past 32 bits
+    assert call(N=1 << 20, K=12 << 17, ldp=(12 << 17) // 32) == _lib.RB_ERR_UNSUPPORTED
     assert call(c=0) == _lib.RB_ERR_INVALID_ARG
     assert call(v=33) == _lib.RB_ERR_INVALID_ARG
     assert call(v=25) == _lib.RB_ERR_UNSUPPORTED

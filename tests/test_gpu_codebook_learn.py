@@ -48,6 +48,29 @@ def test_mstep_matches_oracle(N, K, v, c, assign):
     assert np.array_equal(u32(cnt), cnt_ref.astype(np.uint32))
 
 
+def test_mstep_skewed_assignments():
+    """Skewed memberships against the 4096-block slices the M-step counts in: one codeword with
+    12000 members (three slices of one bucket), a bucket of exactly 4096 members (one full
+    slice), one of 4097 (a full slice and a single member), the rest in the last, partial bucket
+    (c = 65436 is not a multiple of 256), every other bucket empty; positions shuffled, K ragged."""
+    N, K, v, c = 300, 1990, 20, 65436
+    words = sign_plane(720, N, K)
+    P = O.sign_blocks(words, K, v)
+    total = P.size
+    rng = np.random.default_rng(721)
+    parts = [np.full(12000, 777), rng.integers(4864, 5120, 4096), rng.integers(51200, 51456, 4097)]
+    parts.append(rng.integers(65280, c, total - sum(len(q) for q in parts)))
+    idx = rng.permutation(np.concatenate(parts)).astype(np.uint16).reshape(P.shape)
+    C0 = init_codebook(21, c, v)
+    C_ref, cnt_ref = O.codebook_mstep(P, idx, C0, v)
+    C = to_dev(C0)
+    cnt = rb.codebook_mstep(to_dev(words), K, to_dev(idx), C, v)
+    torch.cuda.synchronize()
+    assert cnt_ref[777] == 12000 and cnt_ref[4864:5120].sum() == 4096 and cnt_ref[51200:51456].sum() == 4097
+    assert np.array_equal(u32(C), C_ref)
+    assert np.array_equal(u32(cnt), cnt_ref.astype(np.uint32))
+
+
 @pytest.mark.parametrize("distinct_vals,c", [(5, 8), (8, 8), (1, 3), (300, 1000)])
 def test_distinct_matches_oracle(distinct_vals, c):
     # rows built from a few repeated 10-column blocks, so the layer has few distinct blocks

@@ -274,7 +274,8 @@ rb_status rb_codebook_mstep(const uint32_t* sign_plane, int64_t ldp, int64_t N, 
 /* rb_codebook_distinct -- M = the number of distinct blocks, written to *n_distinct (device
  *   int32). If M < c the codebook becomes the distinct blocks in ascending order, entries M..c-1
  *   repeating the largest (a repeat never wins a tie, so the effective size is M); otherwise the
- *   codebook is not touched. v 1..24 (the bitmap of 2^v patterns lives in ws). */
+ *   codebook is not touched. v 1..24 (a flag byte and a bit per each of the 2^v patterns live in
+ *   ws). */
 rb_status rb_codebook_distinct(const uint32_t* sign_plane, int64_t ldp, int64_t N, int64_t K, int32_t v,
                                uint32_t* codebook, int32_t c, int32_t* n_distinct, void* ws, size_t ws_bytes,
                                void* stream);

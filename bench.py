@@ -386,16 +386,16 @@ def measure_codebook_learn(torch, np, rb, dev, pl, Kc: int, idx, C, enc_us, with
     set_bits = int(np.bitwise_count(np.ascontiguousarray(words_np)).sum())
     # one per block (member) + one per +1 bit, the last block's padding columns counting as +1
     loop_atomics = Nc * nb + set_bits + Nc * (nb * 20 - Kc)
-    # standalone M-step: idx read twice (histogram, scatter), the plane once, the records (a
-    # pattern word and an index byte per block) written and read, the slice tables written and
-    # read, the codebook read and written
+    # standalone M-step: idx read twice (histogram, scatter), the plane once, the records (one
+    # word per block at v = 20: pattern and index byte) written and read, the slice tables
+    # written and read, the codebook read and written
     nblk = Nc * nb
     n_slices = nblk // 4096 + min(-(-C.numel() // 256), nblk)
-    ms_bytes = (pl[0].numel() * 4 + 2 * idx.numel() * 2 + 2 * nblk * 5 + 2 * n_slices * 256 * 21 * 4
+    ms_bytes = (pl[0].numel() * 4 + 2 * idx.numel() * 2 + 2 * nblk * 4 + 2 * n_slices * 256 * 21 * 4
                 + 2 * 4 * C.numel())
     row = {
         "mstep": roof("hbm", ms_bytes / (ms_us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s", ms_us, algorithmic_bytes=ms_bytes,
-                      note="radix pass of the blocks on idx >> 8 writing (pattern, index byte) records, "
+                      note="radix pass of the blocks on idx >> 8 writing one-word (pattern, index byte) records, "
                            "sliced counting with LDS atomics, per-codeword sums of the slices; no global "
                            "atomics"),
         "distinct_us": round(ds_us, 2),

@@ -364,8 +364,9 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
 //   scan     per bucket, H[bucket][.] becomes the exclusive prefix over the chunks, and
 //            btot[bucket] the bucket's total
 //   scatter  chunk q extracts each block's v-bit pattern and writes it to Rp, and the low byte of
-//            its index to Rb, at the bucket's start + H[bucket][q] + a rank from an LDS counter
-//            (the order inside a bucket is the scheduler's)
+//            its index to Rb (v > 24) or to Rp's top byte (v <= 24), at the bucket's start +
+//            H[bucket][q] + a rank from an LDS counter (the order inside a bucket is the
+//            scheduler's)
 //   vote     one block per slice of up to 4096 consecutive records of one bucket: members and
 //            ones per bit of each of the bucket's 256 codewords, counted with LDS atomics and
 //            written as the slice's table
@@ -474,8 +475,12 @@ __global__ __launch_bounds__(kMsThreads) void mstep_scatter_kernel(const uint32_
       if (!ok[u] || id[u] >= (uint32_t)c) continue;  // indices >= c are skipped
       const uint32_t pat = block_from_words(lo[u], hi[u], col[u], K, Kw, v);
       const uint32_t pos = atomicAdd(&cur[id[u] >> 8], 1u);
-      Rp[pos] = pat;
-      Rb[pos] = (uint8_t)(id[u] & 0xffu);
+      if (v <= 24) {  // one word per record: the index byte above the pattern
+        Rp[pos] = pat | (id[u] << 24);
+      } else {
+        Rp[pos] = pat;
+        Rb[pos] = (uint8_t)(id[u] & 0xffu);
+      }
     }
   }
 }
@@ -544,8 +549,14 @@ __global__ __launch_bounds__(kMsVoteThreads) void mstep_vote_kernel(int v, const
   for (int u = 0; u < kMsVoteUnroll; ++u) {  // the slice's records, all loads issued first
     const uint32_t q = lo + (uint32_t)(u * kMsVoteThreads + tid);
     live[u] = q < hi;
-    pat[u] = live[u] ? Rp[q] : 0u;
-    r[u] = live[u] ? (uint32_t)Rb[q] : 0u;
+    const uint32_t rec = live[u] ? Rp[q] : 0u;
+    if (v <= 24) {  // the index byte sits above the pattern
+      pat[u] = rec & 0xffffffu;
+      r[u] = rec >> 24;
+    } else {
+      pat[u] = rec;
+      r[u] = live[u] ? (uint32_t)Rb[q] : 0u;
+    }
   }
 #pragma unroll
   for (int u = 0; u < kMsVoteUnroll; ++u) {

@@ -527,11 +527,14 @@ __global__ __launch_bounds__(kMsVoteThreads) void mstep_vote_kernel(int v, const
                                                                     const uint8_t* __restrict__ Rb,
                                                                     const uint32_t* __restrict__ btot,
                                                                     uint32_t* __restrict__ P) {
-  __shared__ uint32_t cnt[kMsBuckets * 33];  // [codeword][v + 1]
+  // [codeword][W]: counters t = 2 k (low half) and 2 k + 1 (high half) of word k, t = v the
+  // members; a slice holds at most 4096 records, so 16 bits never carry
+  __shared__ uint32_t cnt[kMsBuckets * 17];
   __shared__ uint32_t start[kMsBuckets], first[kMsBuckets], nsl[kMsBuckets];
   const int tid = threadIdx.x;
   const int stride = v + 1;
-  for (int i = tid; i < kMsBuckets * stride; i += kMsVoteThreads) cnt[i] = 0u;
+  const int W = (v + 2) / 2;
+  for (int i = tid; i < kMsBuckets * W; i += kMsVoteThreads) cnt[i] = 0u;
   ms_slices(btot, start, first, nsl, tid);
   const uint32_t slice = blockIdx.x;
   if (slice >= first[kMsBuckets - 1] + nsl[kMsBuckets - 1]) return;  // whole block
@@ -561,16 +564,18 @@ __global__ __launch_bounds__(kMsVoteThreads) void mstep_vote_kernel(int v, const
 #pragma unroll
   for (int u = 0; u < kMsVoteUnroll; ++u) {
     if (!live[u]) continue;
-    uint32_t* row = cnt + r[u] * (uint32_t)stride;
-    atomicAdd(row + v, 1u);
-    for (int t = 0; t < v; ++t)
-      if ((pat[u] >> t) & 1u) atomicAdd(row + t, 1u);
+    uint32_t* row = cnt + r[u] * (uint32_t)W;
+    const uint64_t all = (uint64_t)pat[u] | (1ull << v);  // the pattern's bits, then the member
+    for (int k = 0; k < W; ++k) {
+      const uint32_t add = (uint32_t)((all >> (2 * k)) & 1u) | ((uint32_t)((all >> (2 * k + 1)) & 1u) << 16);
+      if (add) atomicAdd(row + k, add);
+    }
   }
   __syncthreads();
   uint32_t* __restrict__ out = P + (size_t)slice * (size_t)(kMsBuckets * stride);
   for (int i = tid; i < kMsBuckets * stride; i += kMsVoteThreads) {
     const int t = i / kMsBuckets, cw = i % kMsBuckets;
-    out[i] = cnt[cw * stride + t];
+    out[i] = (cnt[cw * W + (t >> 1)] >> (16 * (t & 1))) & 0xffffu;
   }
 }
 

@@ -7,6 +7,8 @@
 #include "rb_device.hpp"
 #include "rb_internal.h"
 
+#include <type_traits>
+
 namespace rb {
 namespace {
 
@@ -797,6 +799,8 @@ __global__ __launch_bounds__(256) void table_seed_kernel(const uint32_t* __restr
   if (blockIdx.x == 0 && threadIdx.x == 0) flag[0] = 1u;
 }
 
+// VMAX >= v, a multiple of 4: the neighbour loop's unrolled length
+template <int VMAX>
 __global__ __launch_bounds__(256) void table_layer_kernel(uint32_t* __restrict__ table, int v, int d,
                                                           uint32_t* __restrict__ flag) {
   if (flag[d] == 0u) return;  // nothing at distance d: everything is reached
@@ -805,13 +809,13 @@ __global__ __launch_bounds__(256) void table_layer_kernel(uint32_t* __restrict__
   __syncthreads();
   const uint32_t p = blockIdx.x * 256u + threadIdx.x;  // the grid covers the 2^v patterns (more when v < 8)
   if (p < (1u << v) && table[p] == kTableUnreached) {
-    uint32_t e[kTableMaxV];
+    uint32_t e[VMAX];
 #pragma unroll
-    for (int t = 0; t < kTableMaxV; ++t)  // all neighbours' loads in flight; bits past v re-read bit v - 1
+    for (int t = 0; t < VMAX; ++t)  // all neighbours' loads in flight; bits past v re-read bit v - 1
       e[t] = table[p ^ (1u << (t < v ? t : v - 1))];
     uint32_t best = kTableUnreached;
 #pragma unroll
-    for (int t = 0; t < kTableMaxV; ++t)
+    for (int t = 0; t < VMAX; ++t)
       if ((e[t] >> 24) == (uint32_t)d) best = (e[t] & 0xffffffu) < best ? (e[t] & 0xffffffu) : best;
     if (best != kTableUnreached) {
       table[p] = ((uint32_t)(d + 1) << 24) | best;
@@ -975,7 +979,17 @@ hipError_t launch_codebook_table(const uint32_t* codebook, int c, int v, void* w
   table_seed_kernel<<<(unsigned)((c + 255) / 256 < 1024 ? (c + 255) / 256 : 1024), 256, 0, s>>>(codebook, c, v, table,
                                                                                                  flag);
   const unsigned grid = (unsigned)((np + 255) / 256);
-  for (int d = 0; d < v; ++d) table_layer_kernel<<<grid, 256, 0, s>>>(table, v, d, flag);
+  auto layers = [&](auto vmax) {
+    for (int d = 0; d < v; ++d) table_layer_kernel<decltype(vmax)::value><<<grid, 256, 0, s>>>(table, v, d, flag);
+  };
+  switch ((v + 3) / 4) {
+    case 1: layers(std::integral_constant<int, 4>{}); break;
+    case 2: layers(std::integral_constant<int, 8>{}); break;
+    case 3: layers(std::integral_constant<int, 12>{}); break;
+    case 4: layers(std::integral_constant<int, 16>{}); break;
+    case 5: layers(std::integral_constant<int, 20>{}); break;
+    default: layers(std::integral_constant<int, kTableMaxV>{}); break;
+  }
   return hipGetLastError();
 }
 
